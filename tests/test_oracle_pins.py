@@ -1,0 +1,360 @@
+"""Pins of the CPU oracle against things other than itself.
+
+These checks use hand-worked values (tests/golden), library routines (torch CPU
+fp64, Python integers), closed forms, brute force on tiny inputs and
+invariants. Each catches a plausible mistake in the oracle: a wrong sign, a
+wrong index, a transposed operand, a dropped term or a wrong mask direction.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import hstu_oracle as O
+from hstu_jagged_pointwise_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rows(name):
+    out = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                out.append(line.split())
+    return out
+
+
+# ---------------------------------------------------------------- buckets
+def test_time_bucket_golden():
+    for dt, T, want in _rows("time_buckets.txt"):
+        got = int(O.time_bucket(np.array([int(dt)], np.int64), int(T))[0])
+        assert got == int(want), (dt, T, got, want)
+
+
+def test_pos_bucket_golden():
+    for d, P, want in _rows("pos_buckets.txt"):
+        assert int(O.pos_bucket(np.array([int(d)]), int(P))[0]) == int(want)
+
+
+def test_floor_log2_matches_python_bit_length():
+    rng = np.random.default_rng(7)
+    xs = [1, 2, 3]
+    for k in range(1, 63):
+        xs += [(1 << k) - 1, 1 << k, (1 << k) + 1]
+    xs += [int(v) for v in rng.integers(1, 2**62, size=2000)]
+    xs = [x for x in xs if 1 <= x < 2**63]
+    got = O.floor_log2(np.array(xs, dtype=np.int64))
+    want = np.array([x.bit_length() - 1 for x in xs])
+    assert np.array_equal(got, want)
+
+
+# ---------------------------------------------------------------- SiLU / LayerNorm
+def test_silu_against_torch_and_identities():
+    x = np.linspace(-60, 60, 4001)
+    ref = torch.nn.functional.silu(torch.from_numpy(x)).numpy()
+    np.testing.assert_allclose(O.silu(x), ref, rtol=1e-14, atol=1e-300)
+    # SiLU(x) - SiLU(-x) = x (x*s(x) + x*s(-x) = x): catches a sign slip in the exponent
+    np.testing.assert_allclose(O.silu(x) - O.silu(-x), x, rtol=1e-12, atol=1e-12)
+    assert O.silu(0.0) == 0.0
+    assert O.silu(-1e4) == 0.0 and np.isfinite(O.silu(-1e4))
+
+
+def test_layer_norm_against_torch():
+    rng = np.random.default_rng(3)
+    z = rng.standard_normal((17, 96)) * 3 + 1
+    g = rng.standard_normal(96)
+    b = rng.standard_normal(96)
+    ref = torch.nn.functional.layer_norm(torch.from_numpy(z), (96,), torch.from_numpy(g),
+                                         torch.from_numpy(b), eps=1e-5).numpy()
+    np.testing.assert_allclose(O.layer_norm_rows(z, g, b, 1e-5), ref, rtol=1e-12, atol=1e-12)
+    y = O.layer_norm_rows(z, None, None, 0.0)
+    np.testing.assert_allclose(y.mean(1), 0, atol=1e-12)
+    np.testing.assert_allclose(y.var(1), 1, atol=1e-12)
+
+
+# ---------------------------------------------------------------- worked example
+def test_worked_example_by_hand():
+    rows = _rows("worked_example.txt")
+    n, N = 4, 4
+    q = np.zeros((n, 1, 2))
+    k = np.zeros((n, 1, 2))
+    for i in range(n):
+        q[i, 0] = (i, 1)
+        k[i, 0] = (2, i)
+    v = np.eye(n).reshape(n, 1, n)
+    ts = np.array([0, 1, 3, 10], np.int64)
+    rp = np.array([[0.1, 0.2, 0.3]])
+    rt = np.array([[0.01, 0.02, 0.03, 0.04]])
+    out = O.hstu_attention(np.array([0, n]), ts, q, k, v, rp, rt, N)[:, 0, :]
+    want = np.zeros((n, n))
+    for i, j, _s, _bp, _bt, x in rows:
+        x = float(x)
+        want[int(i), int(j)] = x / (1.0 + math.exp(-x)) / N
+    np.testing.assert_allclose(out, want, rtol=1e-13, atol=0)
+    assert np.all(out[np.triu_indices(n, 1)] == 0.0)  # hidden pairs contribute exactly 0
+
+
+# ---------------------------------------------------------------- brute force
+def _brute_attention(offsets, ts, q, k, v, rp, rt, N):
+    """Scalar loops, written from the definition, independent of numpy broadcasting."""
+    Ttot, H, dv = v.shape
+    out = [[[0.0] * dv for _ in range(H)] for _ in range(Ttot)]
+    for b in range(len(offsets) - 1):
+        s0, s1 = int(offsets[b]), int(offsets[b + 1])
+        for h in range(H):
+            for i in range(s1 - s0):
+                for j in range(i + 1):
+                    sc = sum(float(q[s0 + i, h, c]) * float(k[s0 + j, h, c])
+                             for c in range(q.shape[2]))
+                    if rp is not None:
+                        sc += float(rp[h][min(i - j, rp.shape[1] - 1)])
+                    if rt is not None:
+                        dt = max(int(ts[s0 + i]) - int(ts[s0 + j]), 0)
+                        sc += float(rt[h][min((dt + 1).bit_length() - 1, rt.shape[1] - 1)])
+                    a = sc / (1.0 + math.exp(-sc)) / N
+                    for c in range(dv):
+                        out[s0 + i][h][c] += a * float(v[s0 + j, h, c])
+    return np.array(out)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_attention_matches_brute_force(seed):
+    x = synth.make_attn(seed, lambda r: synth.lengths_uniform(r, 3, 1, 9), 2, 3, 5, 4, 6, "f32",
+                        rab_std=0.5)
+    got = O.hstu_attention(x.offsets, x.ts, x.q, x.k, x.v, x.rab_pos, x.rab_time, x.max_seq_len)
+    want = _brute_attention(x.offsets, x.ts, x.q, x.k, x.v, x.rab_pos, x.rab_time, x.max_seq_len)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-14)
+
+
+def test_attention_matches_padded_torch_route():
+    """Padded dense batch through torch.matmul with a lower-triangular mask equals the
+    jagged per-sequence oracle (the ragged special case reduces to a masked matmul)."""
+    x = synth.make_attn(5, lambda r: synth.lengths_uniform(r, 5, 0, 23), 3, 8, 6, 16, 16, "f32",
+                        rab_std=0.3)
+    got = O.hstu_attention(x.offsets, x.ts, x.q, x.k, x.v, x.rab_pos, x.rab_time, x.max_seq_len)
+    B = len(x.offsets) - 1
+    n = int(x.lengths.max())
+    H = x.num_heads
+    qp = torch.zeros(B, H, n, x.d_qk, dtype=torch.float64)
+    kp = torch.zeros_like(qp)
+    vp = torch.zeros(B, H, n, x.d_v, dtype=torch.float64)
+    tp = torch.zeros(B, n, dtype=torch.int64)
+    for b in range(B):
+        s, e = x.offsets[b], x.offsets[b + 1]
+        qp[b, :, : e - s] = torch.from_numpy(x.q[s:e].astype(np.float64)).transpose(0, 1)
+        kp[b, :, : e - s] = torch.from_numpy(x.k[s:e].astype(np.float64)).transpose(0, 1)
+        vp[b, :, : e - s] = torch.from_numpy(x.v[s:e].astype(np.float64)).transpose(0, 1)
+        tp[b, : e - s] = torch.from_numpy(x.ts[s:e])
+    idx = torch.arange(n)
+    dpos = (idx[:, None] - idx[None, :]).clamp(min=0, max=x.num_pos_buckets - 1)
+    dt = (tp[:, :, None] - tp[:, None, :]).clamp(min=0) + 1
+    bt = (torch.floor(torch.log2(dt.double())).long()).clamp(max=x.num_time_buckets - 1)
+    rp = torch.from_numpy(x.rab_pos.astype(np.float64))
+    rt = torch.from_numpy(x.rab_time.astype(np.float64))
+    bias = rp[:, dpos][None] + rt[torch.arange(H)[None, :, None, None], bt[:, None]]
+    s = torch.matmul(qp, kp.transpose(-1, -2).contiguous()) + bias
+    a = torch.nn.functional.silu(s) / x.max_seq_len
+    a = a * torch.tril(torch.ones(n, n, dtype=torch.float64))
+    o = torch.matmul(a, vp)
+    want = np.zeros_like(got)
+    for b in range(B):
+        s0, e0 = x.offsets[b], x.offsets[b + 1]
+        want[s0:e0] = o[b, :, : e0 - s0].transpose(0, 1).numpy()
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-13)
+
+
+# ---------------------------------------------------------------- closed forms
+def test_single_token_closed_form():
+    rng = np.random.default_rng(11)
+    q, k, v = rng.standard_normal((1, 1, 4)), rng.standard_normal((1, 1, 4)), rng.standard_normal((1, 1, 3))
+    rp, rt = rng.standard_normal((1, 8)), rng.standard_normal((1, 8))
+    N = 7
+    got = O.hstu_attention(np.array([0, 1]), np.array([123], np.int64), q, k, v, rp, rt, N)
+    x = float(q[0, 0] @ k[0, 0]) + rp[0, 0] + rt[0, 0]
+    np.testing.assert_allclose(got[0, 0], x / (1 + math.exp(-x)) / N * v[0, 0], rtol=1e-14)
+
+
+def test_zero_query_gives_zero_and_gate_gives_beta_times_u():
+    x = synth.make_attn(2, lambda r: synth.lengths_uniform(r, 4, 1, 20), 2, 8, 8, 8, 8, "f32",
+                        with_u=True, with_ln_affine=True)
+    q = np.zeros_like(x.q)
+    o = O.hstu_attention(x.offsets, None, q, x.k, x.v, None, None, x.max_seq_len)
+    assert np.all(o == 0.0)
+    g = O.hstu_attention(x.offsets, None, q, x.k, x.v, None, None, x.max_seq_len, u=x.u,
+                         gamma=x.gamma, beta=x.beta)
+    want = x.beta.astype(np.float64)[None, :] * x.u.reshape(len(q), -1).astype(np.float64)
+    np.testing.assert_allclose(g.reshape(len(q), -1), want, rtol=1e-14, atol=0)
+
+
+def test_count_is_preserved_without_normalization():
+    """Identical keys and values: O_i = (i+1) SiLU(q_i.k)/N v. Pointwise attention keeps
+    the count of matching history (HSTU chapter, "No sequence-wise softmax")."""
+    rng = np.random.default_rng(4)
+    n, d = 12, 5
+    q = rng.standard_normal((n, 1, d))
+    kk = rng.standard_normal(d)
+    vv = rng.standard_normal(d)
+    k = np.tile(kk, (n, 1, 1))
+    v = np.tile(vv, (n, 1, 1))
+    N = 20
+    o = O.hstu_attention(np.array([0, n]), None, q, k, v, None, None, N)
+    for i in range(n):
+        s = float(q[i, 0] @ kk)
+        np.testing.assert_allclose(o[i, 0], (i + 1) * s / (1 + math.exp(-s)) / N * vv, rtol=1e-13)
+
+
+def test_linear_in_v_and_inverse_in_n():
+    x = synth.make_attn(9, lambda r: synth.lengths_uniform(r, 3, 1, 30), 2, 8, 8, 32, 32, "f32")
+    o1 = O.hstu_attention(x.offsets, x.ts, x.q, x.k, x.v, x.rab_pos, x.rab_time, 50)
+    o2 = O.hstu_attention(x.offsets, x.ts, x.q, x.k, 2.5 * x.v.astype(np.float64), x.rab_pos,
+                          x.rab_time, 50)
+    o3 = O.hstu_attention(x.offsets, x.ts, x.q, x.k, x.v, x.rab_pos, x.rab_time, 100)
+    np.testing.assert_allclose(o2, 2.5 * o1, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(o3, 0.5 * o1, rtol=1e-13, atol=1e-15)
+
+
+# ---------------------------------------------------------------- invariants
+def test_jagged_equals_each_sequence_alone_and_reorder_permutes():
+    x = synth.make_attn(6, lambda r: synth.lengths_uniform(r, 5, 0, 40), 2, 16, 16, 32, 32, "f32",
+                        with_u=True)
+    full = O.hstu_attention(x.offsets, x.ts, x.q, x.k, x.v, x.rab_pos, x.rab_time, 64, u=x.u)
+    for b in range(5):
+        s, e = x.offsets[b], x.offsets[b + 1]
+        one = O.hstu_attention(np.array([0, e - s]), x.ts[s:e], x.q[s:e], x.k[s:e], x.v[s:e],
+                               x.rab_pos, x.rab_time, 64, u=x.u[s:e])
+        assert np.array_equal(one, full[s:e])
+    perm = [3, 0, 4, 2, 1]
+    idx = np.concatenate([np.arange(x.offsets[b], x.offsets[b + 1]) for b in perm]).astype(int)
+    off2 = synth.offsets_from_lengths(x.lengths[perm])
+    re = O.hstu_attention(off2, x.ts[idx], x.q[idx], x.k[idx], x.v[idx], x.rab_pos, x.rab_time, 64,
+                          u=x.u[idx])
+    assert np.array_equal(re, full[idx])
+
+
+def test_future_and_other_sequences_do_not_leak():
+    x = synth.make_attn(8, lambda r: np.array([17, 23]), 2, 8, 8, 32, 32, "f32")
+    base = O.hstu_attention(x.offsets, x.ts, x.q, x.k, x.v, x.rab_pos, x.rab_time, 23)
+    k2, v2, t2 = x.k.copy(), x.v.copy(), x.ts.copy()
+    cut = 9  # perturb keys/values/timestamps at positions >= 9 of sequence 0, and all of seq 1
+    k2[cut:] += 100.0
+    v2[cut:] -= 50.0
+    t2[cut:17] += 10_000_000
+    out = O.hstu_attention(x.offsets, t2, x.q, k2, v2, x.rab_pos, x.rab_time, 23)
+    assert np.array_equal(out[:cut], base[:cut])
+
+
+# ---------------------------------------------------------------- layer
+def test_layer_matches_torch_modules_route():
+    """eq. 1-3 through torch.nn.functional.linear / silu / layer_norm plus a padded
+    masked attention; split order U|V|Q|K."""
+    x = synth.make_layer(12, lambda r: synth.lengths_uniform(r, 3, 1, 14), 2, 8, 4, 12, 16, 16,
+                         "f32", random_bias=True, with_ln_affine=True)
+    w = x.layers[0]
+    got = O.hstu_layer(x.offsets, x.ts, x.x, w, 2, 8, 4, x.max_seq_len)
+    T = torch.from_numpy
+    z = torch.nn.functional.silu(torch.nn.functional.linear(T(x.x).double(), T(w.w1).double(),
+                                                            T(w.b1).double()))
+    U, V, Q, K = torch.split(z, [8, 8, 16, 16], dim=1)
+    G = torch.zeros(len(x.x), 8, dtype=torch.float64)
+    for b in range(len(x.offsets) - 1):
+        s, e = int(x.offsets[b]), int(x.offsets[b + 1])
+        n = e - s
+        heads = []
+        for h in range(2):
+            q = Q[s:e, h * 8:(h + 1) * 8]
+            k = K[s:e, h * 8:(h + 1) * 8]
+            v = V[s:e, h * 4:(h + 1) * 4]
+            i = torch.arange(n)
+            dpos = (i[:, None] - i[None, :]).clamp(0, 15)
+            t = torch.from_numpy(x.ts[s:e])
+            bt = torch.floor(torch.log2(((t[:, None] - t[None, :]).clamp(min=0) + 1).double())).long()
+            bias = T(w.rab_pos).double()[h][dpos] + T(w.rab_time).double()[h][bt.clamp(max=15)]
+            a = torch.nn.functional.silu(q @ k.T + bias) / x.max_seq_len * torch.tril(torch.ones(n, n))
+            heads.append(a @ v)
+        av = torch.cat(heads, dim=1)
+        G[s:e] = torch.nn.functional.layer_norm(av, (8,), T(w.gamma).double(), T(w.beta).double(),
+                                                1e-5) * U[s:e]
+    want = torch.nn.functional.linear(G, T(w.w2).double(), T(w.b2).double()).numpy()
+    np.testing.assert_allclose(got, want, rtol=1e-11, atol=1e-12)
+
+
+# ---------------------------------------------------------------- M-FALCON
+def _small_mfalcon(seed, hist, cands, layers=2, shared=False, mb=3):
+    return synth.make_mfalcon(seed, hist, cands, 2, 8, 8, 12, 8, 16, "f32", num_layers=layers,
+                              microbatch=mb, shared_request_time=shared, w_std=0.3,
+                              random_bias=True, with_ln_affine=True)
+
+
+def _run_mf(x, mb=None):
+    return O.mfalcon_score(x.hist_offsets, x.hist_ts, x.hist_x, x.cand_offsets, x.cand_ts,
+                           x.cand_x, x.layers, x.num_heads, x.d_qk, x.d_v, x.max_seq_len,
+                           mb or x.microbatch, x.w_head)
+
+
+def test_mfalcon_equals_last_row_of_history_plus_candidate():
+    x = _small_mfalcon(1, [7, 0, 12], [4, 3, 5])
+    got, lg = _run_mf(x)
+    want, lw = O.mfalcon_by_definition(x.hist_offsets, x.hist_ts, x.hist_x, x.cand_offsets,
+                                       x.cand_ts, x.cand_x, x.layers, 2, 8, 8, x.max_seq_len,
+                                       x.w_head)
+    np.testing.assert_allclose(got, want, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(lg, lw, rtol=1e-10, atol=1e-12)
+
+
+def test_mfalcon_candidate_independence():
+    """fp64 BLAS blocking depends on the row count, so these hold to rounding here."""
+    x = _small_mfalcon(2, [10], [7], shared=False)
+    base, _ = _run_mf(x)
+    # permuting candidates permutes outputs
+    perm = np.array([4, 1, 6, 0, 2, 5, 3])
+    y = _small_mfalcon(2, [10], [7], shared=False)
+    y.cand_x, y.cand_ts = x.cand_x[perm], x.cand_ts[perm]
+    out, _ = _run_mf(y)
+    np.testing.assert_allclose(out, base[perm], rtol=1e-12, atol=1e-14)
+    # adding a candidate leaves the others unchanged
+    z = _small_mfalcon(2, [10], [7], shared=False)
+    z.cand_x = np.concatenate([x.cand_x, x.cand_x[:1] * 3.0])
+    z.cand_ts = np.concatenate([x.cand_ts, x.cand_ts[:1] + 5])
+    z.cand_offsets = np.array([0, 8])
+    out2, _ = _run_mf(z)
+    np.testing.assert_allclose(out2[:7], base, rtol=1e-12, atol=1e-14)
+    # microbatch size does not change results
+    for mb in (1, 2, 7, 100):
+        np.testing.assert_allclose(_run_mf(x, mb)[0], base, rtol=1e-12, atol=1e-14)
+
+
+def test_candidate_attention_by_hand():
+    """Worked by hand from the setup of tests/golden/worked_example.txt: a
+    candidate at position n_h = 3 after history times (0, 1, 3), with its own time
+    t_c = 10, P = 3, T = 4. History keys use bp = (2, 2, 1) and bt = (3, 3, 3). The
+    self term uses bp = 0 and bt = 0. The history keys are k_j = (2, j) and the
+    candidate has q = (3, 1) and k_c = (2, 3), so the scores are 6, 7, 8 and 9.
+    The values are one-hot: history j is e_j and the candidate is e_3."""
+    N = 4
+    Kh = np.array([[2, 0], [2, 1], [2, 2]], float).reshape(3, 1, 2)
+    Vh = np.eye(4)[:3].reshape(3, 1, 4)
+    Qc = np.array([[3, 1]], float).reshape(1, 1, 2)
+    Kc = np.array([[2, 3]], float).reshape(1, 1, 2)
+    Vc = np.eye(4)[3:].reshape(1, 1, 4)
+    rp = np.array([[0.1, 0.2, 0.3]])
+    rt = np.array([[0.01, 0.02, 0.03, 0.04]])
+    got = O.candidate_attention(Qc, Kc, Vc, Kh, Vh, np.array([10]), np.array([0, 1, 3]), rp, rt, N)
+    xs = [6.34, 7.34, 8.24, 9.11]   # the same numbers as row i = 3 of the worked example
+    want = np.array([x / (1 + math.exp(-x)) / N for x in xs])
+    np.testing.assert_allclose(got[0, 0], want, rtol=1e-13)
+
+
+# ---------------------------------------------------------------- workloads
+def test_workload_shapes():
+    x = synth.workload_tiny_attention()
+    assert len(x.offsets) == 5 and x.lengths.min() >= 8 and x.lengths.max() <= 64
+    assert x.max_seq_len == x.lengths.max()
+    y = synth.workload_long_attention()
+    assert y.lengths[0] == 8192 and y.lengths.min() >= 4096 and y.lengths.max() == 8192
+    assert np.all(np.diff(y.ts[y.offsets[0]:y.offsets[1]]) >= 1)
+    bits = synth.bf16_bits(y.q[:4].ravel())
+    np.testing.assert_array_equal(synth.bf16_to_f32(bits), y.q[:4].ravel())
