@@ -1,0 +1,633 @@
+// C-ABI host layer of libhstu: argument validation (host data only, so every
+// rejection happens before any HIP call), workspace carving and launch order.
+// The operations are the HSTU layer's eqs. 1-3 ("What an HSTU layer changes",
+// HSTU chapter) and M-FALCON candidate scoring (same chapter, "M-FALCON").
+#include "hstu.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+
+using namespace hstu;
+
+namespace {
+
+thread_local std::string g_err;
+
+hstu_status fail(hstu_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+hstu_status device_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return HSTU_OK;
+  return fail(HSTU_DEVICE_ERROR, "%s: %s", where, hipGetErrorString(e));
+}
+
+#define HSTU_TRY(expr, where)                                   \
+  do {                                                          \
+    hstu_status st_ = device_status((expr), (where));           \
+    if (st_ != HSTU_OK) return st_;                             \
+  } while (0)
+
+constexpr size_t kAlign = 256;
+constexpr int64_t kMaxRows = int64_t(1) << 30;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+size_t elt_size(hstu_dtype t) { return t == HSTU_BF16 ? 2 : 4; }
+
+// Sequential carving of the caller's workspace.
+struct Carver {
+  char* base;
+  size_t off = 0;
+  void* take(size_t bytes) {
+    void* p = base ? base + off : nullptr;
+    off += align_up(bytes);
+    return p;
+  }
+};
+
+struct Jagged {
+  int64_t total = 0;    // rows
+  int64_t max_len = 0;  // longest sequence
+  int64_t items = 0;    // query tiles for the chosen kernel
+  int max_tiles = 0;    // query tiles of the longest sequence
+};
+
+hstu_status check_offsets(const int64_t* off, int B, int64_t limit_len, int tile_rows,
+                          const char* name, Jagged* j) {
+  *j = Jagged{};
+  if (B < 0) return fail(HSTU_INVALID_ARGUMENT, "%s: batch must be >= 0 (got %d)", name, B);
+  if (B == 0) return HSTU_OK;
+  if (!off) return fail(HSTU_INVALID_ARGUMENT, "%s: host offsets are NULL", name);
+  if (off[0] != 0) return fail(HSTU_INVALID_ARGUMENT, "%s: offsets[0] must be 0", name);
+  for (int b = 0; b < B; ++b) {
+    const int64_t n = off[b + 1] - off[b];
+    if (n < 0) return fail(HSTU_INVALID_ARGUMENT, "%s: offsets decrease at %d", name, b);
+    if (limit_len >= 0 && n > limit_len)
+      return fail(HSTU_INVALID_ARGUMENT, "%s: sequence %d has length %lld > max_seq_len %lld",
+                  name, b, (long long)n, (long long)limit_len);
+    j->max_len = std::max(j->max_len, n);
+    j->items += (n + tile_rows - 1) / tile_rows;
+  }
+  j->total = off[B];
+  if (j->total > kMaxRows)
+    return fail(HSTU_UNSUPPORTED, "%s: %lld rows exceed the supported 2^30", name,
+                (long long)j->total);
+  j->max_tiles = (int)((j->max_len + tile_rows - 1) / tile_rows);
+  return HSTU_OK;
+}
+
+hstu_status check_attn_desc(const hstu_attn_desc* d) {
+  if (!d) return fail(HSTU_INVALID_ARGUMENT, "descriptor is NULL");
+  if (d->batch < 0) return fail(HSTU_INVALID_ARGUMENT, "batch must be >= 0");
+  if (d->num_heads < 1 || d->num_heads > 1024)
+    return fail(HSTU_INVALID_ARGUMENT, "num_heads must be in [1, 1024] (got %d)", d->num_heads);
+  auto okd = [](int x) { return x == 32 || x == 64 || x == 128; };
+  if (!okd(d->d_qk) || !okd(d->d_v))
+    return fail(HSTU_UNSUPPORTED, "d_qk and d_v must be 32, 64 or 128 (got %d, %d)", d->d_qk,
+                d->d_v);
+  if (d->max_seq_len < 1) return fail(HSTU_INVALID_ARGUMENT, "max_seq_len (N) must be >= 1");
+  if (d->num_pos_buckets < 1 || d->num_time_buckets < 1)
+    return fail(HSTU_INVALID_ARGUMENT, "bucket counts must be >= 1");
+  if (d->dtype != HSTU_F32 && d->dtype != HSTU_BF16)
+    return fail(HSTU_UNSUPPORTED, "dtype must be HSTU_F32 or HSTU_BF16");
+  return HSTU_OK;
+}
+
+hstu_status check_eps(float eps) {
+  if (!(eps > 0.f) || !std::isfinite(eps))
+    return fail(HSTU_INVALID_ARGUMENT, "ln_eps must be finite and > 0");
+  return HSTU_OK;
+}
+
+int attn_tile_rows(const hstu_attn_desc* d) {
+  return attn_mfma_supported(d->dtype == HSTU_BF16, d->d_qk, d->d_v, d->num_pos_buckets,
+                             d->num_time_buckets)
+             ? kMfmaRows
+             : kSimpleRows;
+}
+
+hipError_t run_attention(const hstu_attn_desc* d, const AttnArgs& a, bool cand, hipStream_t s) {
+  const bool mfma = attn_mfma_supported(d->dtype == HSTU_BF16, d->d_qk, d->d_v,
+                                        d->num_pos_buckets, d->num_time_buckets);
+  return mfma ? launch_attn_mfma(a, cand, s) : launch_attn_simple(a, d->dtype == HSTU_BF16, cand, s);
+}
+
+AttnArgs base_args(const hstu_attn_desc* d) {
+  AttnArgs a{};
+  a.batch = d->batch;
+  a.H = d->num_heads;
+  a.d_qk = d->d_qk;
+  a.d_v = d->d_v;
+  a.P = d->num_pos_buckets;
+  a.T = d->num_time_buckets;
+  a.inv_n = 1.0f / (float)d->max_seq_len;
+  return a;
+}
+
+// ---------------------------------------------------------------- attention
+struct AttnPlan {
+  Jagged j;
+  size_t ws = 0;
+};
+
+hstu_status plan_attn(const hstu_attn_desc* d, const int64_t* off_host, bool gated, AttnPlan* p) {
+  hstu_status st = check_attn_desc(d);
+  if (st) return st;
+  st = check_offsets(off_host, d->batch, d->max_seq_len, attn_tile_rows(d), "seq_offsets", &p->j);
+  if (st) return st;
+  if ((int64_t)p->j.items * d->num_heads >= (int64_t(1) << 31))
+    return fail(HSTU_UNSUPPORTED, "too many query tiles for one launch");
+  Carver c{nullptr};
+  c.take((size_t)p->j.items * sizeof(int2));
+  if (gated) c.take((size_t)p->j.total * d->num_heads * d->d_v * sizeof(float));
+  p->ws = c.off;
+  return HSTU_OK;
+}
+
+// ---------------------------------------------------------------- layer
+struct LayerPlan {
+  Jagged j;
+  size_t ws = 0;
+  int64_t f1_cols = 0;
+};
+
+hstu_status check_layer_desc(const hstu_layer_desc* d) {
+  if (!d) return fail(HSTU_INVALID_ARGUMENT, "descriptor is NULL");
+  hstu_status st = check_attn_desc(&d->attn);
+  if (st) return st;
+  if (d->d_model < 8 || d->d_model % 8 != 0 || d->d_model > 65536)
+    return fail(HSTU_UNSUPPORTED, "d_model must be a multiple of 8 in [8, 65536] (got %d)",
+                d->d_model);
+  if (d->residual != 0 && d->residual != 1)
+    return fail(HSTU_INVALID_ARGUMENT, "residual must be 0 or 1");
+  if (d->num_layers < 1 || d->num_layers > 4096)
+    return fail(HSTU_INVALID_ARGUMENT, "num_layers must be in [1, 4096]");
+  return check_eps(d->attn.ln_eps);
+}
+
+hstu_status check_weights(const hstu_layer_weights* w, int L) {
+  if (!w) return fail(HSTU_INVALID_ARGUMENT, "weights array is NULL");
+  for (int l = 0; l < L; ++l) {
+    if (!w[l].w1 || !w[l].w2)
+      return fail(HSTU_INVALID_ARGUMENT, "layer %d: w1 and w2 are required", l);
+    if (!aligned16(w[l].w1) || !aligned16(w[l].w2))
+      return fail(HSTU_INVALID_ARGUMENT, "layer %d: w1 and w2 must be 16-byte aligned", l);
+  }
+  return HSTU_OK;
+}
+
+struct LayerBufs {
+  int2* items;
+  void* uvqk;
+  float* o;
+  void* g;
+  void* tmp;
+};
+
+void carve_layer(Carver& c, const hstu_layer_desc* d, int64_t rows, int64_t items, LayerBufs* b) {
+  const hstu_attn_desc& a = d->attn;
+  const size_t es = elt_size(a.dtype);
+  const int64_t f1 = 2LL * a.num_heads * (a.d_v + a.d_qk);
+  const int64_t hv = (int64_t)a.num_heads * a.d_v;
+  b->items = (int2*)c.take((size_t)items * sizeof(int2));
+  b->uvqk = c.take((size_t)rows * f1 * es);
+  b->o = (float*)c.take((size_t)rows * hv * sizeof(float));
+  b->g = c.take((size_t)rows * hv * es);
+  b->tmp = d->num_layers > 1 ? c.take((size_t)rows * d->d_model * es) : nullptr;
+}
+
+hstu_status plan_layer(const hstu_layer_desc* d, const int64_t* off_host, LayerPlan* p) {
+  hstu_status st = check_layer_desc(d);
+  if (st) return st;
+  st = check_offsets(off_host, d->attn.batch, d->attn.max_seq_len, attn_tile_rows(&d->attn),
+                     "seq_offsets", &p->j);
+  if (st) return st;
+  if ((int64_t)p->j.items * d->attn.num_heads >= (int64_t(1) << 31))
+    return fail(HSTU_UNSUPPORTED, "too many query tiles for one launch");
+  Carver c{nullptr};
+  LayerBufs b;
+  carve_layer(c, d, p->j.total, p->j.items, &b);
+  p->ws = c.off;
+  p->f1_cols = 2LL * d->attn.num_heads * (d->attn.d_v + d->attn.d_qk);
+  return HSTU_OK;
+}
+
+// Views into the f1 output [rows, U|V|Q|K].
+struct UVQK {
+  const char* u;
+  const char* v;
+  const char* q;
+  const char* k;
+  int64_t ld;
+};
+UVQK split_view(const void* base, const hstu_attn_desc& a) {
+  const size_t es = elt_size(a.dtype);
+  const int64_t hv = (int64_t)a.num_heads * a.d_v, hq = (int64_t)a.num_heads * a.d_qk;
+  const char* p = (const char*)base;
+  return UVQK{p, p + hv * es, p + 2 * hv * es, p + (2 * hv + hq) * es, 2 * hv + 2 * hq};
+}
+
+// One layer over `rows` jagged rows: f1 -> causal attention -> LN gate -> f2.
+hstu_status layer_once(const hstu_layer_desc* d, const int64_t* off_dev, const int64_t* ts,
+                       const Jagged& j, const void* x, const hstu_layer_weights& w, void* y,
+                       const LayerBufs& b, bool items_ready, hipStream_t s, bool f1_only) {
+  const hstu_attn_desc& a = d->attn;
+  const int bf = a.dtype == HSTU_BF16;
+  const int64_t rows = j.total;
+  const int64_t f1 = 2LL * a.num_heads * (a.d_v + a.d_qk);
+  const int hv = a.num_heads * a.d_v;
+  HSTU_TRY(launch_gemm(x, d->d_model, w.w1, d->d_model, w.b1, nullptr, 0, b.uvqk, f1, rows, (int)f1,
+                       d->d_model, 1, bf, s),
+           "f1 projection");
+  if (f1_only) return HSTU_OK;
+  if (!items_ready)
+    HSTU_TRY(launch_plan_causal(off_dev, a.batch, attn_tile_rows(&a), j.max_tiles, b.items,
+                                (int)j.items, s),
+             "tile planner");
+  const UVQK vw = split_view(b.uvqk, a);
+  AttnArgs aa = base_args(&a);
+  aa.q = vw.q;
+  aa.k = vw.k;
+  aa.v = vw.v;
+  aa.ld_q = aa.ld_k = aa.ld_v = vw.ld;
+  aa.out = b.o;
+  aa.ld_o = hv;
+  aa.out_f32 = 1;
+  aa.q_offsets = aa.k_offsets = off_dev;
+  aa.ts_q = aa.ts_k = ts;
+  aa.rab_pos = w.rab_pos;
+  aa.rab_time = w.rab_time;
+  aa.items = b.items;
+  aa.n_items = (int)j.items;
+  HSTU_TRY(run_attention(&a, aa, false, s), "attention");
+  HSTU_TRY(launch_ln_gate(b.o, hv, vw.u, vw.ld, w.ln_gamma, w.ln_beta, a.ln_eps, b.g, hv, rows, hv,
+                          bf, s),
+           "layer norm gate");
+  HSTU_TRY(launch_gemm(b.g, hv, w.w2, hv, w.b2, d->residual ? x : nullptr, d->d_model, y,
+                       d->d_model, rows, d->d_model, hv, 0, bf, s),
+           "f2 projection");
+  return HSTU_OK;
+}
+
+// ---------------------------------------------------------------- M-FALCON
+struct MfPlan {
+  Jagged hist;
+  int64_t cand_total = 0;
+  size_t ws = 0;
+};
+
+struct MfBufs {
+  LayerBufs hist;             // history scratch (items, uvqk of the current layer unused)
+  std::vector<void*> hist_uvqk;  // per layer f1 output over the history (cached K and V)
+  void* hx[2];
+  void* c_uvqk;
+  float* c_o;
+  void* c_g;
+  void* cx[2];
+};
+
+void carve_mfalcon(Carver& c, const mfalcon_desc* d, const MfPlan& p, MfBufs* b) {
+  const hstu_layer_desc& ld = d->layer;
+  const hstu_attn_desc& a = ld.attn;
+  const size_t es = elt_size(a.dtype);
+  const int64_t f1 = 2LL * a.num_heads * (a.d_v + a.d_qk);
+  const int64_t hv = (int64_t)a.num_heads * a.d_v;
+  const int64_t nh = p.hist.total;
+  const int64_t m = std::min<int64_t>(d->microbatch, std::max<int64_t>(p.cand_total, 1));
+  b->hist.items = (int2*)c.take((size_t)p.hist.items * sizeof(int2));
+  b->hist.o = (float*)c.take((size_t)nh * hv * sizeof(float));
+  b->hist.g = c.take((size_t)nh * hv * es);
+  b->hist_uvqk.assign(ld.num_layers, nullptr);
+  for (int l = 0; l < ld.num_layers; ++l) b->hist_uvqk[l] = c.take((size_t)nh * f1 * es);
+  b->hx[0] = ld.num_layers > 1 ? c.take((size_t)nh * ld.d_model * es) : nullptr;
+  b->hx[1] = ld.num_layers > 2 ? c.take((size_t)nh * ld.d_model * es) : nullptr;
+  b->c_uvqk = c.take((size_t)m * f1 * es);
+  b->c_o = (float*)c.take((size_t)m * hv * sizeof(float));
+  b->c_g = c.take((size_t)m * hv * es);
+  b->cx[0] = ld.num_layers > 1 ? c.take((size_t)m * ld.d_model * es) : nullptr;
+  b->cx[1] = ld.num_layers > 2 ? c.take((size_t)m * ld.d_model * es) : nullptr;
+}
+
+hstu_status plan_mfalcon(const mfalcon_desc* d, const int64_t* hoff, const int64_t* coff,
+                         MfPlan* p) {
+  if (!d) return fail(HSTU_INVALID_ARGUMENT, "descriptor is NULL");
+  hstu_status st = check_layer_desc(&d->layer);
+  if (st) return st;
+  if (d->microbatch < 1) return fail(HSTU_INVALID_ARGUMENT, "microbatch must be >= 1");
+  const hstu_attn_desc& a = d->layer.attn;
+  st = check_offsets(hoff, a.batch, a.max_seq_len, attn_tile_rows(&a), "hist_offsets", &p->hist);
+  if (st) return st;
+  Jagged cj;
+  st = check_offsets(coff, a.batch, -1, 1, "cand_offsets", &cj);
+  if (st) return st;
+  for (int b = 0; b < a.batch; ++b) {
+    const int64_t nh = hoff[b + 1] - hoff[b], nc = coff[b + 1] - coff[b];
+    if (nc > 0 && nh + 1 > a.max_seq_len)
+      return fail(HSTU_INVALID_ARGUMENT,
+                  "user %d: history %lld plus the candidate exceeds max_seq_len %d", b,
+                  (long long)nh, a.max_seq_len);
+  }
+  p->cand_total = cj.total;
+  if ((int64_t)p->hist.items * a.num_heads >= (int64_t(1) << 31))
+    return fail(HSTU_UNSUPPORTED, "too many history tiles for one launch");
+  Carver c{nullptr};
+  MfBufs b;
+  carve_mfalcon(c, d, *p, &b);
+  p->ws = c.off;
+  return HSTU_OK;
+}
+
+}  // namespace
+
+// =========================================================================
+extern "C" {
+
+int hstu_version(void) { return HSTU_VERSION; }
+
+const char* hstu_status_string(hstu_status s) {
+  switch (s) {
+    case HSTU_OK: return "HSTU_OK";
+    case HSTU_INVALID_ARGUMENT: return "HSTU_INVALID_ARGUMENT";
+    case HSTU_UNSUPPORTED: return "HSTU_UNSUPPORTED";
+    case HSTU_WORKSPACE_TOO_SMALL: return "HSTU_WORKSPACE_TOO_SMALL";
+    case HSTU_DEVICE_ERROR: return "HSTU_DEVICE_ERROR";
+  }
+  return "unknown hstu_status";
+}
+
+const char* hstu_last_error(void) { return g_err.c_str(); }
+
+hstu_status hstu_attn_workspace_size(const hstu_attn_desc* desc, const int64_t* seq_offsets_host,
+                                     size_t* bytes) {
+  if (!bytes) return fail(HSTU_INVALID_ARGUMENT, "bytes is NULL");
+  AttnPlan p;
+  hstu_status st = plan_attn(desc, seq_offsets_host, true, &p);
+  if (st) return st;
+  *bytes = p.ws;
+  return HSTU_OK;
+}
+
+hstu_status hstu_attn_fwd(const hstu_attn_desc* desc, const int64_t* seq_offsets_host,
+                          const int64_t* seq_offsets, const int64_t* timestamps, const void* q,
+                          const void* k, const void* v, const float* rab_pos,
+                          const float* rab_time, const void* u, const float* ln_gamma,
+                          const float* ln_beta, void* out, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  AttnPlan p;
+  hstu_status st = plan_attn(desc, seq_offsets_host, u != nullptr, &p);
+  if (st) return st;
+  if (u && (st = check_eps(desc->ln_eps))) return st;
+  if (p.j.total == 0) return HSTU_OK;
+  if (!seq_offsets) return fail(HSTU_INVALID_ARGUMENT, "device seq_offsets is NULL");
+  if (!q || !k || !v || !out) return fail(HSTU_INVALID_ARGUMENT, "q, k, v and out are required");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || (u && !aligned16(u)))
+    return fail(HSTU_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
+  if (workspace_bytes < p.ws || (!workspace && p.ws))
+    return fail(HSTU_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes (got %zu)", p.ws,
+                workspace_bytes);
+  if (((uintptr_t)workspace & (kAlign - 1)) != 0)
+    return fail(HSTU_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  Carver c{(char*)workspace};
+  int2* items = (int2*)c.take((size_t)p.j.items * sizeof(int2));
+  float* o32 = u ? (float*)c.take((size_t)p.j.total * desc->num_heads * desc->d_v * 4) : nullptr;
+  HSTU_TRY(launch_plan_causal(seq_offsets, desc->batch, attn_tile_rows(desc), p.j.max_tiles, items,
+                              (int)p.j.items, s),
+           "tile planner");
+  AttnArgs a = base_args(desc);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.ld_q = a.ld_k = (int64_t)desc->num_heads * desc->d_qk;
+  a.ld_v = (int64_t)desc->num_heads * desc->d_v;
+  a.out = u ? (void*)o32 : out;
+  a.ld_o = (int64_t)desc->num_heads * desc->d_v;
+  a.out_f32 = u ? 1 : (desc->dtype == HSTU_F32);
+  a.q_offsets = a.k_offsets = seq_offsets;
+  a.ts_q = a.ts_k = timestamps;
+  a.rab_pos = rab_pos;
+  a.rab_time = rab_time;
+  a.items = items;
+  a.n_items = (int)p.j.items;
+  HSTU_TRY(run_attention(desc, a, false, s), "attention");
+  if (u) {
+    const int hv = desc->num_heads * desc->d_v;
+    HSTU_TRY(launch_ln_gate(o32, hv, u, hv, ln_gamma, ln_beta, desc->ln_eps, out, hv, p.j.total, hv,
+                            desc->dtype == HSTU_BF16, s),
+             "layer norm gate");
+  }
+  return HSTU_OK;
+}
+
+hstu_status hstu_layer_workspace_size(const hstu_layer_desc* desc,
+                                      const int64_t* seq_offsets_host, size_t* bytes) {
+  if (!bytes) return fail(HSTU_INVALID_ARGUMENT, "bytes is NULL");
+  LayerPlan p;
+  hstu_status st = plan_layer(desc, seq_offsets_host, &p);
+  if (st) return st;
+  *bytes = p.ws;
+  return HSTU_OK;
+}
+
+hstu_status hstu_layer_fwd(const hstu_layer_desc* desc, const int64_t* seq_offsets_host,
+                           const int64_t* seq_offsets, const int64_t* timestamps, const void* x,
+                           const hstu_layer_weights* weights, void* y, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  LayerPlan p;
+  hstu_status st = plan_layer(desc, seq_offsets_host, &p);
+  if (st) return st;
+  if ((st = check_weights(weights, desc->num_layers))) return st;
+  if (p.j.total == 0) return HSTU_OK;
+  if (!seq_offsets) return fail(HSTU_INVALID_ARGUMENT, "device seq_offsets is NULL");
+  if (!x || !y) return fail(HSTU_INVALID_ARGUMENT, "x and y are required");
+  if (!aligned16(x) || !aligned16(y))
+    return fail(HSTU_INVALID_ARGUMENT, "x and y must be 16-byte aligned");
+  if (workspace_bytes < p.ws || (!workspace && p.ws))
+    return fail(HSTU_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes (got %zu)", p.ws,
+                workspace_bytes);
+  if (((uintptr_t)workspace & (kAlign - 1)) != 0)
+    return fail(HSTU_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  Carver c{(char*)workspace};
+  LayerBufs b;
+  carve_layer(c, desc, p.j.total, p.j.items, &b);
+  const int L = desc->num_layers;
+  const void* in = x;
+  for (int l = 0; l < L; ++l) {
+    // layer outputs alternate between y and tmp so that the last one lands in y
+    void* out = ((L - 1 - l) % 2 == 0) ? y : b.tmp;
+    st = layer_once(desc, seq_offsets, timestamps, p.j, in, weights[l], out, b, l > 0, s, false);
+    if (st) return st;
+    in = out;
+  }
+  return HSTU_OK;
+}
+
+hstu_status mfalcon_workspace_size(const mfalcon_desc* desc, const int64_t* hist_offsets_host,
+                                   const int64_t* cand_offsets_host, size_t* bytes) {
+  if (!bytes) return fail(HSTU_INVALID_ARGUMENT, "bytes is NULL");
+  MfPlan p;
+  hstu_status st = plan_mfalcon(desc, hist_offsets_host, cand_offsets_host, &p);
+  if (st) return st;
+  *bytes = p.ws;
+  return HSTU_OK;
+}
+
+hstu_status mfalcon_score(const mfalcon_desc* desc, const int64_t* hist_offsets_host,
+                          const int64_t* hist_offsets, const int64_t* hist_ts, const void* hist_x,
+                          const int64_t* cand_offsets_host, const int64_t* cand_offsets,
+                          const int64_t* cand_ts, const void* cand_x,
+                          const hstu_layer_weights* weights, const float* w_head,
+                          void* cand_out, float* cand_logit, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  MfPlan p;
+  hstu_status st = plan_mfalcon(desc, hist_offsets_host, cand_offsets_host, &p);
+  if (st) return st;
+  const hstu_layer_desc& ld = desc->layer;
+  const hstu_attn_desc& a = ld.attn;
+  if ((st = check_weights(weights, ld.num_layers))) return st;
+  if ((hist_ts == nullptr) != (cand_ts == nullptr))
+    return fail(HSTU_INVALID_ARGUMENT, "hist_ts and cand_ts must both be set or both be NULL");
+  if (p.cand_total == 0) return HSTU_OK;
+  if (!hist_offsets || !cand_offsets)
+    return fail(HSTU_INVALID_ARGUMENT, "device offsets are required");
+  if (!cand_x || !cand_out || (p.hist.total > 0 && !hist_x))
+    return fail(HSTU_INVALID_ARGUMENT, "hist_x, cand_x and cand_out are required");
+  if (!aligned16(cand_x) || !aligned16(cand_out) || (hist_x && !aligned16(hist_x)))
+    return fail(HSTU_INVALID_ARGUMENT, "activation pointers must be 16-byte aligned");
+  if (cand_logit && !w_head) return fail(HSTU_INVALID_ARGUMENT, "cand_logit needs w_head");
+  if (workspace_bytes < p.ws || (!workspace && p.ws))
+    return fail(HSTU_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes (got %zu)", p.ws,
+                workspace_bytes);
+  if (((uintptr_t)workspace & (kAlign - 1)) != 0)
+    return fail(HSTU_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  Carver c{(char*)workspace};
+  MfBufs b;
+  carve_mfalcon(c, desc, p, &b);
+  const int L = ld.num_layers;
+  const int bf = a.dtype == HSTU_BF16;
+  const size_t es = elt_size(a.dtype);
+  const int hv = a.num_heads * a.d_v;
+  const int dm = ld.d_model;
+
+  // history pass, once: layers 0..L-2 in full; layer L-1 only needs its K and V
+  if (p.hist.total > 0) {
+    LayerBufs hb = b.hist;
+    const void* in = hist_x;
+    for (int l = 0; l < L; ++l) {
+      hb.uvqk = b.hist_uvqk[l];
+      void* out = (l < L - 1) ? b.hx[l % 2] : nullptr;
+      st = layer_once(&ld, hist_offsets, hist_ts, p.hist, in, weights[l], out, hb, l > 0, s,
+                      l == L - 1);
+      if (st) return st;
+      in = out;
+    }
+  }
+
+  // candidate microbatches, in global candidate order
+  const int B = a.batch;
+  const int64_t m = desc->microbatch;
+  for (int64_t m0 = 0; m0 < p.cand_total; m0 += m) {
+    const int64_t m1 = std::min(m0 + m, p.cand_total);
+    const int64_t rows = m1 - m0;
+    // users whose candidate range overlaps [m0, m1)
+    int ub = (int)(std::upper_bound(cand_offsets_host, cand_offsets_host + B + 1, m0) -
+                   cand_offsets_host) - 1;
+    int ue = (int)(std::lower_bound(cand_offsets_host, cand_offsets_host + B + 1, m1) -
+                   cand_offsets_host);  // one past the last overlapping user
+    ub = std::max(ub, 0);
+    ue = std::min(ue, B);
+    int64_t max_rows = 0;
+    for (int u = ub; u < ue; ++u) {
+      const int64_t cs = std::max(cand_offsets_host[u], m0), ce = std::min(cand_offsets_host[u + 1], m1);
+      max_rows = std::max(max_rows, ce - cs);
+    }
+    const void* in = (const char*)cand_x + (size_t)m0 * dm * es;
+    for (int l = 0; l < L; ++l) {
+      const hstu_layer_weights& w = weights[l];
+      void* out = (l == L - 1) ? (void*)((char*)cand_out + (size_t)m0 * dm * es) : b.cx[l % 2];
+      const int64_t f1 = 2LL * a.num_heads * (a.d_v + a.d_qk);
+      HSTU_TRY(launch_gemm(in, dm, w.w1, dm, w.b1, nullptr, 0, b.c_uvqk, f1, rows, (int)f1, dm, 1,
+                           bf, s),
+               "candidate f1 projection");
+      const UVQK cv = split_view(b.c_uvqk, a);
+      const UVQK hvw = split_view(b.hist_uvqk[l], a);
+      AttnArgs aa = base_args(&a);
+      aa.q = cv.q;
+      aa.ld_q = cv.ld;
+      aa.kc = cv.k;
+      aa.vc = cv.v;
+      aa.ld_kc = aa.ld_vc = cv.ld;
+      aa.k = hvw.k;
+      aa.v = hvw.v;
+      aa.ld_k = aa.ld_v = hvw.ld;
+      aa.out = b.c_o;
+      aa.ld_o = hv;
+      aa.out_f32 = 1;
+      aa.q_offsets = cand_offsets;
+      aa.k_offsets = hist_offsets;
+      aa.ts_q = cand_ts;
+      aa.ts_k = hist_ts;
+      aa.rab_pos = w.rab_pos;
+      aa.rab_time = w.rab_time;
+      aa.row_begin = m0;
+      aa.row_end = m1;
+      aa.max_user_rows = max_rows;
+      for (int u0 = ub; u0 < ue; u0 += 65535) {
+        aa.user_begin = u0;
+        aa.n_users = std::min(ue - u0, 65535);
+        HSTU_TRY(run_attention(&a, aa, true, s), "candidate attention");
+      }
+      HSTU_TRY(launch_ln_gate(b.c_o, hv, cv.u, cv.ld, w.ln_gamma, w.ln_beta, a.ln_eps, b.c_g, hv,
+                              rows, hv, bf, s),
+               "candidate layer norm gate");
+      HSTU_TRY(launch_gemm(b.c_g, hv, w.w2, hv, w.b2, ld.residual ? in : nullptr, dm, out, dm, rows,
+                           dm, hv, 0, bf, s),
+               "candidate f2 projection");
+      in = out;
+    }
+    if (cand_logit)
+      HSTU_TRY(launch_rowdot((const char*)cand_out + (size_t)m0 * dm * es, dm, w_head,
+                             cand_logit + m0, rows, dm, bf, s),
+               "candidate logit");
+  }
+  return HSTU_OK;
+}
+
+hstu_status hstu_debug_buckets(const hstu_attn_desc* desc, const int64_t* seq_offsets_host,
+                               const int64_t* seq_offsets, const int64_t* timestamps, int32_t seq,
+                               int32_t* pos_bucket, int32_t* time_bucket, void* stream) {
+  hstu_status st = check_attn_desc(desc);
+  if (st) return st;
+  Jagged j;
+  st = check_offsets(seq_offsets_host, desc->batch, desc->max_seq_len, 1, "seq_offsets", &j);
+  if (st) return st;
+  if (seq < 0 || seq >= desc->batch) return fail(HSTU_INVALID_ARGUMENT, "seq out of range");
+  const int64_t n = seq_offsets_host[seq + 1] - seq_offsets_host[seq];
+  if (n > 46340) return fail(HSTU_UNSUPPORTED, "sequence too long for the n x n export");
+  if (n == 0) return HSTU_OK;
+  if (!seq_offsets || !pos_bucket || !time_bucket)
+    return fail(HSTU_INVALID_ARGUMENT, "device pointers are required");
+  HSTU_TRY(launch_debug_buckets(seq_offsets, timestamps, seq, (int)n, desc->num_pos_buckets,
+                                desc->num_time_buckets, pos_bucket, time_bucket,
+                                (hipStream_t)stream),
+           "bucket export");
+  return HSTU_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,62 @@
+// Work decoding shared by the attention kernels.
+#pragma once
+#include "common.h"
+#include "kernels.h"
+
+namespace hstu {
+
+struct TileDecode {
+  int h;
+  int64_t q_base;   // global row of tile row 0 (candidate mode: global candidate row)
+  int64_t q_local;  // row index into q/out/kc/vc of tile row 0
+  int rows;         // valid query rows in the tile
+  int64_t k_base;   // global row of key 0
+  int64_t nk;       // keys that hold data (causal: whole sequence; candidates: history)
+  int64_t kend;     // keys that can be visible (causal: up to the last row of the tile)
+  int64_t qpos0;    // position of tile row 0 (causal) or of every candidate (n_h)
+  bool valid;
+};
+
+template <bool CAND>
+__device__ __forceinline__ TileDecode decode(const AttnArgs& a, int bm) {
+  TileDecode d;
+  d.valid = false;
+  if (!CAND) {
+    const int item = blockIdx.x / a.H;
+    d.h = blockIdx.x % a.H;
+    if (item >= a.n_items) return d;
+    const int2 it = a.items[item];
+    if (it.x < 0 || it.x >= a.batch || it.y < 0) return d;
+    const int64_t s0 = a.q_offsets[it.x];
+    const int64_t n = a.q_offsets[it.x + 1] - s0;
+    const int64_t r0 = (int64_t)it.y * bm;
+    if (r0 >= n) return d;
+    d.rows = (int)(n - r0 < bm ? n - r0 : bm);
+    d.q_base = s0 + r0;
+    d.q_local = d.q_base;
+    d.k_base = s0;
+    d.nk = n;
+    d.kend = r0 + d.rows;
+    d.qpos0 = r0;
+  } else {
+    d.h = blockIdx.x % a.H;
+    const int tile = blockIdx.x / a.H;
+    const int b = a.user_begin + blockIdx.y;
+    int64_t cs = a.q_offsets[b], ce = a.q_offsets[b + 1];
+    cs = cs > a.row_begin ? cs : a.row_begin;
+    ce = ce < a.row_end ? ce : a.row_end;
+    const int64_t r0 = cs + (int64_t)tile * bm;
+    if (r0 >= ce) return d;
+    d.rows = (int)(ce - r0 < bm ? ce - r0 : bm);
+    d.q_base = r0;
+    d.q_local = r0 - a.row_begin;
+    d.k_base = a.k_offsets[b];
+    d.nk = a.k_offsets[b + 1] - d.k_base;
+    d.kend = d.nk;
+    d.qpos0 = d.nk;
+  }
+  d.valid = true;
+  return d;
+}
+
+}  // namespace hstu

@@ -1,0 +1,69 @@
+// Internal launch interface between the C-ABI host layer and the HIP kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hstu {
+
+// One attention launch. Row strides (ld_*) are in elements. Tensor bases point
+// at head 0 of row 0; head h sits at column h * d within each row.
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;          // bf16 or f32 (out_f32), [rows, H, d_v] with stride ld_o
+  int64_t ld_q, ld_k, ld_v, ld_o;
+  const int64_t* q_offsets;   // causal: sequence offsets; candidate mode: candidate offsets
+  const int64_t* k_offsets;   // causal: same as q_offsets; candidate mode: history offsets
+  const int64_t* ts_q;        // per query row, or NULL
+  const int64_t* ts_k;        // per key row, or NULL
+  const float* rab_pos;       // [H][P] or NULL
+  const float* rab_time;      // [H][T] or NULL
+  int batch;                  // number of sequences (causal) or users (candidate mode)
+  int H, d_qk, d_v, P, T;
+  float inv_n;
+  int out_f32;
+  // causal mode: work list of (sequence, query tile), longest first
+  const int2* items;
+  int n_items;
+  // candidate mode: candidates' own K and V rows (the self term), the global
+  // candidate row range of this microbatch and the users overlapping it
+  const void* kc;
+  const void* vc;
+  int64_t ld_kc, ld_vc;
+  int64_t row_begin, row_end;
+  int user_begin, n_users;
+  int64_t max_user_rows;      // most candidate rows any one user has in this microbatch
+};
+
+// Tile sizes (query rows per work item) of the two attention kernels.
+constexpr int kMfmaRows = 128;
+constexpr int kSimpleRows = 64;
+
+// True when the MFMA kernel handles this shape (bf16, d_qk == d_v in {32,64,128}
+// and the bias tables fit its LDS).
+bool attn_mfma_supported(int dtype_bf16, int d_qk, int d_v, int P, int T);
+
+hipError_t launch_plan_causal(const int64_t* offsets, int B, int tile_rows, int max_tiles,
+                              int2* items, int n_items, hipStream_t s);
+hipError_t launch_attn_simple(const AttnArgs& a, int use_bf16, bool cand, hipStream_t s);
+hipError_t launch_attn_mfma(const AttnArgs& a, bool cand, hipStream_t s);
+
+// out[r, :] = (LN(o[r, :]) * gamma + beta) (.) u[r, :], width w, over `rows` rows.
+hipError_t launch_ln_gate(const float* o, int64_t ld_o, const void* u, int64_t ld_u,
+                          const float* gamma, const float* beta, float eps, void* out,
+                          int64_t ld_out, int64_t rows, int w, int use_bf16, hipStream_t s);
+
+// C[M,N] = epi(A[M,K] W[N,K]^T + bias[N]); epi = SiLU when silu, + R[M,N] when R.
+hipError_t launch_gemm(const void* A, int64_t lda, const void* W, int64_t ldw,
+                       const float* bias, const void* R, int64_t ldr, void* C, int64_t ldc,
+                       int64_t M, int N, int K, int silu, int use_bf16, hipStream_t s);
+
+// logit[r] = sum_c y[r, c] * w[c] (fp32 accumulate).
+hipError_t launch_rowdot(const void* y, int64_t ld_y, const float* w, float* logit, int64_t rows,
+                         int d, int use_bf16, hipStream_t s);
+
+hipError_t launch_debug_buckets(const int64_t* offsets, const int64_t* ts, int seq, int n, int P,
+                                int T, int32_t* pos_bucket, int32_t* time_bucket, hipStream_t s);
+
+}  // namespace hstu

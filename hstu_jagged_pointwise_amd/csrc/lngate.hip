@@ -1,0 +1,117 @@
+// Norm(AV) (.) U, the gating of eq. 3 of the HSTU layer ("What an HSTU layer
+// changes" and "Gating instead of a separate FFN", HSTU chapter). The pooled
+// value of each token, all H*d_v attention outputs of the row, is
+// layer-normalised (biased variance, fp32 statistics), then scaled by gamma,
+// shifted by beta and multiplied elementwise by the gate U.
+//
+// This step is bound by HBM bandwidth. One wavefront owns one row. When the row
+// is at most 64 * 16 values wide it stays in registers, so it is read once;
+// otherwise three passes reread it (from L2). The statistics use two passes
+// over the values (mean, then squared deviations), not E[x^2] - E[x]^2.
+#include "common.h"
+#include "kernels.h"
+
+namespace hstu {
+
+template <typename T, int NPL>
+__global__ __launch_bounds__(256) void ln_gate_reg_kernel(const float* __restrict__ o, int64_t ld_o,
+                                                          const T* __restrict__ u, int64_t ld_u,
+                                                          const float* __restrict__ gamma,
+                                                          const float* __restrict__ beta, float eps,
+                                                          T* __restrict__ out, int64_t ld_out,
+                                                          int64_t rows, int w) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const float* orow = o + row * ld_o;
+  float x[NPL];
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    const int c = lane + 64 * i;
+    x[i] = c < w ? orow[c] : 0.f;
+    sum += x[i];
+  }
+  const float mean = wave_sum(sum) / (float)w;
+  float sq = 0.f;
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    const int c = lane + 64 * i;
+    const float d = c < w ? x[i] - mean : 0.f;
+    sq = fmaf(d, d, sq);
+  }
+  const float rstd = rsqrtf(wave_sum(sq) / (float)w + eps);
+  const T* urow = u + row * ld_u;
+  T* dst = out + row * ld_out;
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    const int c = lane + 64 * i;
+    if (c < w) {
+      float y = (x[i] - mean) * rstd;
+      if (gamma) y *= gamma[c];
+      if (beta) y += beta[c];
+      dst[c] = from_f32<T>(y * to_f32<T>(urow[c]));
+    }
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void ln_gate_loop_kernel(const float* __restrict__ o, int64_t ld_o,
+                                                           const T* __restrict__ u, int64_t ld_u,
+                                                           const float* __restrict__ gamma,
+                                                           const float* __restrict__ beta, float eps,
+                                                           T* __restrict__ out, int64_t ld_out,
+                                                           int64_t rows, int w) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const float* orow = o + row * ld_o;
+  float sum = 0.f;
+  for (int c = lane; c < w; c += 64) sum += orow[c];
+  const float mean = wave_sum(sum) / (float)w;
+  float sq = 0.f;
+  for (int c = lane; c < w; c += 64) {
+    const float d = orow[c] - mean;
+    sq = fmaf(d, d, sq);
+  }
+  const float rstd = rsqrtf(wave_sum(sq) / (float)w + eps);
+  const T* urow = u + row * ld_u;
+  T* dst = out + row * ld_out;
+  for (int c = lane; c < w; c += 64) {
+    float y = (orow[c] - mean) * rstd;
+    if (gamma) y *= gamma[c];
+    if (beta) y += beta[c];
+    dst[c] = from_f32<T>(y * to_f32<T>(urow[c]));
+  }
+}
+
+template <typename T>
+static hipError_t ln_dispatch(const float* o, int64_t ld_o, const void* u, int64_t ld_u,
+                              const float* gamma, const float* beta, float eps, void* out,
+                              int64_t ld_out, int64_t rows, int w, hipStream_t s) {
+  const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+  const T* uu = (const T*)u;
+  T* oo = (T*)out;
+  const int npl = (w + 63) / 64;
+#define HSTU_LN_CASE(N)                                                                          \
+  if (npl <= N) {                                                                                \
+    hipLaunchKernelGGL((ln_gate_reg_kernel<T, N>), grid, block, 0, s, o, ld_o, uu, ld_u, gamma,  \
+                       beta, eps, oo, ld_out, rows, w);                                          \
+    return hipGetLastError();                                                                    \
+  }
+  HSTU_LN_CASE(1) HSTU_LN_CASE(2) HSTU_LN_CASE(4) HSTU_LN_CASE(8) HSTU_LN_CASE(16)
+#undef HSTU_LN_CASE
+  hipLaunchKernelGGL((ln_gate_loop_kernel<T>), grid, block, 0, s, o, ld_o, uu, ld_u, gamma, beta,
+                     eps, oo, ld_out, rows, w);
+  return hipGetLastError();
+}
+
+hipError_t launch_ln_gate(const float* o, int64_t ld_o, const void* u, int64_t ld_u,
+                          const float* gamma, const float* beta, float eps, void* out,
+                          int64_t ld_out, int64_t rows, int w, int bf16flag, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  return bf16flag ? ln_dispatch<bf16>(o, ld_o, u, ld_u, gamma, beta, eps, out, ld_out, rows, w, s)
+                  : ln_dispatch<float>(o, ld_o, u, ld_u, gamma, beta, eps, out, ld_out, rows, w, s);
+}
+
+}  // namespace hstu

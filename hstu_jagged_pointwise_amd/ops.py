@@ -1,0 +1,279 @@
+"""ctypes binding to libhstu.so (C ABI in include/hstu.h).
+
+This layer only marshals arguments. It turns torch tensors into device
+pointers, builds the descriptor structs, allocates the workspace with torch
+(PyTorch is used for device memory and streams) and raises on a non-OK status.
+Every step of the computation runs in libhstu's HIP kernels. There is no
+fallback: if the library is missing, importing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libhstu.so")
+
+HSTU_OK, HSTU_INVALID_ARGUMENT, HSTU_UNSUPPORTED, HSTU_WORKSPACE_TOO_SMALL, HSTU_DEVICE_ERROR = range(5)
+HSTU_F32, HSTU_BF16 = 0, 1
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -m hstu_jagged_pointwise_amd.build` "
+        "(hipcc, gfx950). There is no non-HIP fallback.")
+lib = ctypes.CDLL(LIB_PATH)
+
+
+class hstu_attn_desc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_heads", ctypes.c_int32), ("d_qk", ctypes.c_int32),
+                ("d_v", ctypes.c_int32), ("max_seq_len", ctypes.c_int32),
+                ("num_pos_buckets", ctypes.c_int32), ("num_time_buckets", ctypes.c_int32),
+                ("dtype", ctypes.c_int), ("ln_eps", ctypes.c_float)]
+
+
+class hstu_layer_desc(ctypes.Structure):
+    _fields_ = [("attn", hstu_attn_desc), ("d_model", ctypes.c_int32), ("residual", ctypes.c_int32),
+                ("num_layers", ctypes.c_int32)]
+
+
+class hstu_layer_weights(ctypes.Structure):
+    _fields_ = [("w1", ctypes.c_void_p), ("b1", ctypes.c_void_p), ("rab_pos", ctypes.c_void_p),
+                ("rab_time", ctypes.c_void_p), ("ln_gamma", ctypes.c_void_p),
+                ("ln_beta", ctypes.c_void_p), ("w2", ctypes.c_void_p), ("b2", ctypes.c_void_p)]
+
+
+class mfalcon_desc(ctypes.Structure):
+    _fields_ = [("layer", hstu_layer_desc), ("microbatch", ctypes.c_int32)]
+
+
+_P = ctypes.c_void_p
+_I64P = ctypes.POINTER(ctypes.c_int64)
+_SZP = ctypes.POINTER(ctypes.c_size_t)
+_sig = {
+    "hstu_version": ([], ctypes.c_int),
+    "hstu_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    "hstu_last_error": ([], ctypes.c_char_p),
+    "hstu_attn_workspace_size": ([ctypes.POINTER(hstu_attn_desc), _I64P, _SZP], ctypes.c_int),
+    "hstu_attn_fwd": ([ctypes.POINTER(hstu_attn_desc), _I64P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                       _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "hstu_layer_workspace_size": ([ctypes.POINTER(hstu_layer_desc), _I64P, _SZP], ctypes.c_int),
+    "hstu_layer_fwd": ([ctypes.POINTER(hstu_layer_desc), _I64P, _P, _P, _P,
+                        ctypes.POINTER(hstu_layer_weights), _P, _P, ctypes.c_size_t, _P],
+                       ctypes.c_int),
+    "mfalcon_workspace_size": ([ctypes.POINTER(mfalcon_desc), _I64P, _I64P, _SZP], ctypes.c_int),
+    "mfalcon_score": ([ctypes.POINTER(mfalcon_desc), _I64P, _P, _P, _P, _I64P, _P, _P, _P,
+                       ctypes.POINTER(hstu_layer_weights), _P, _P, _P, _P, ctypes.c_size_t, _P],
+                      ctypes.c_int),
+    "hstu_debug_buckets": ([ctypes.POINTER(hstu_attn_desc), _I64P, _P, _P, ctypes.c_int32, _P, _P,
+                            _P], ctypes.c_int),
+}
+for _name, (_args, _res) in _sig.items():
+    _f = getattr(lib, _name)
+    _f.argtypes = _args
+    _f.restype = _res
+
+EXPORTED = tuple(_sig)
+
+
+class HstuError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{lib.hstu_status_string(status).decode()}: {message}")
+        self.status = status
+
+
+def _check(status: int):
+    if status != HSTU_OK:
+        raise HstuError(status, lib.hstu_last_error().decode())
+
+
+def hstu_version() -> int:
+    return lib.hstu_version()
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libhstu must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _host_offsets(dev: torch.Tensor, host) -> np.ndarray:
+    if host is None:
+        host = dev.detach().to("cpu")
+    if isinstance(host, torch.Tensor):
+        host = host.numpy()
+    return np.ascontiguousarray(host, dtype=np.int64)
+
+
+def _i64p(a: np.ndarray):
+    return a.ctypes.data_as(_I64P)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return HSTU_F32
+    if t.dtype == torch.bfloat16:
+        return HSTU_BF16
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]):
+    if workspace is not None:
+        return workspace, workspace.numel() * workspace.element_size()
+    if nbytes == 0:
+        return None, 0
+    return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
+
+
+def attn_desc(batch, num_heads, d_qk, d_v, max_seq_len, num_pos_buckets, num_time_buckets,
+              dtype_code, ln_eps=1e-5) -> hstu_attn_desc:
+    return hstu_attn_desc(int(batch), int(num_heads), int(d_qk), int(d_v), int(max_seq_len),
+                          int(num_pos_buckets), int(num_time_buckets), int(dtype_code),
+                          float(ln_eps))
+
+
+# ---------------------------------------------------------------------------
+# entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------
+def hstu_attn_workspace_size(desc: hstu_attn_desc, seq_offsets_host: np.ndarray) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib.hstu_attn_workspace_size(ctypes.byref(desc), _i64p(seq_offsets_host), ctypes.byref(n)))
+    return n.value
+
+
+def hstu_attn_fwd(seq_offsets: torch.Tensor, timestamps: Optional[torch.Tensor], q, k, v,
+                  rab_pos=None, rab_time=None, *, max_seq_len: int, num_pos_buckets=None,
+                  num_time_buckets=None, u=None, ln_gamma=None, ln_beta=None, ln_eps=1e-5,
+                  out=None, workspace=None, seq_offsets_host=None, stream=None) -> torch.Tensor:
+    """Jagged causal HSTU attention; with u, the gated LayerNorm output. See include/hstu.h."""
+    host = _host_offsets(seq_offsets, seq_offsets_host)
+    T_tot, H, d_qk = q.shape
+    d_v = v.shape[2]
+    P = rab_pos.shape[1] if rab_pos is not None else (num_pos_buckets or 1)
+    T = rab_time.shape[1] if rab_time is not None else (num_time_buckets or 1)
+    desc = attn_desc(len(host) - 1, H, d_qk, d_v, max_seq_len, P, T, _dtype_code(q), ln_eps)
+    if out is None:
+        out = torch.empty((T_tot, H, d_v), dtype=q.dtype, device=q.device)
+    ws, nbytes = _workspace(hstu_attn_workspace_size(desc, host), q.device, workspace)
+    _check(lib.hstu_attn_fwd(ctypes.byref(desc), _i64p(host), _ptr(seq_offsets), _ptr(timestamps),
+                             _ptr(q), _ptr(k), _ptr(v), _ptr(rab_pos), _ptr(rab_time), _ptr(u),
+                             _ptr(ln_gamma), _ptr(ln_beta), _ptr(out), _ptr(ws), nbytes,
+                             _stream(stream)))
+    return out
+
+
+@dataclass
+class LayerWeights:
+    """Device tensors of one HSTU layer. w1 [2H(d_v+d_qk), d_model] and
+    w2 [d_model, H*d_v] are stored [out, in] in the activation dtype; everything
+    else is fp32 or None."""
+    w1: torch.Tensor
+    w2: torch.Tensor
+    b1: Optional[torch.Tensor] = None
+    b2: Optional[torch.Tensor] = None
+    rab_pos: Optional[torch.Tensor] = None
+    rab_time: Optional[torch.Tensor] = None
+    ln_gamma: Optional[torch.Tensor] = None
+    ln_beta: Optional[torch.Tensor] = None
+
+    def c_struct(self) -> hstu_layer_weights:
+        return hstu_layer_weights(_ptr(self.w1), _ptr(self.b1), _ptr(self.rab_pos),
+                                  _ptr(self.rab_time), _ptr(self.ln_gamma), _ptr(self.ln_beta),
+                                  _ptr(self.w2), _ptr(self.b2))
+
+
+def _weights_array(layers: Sequence[LayerWeights]):
+    arr = (hstu_layer_weights * len(layers))()
+    for i, w in enumerate(layers):
+        arr[i] = w.c_struct()
+    return arr
+
+
+def layer_desc(layers: Sequence[LayerWeights], batch, num_heads, d_qk, d_v, d_model, max_seq_len,
+               dtype_code, ln_eps=1e-5, residual=0, num_pos_buckets=None, num_time_buckets=None):
+    w0 = layers[0]
+    P = w0.rab_pos.shape[1] if w0.rab_pos is not None else (num_pos_buckets or 1)
+    T = w0.rab_time.shape[1] if w0.rab_time is not None else (num_time_buckets or 1)
+    a = attn_desc(batch, num_heads, d_qk, d_v, max_seq_len, P, T, dtype_code, ln_eps)
+    return hstu_layer_desc(a, int(d_model), int(residual), len(layers))
+
+
+def hstu_layer_workspace_size(desc: hstu_layer_desc, seq_offsets_host: np.ndarray) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib.hstu_layer_workspace_size(ctypes.byref(desc), _i64p(seq_offsets_host), ctypes.byref(n)))
+    return n.value
+
+
+def hstu_layer_fwd(seq_offsets, timestamps, x, layers: Sequence[LayerWeights], *, num_heads, d_qk,
+                   d_v, max_seq_len, ln_eps=1e-5, residual=0, out=None, workspace=None,
+                   seq_offsets_host=None, stream=None) -> torch.Tensor:
+    """A stack of len(layers) HSTU layers over a jagged batch (eqs. 1-3)."""
+    host = _host_offsets(seq_offsets, seq_offsets_host)
+    desc = layer_desc(layers, len(host) - 1, num_heads, d_qk, d_v, x.shape[1], max_seq_len,
+                      _dtype_code(x), ln_eps, residual)
+    if out is None:
+        out = torch.empty_like(x)
+    ws, nbytes = _workspace(hstu_layer_workspace_size(desc, host), x.device, workspace)
+    arr = _weights_array(layers)
+    _check(lib.hstu_layer_fwd(ctypes.byref(desc), _i64p(host), _ptr(seq_offsets), _ptr(timestamps),
+                              _ptr(x), arr, _ptr(out), _ptr(ws), nbytes, _stream(stream)))
+    return out
+
+
+def mfalcon_workspace_size(desc: mfalcon_desc, hist_offsets_host, cand_offsets_host) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib.mfalcon_workspace_size(ctypes.byref(desc), _i64p(hist_offsets_host),
+                                      _i64p(cand_offsets_host), ctypes.byref(n)))
+    return n.value
+
+
+def mfalcon_score(hist_offsets, hist_ts, hist_x, cand_offsets, cand_ts, cand_x,
+                  layers: Sequence[LayerWeights], *, num_heads, d_qk, d_v, max_seq_len, microbatch,
+                  w_head=None, ln_eps=1e-5, residual=0, out=None, logit=None, workspace=None,
+                  hist_offsets_host=None, cand_offsets_host=None, stream=None):
+    """M-FALCON: history once, candidates in microbatches. Returns (cand_out, logits or None)."""
+    hh = _host_offsets(hist_offsets, hist_offsets_host)
+    ch = _host_offsets(cand_offsets, cand_offsets_host)
+    ld = layer_desc(layers, len(hh) - 1, num_heads, d_qk, d_v, cand_x.shape[1], max_seq_len,
+                    _dtype_code(cand_x), ln_eps, residual)
+    desc = mfalcon_desc(ld, int(microbatch))
+    if out is None:
+        out = torch.empty_like(cand_x)
+    if logit is None and w_head is not None:
+        logit = torch.empty(cand_x.shape[0], dtype=torch.float32, device=cand_x.device)
+    ws, nbytes = _workspace(mfalcon_workspace_size(desc, hh, ch), cand_x.device, workspace)
+    arr = _weights_array(layers)
+    _check(lib.mfalcon_score(ctypes.byref(desc), _i64p(hh), _ptr(hist_offsets), _ptr(hist_ts),
+                             _ptr(hist_x), _i64p(ch), _ptr(cand_offsets), _ptr(cand_ts),
+                             _ptr(cand_x), arr, _ptr(w_head), _ptr(out), _ptr(logit), _ptr(ws),
+                             nbytes, _stream(stream)))
+    return out, logit
+
+
+def hstu_debug_buckets(seq_offsets, timestamps, seq: int, *, max_seq_len, num_pos_buckets,
+                       num_time_buckets, num_heads=1, seq_offsets_host=None, stream=None):
+    """(pos_bucket, time_bucket) int32 [n, n] for sequence `seq`, from the kernels' bucket code."""
+    host = _host_offsets(seq_offsets, seq_offsets_host)
+    n = int(host[seq + 1] - host[seq])
+    desc = attn_desc(len(host) - 1, num_heads, 32, 32, max_seq_len, num_pos_buckets,
+                     num_time_buckets, HSTU_F32)
+    pb = torch.empty((n, n), dtype=torch.int32, device=seq_offsets.device)
+    tb = torch.empty((n, n), dtype=torch.int32, device=seq_offsets.device)
+    _check(lib.hstu_debug_buckets(ctypes.byref(desc), _i64p(host), _ptr(seq_offsets),
+                                  _ptr(timestamps), int(seq), _ptr(pb), _ptr(tb), _stream(stream)))
+    return pb, tb

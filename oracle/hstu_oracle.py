@@ -49,14 +49,31 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
-    "silu", "floor_log2", "pos_bucket", "time_bucket", "bias_matrix", "attention_one_head",
-    "hstu_attention", "layer_norm_rows", "hstu_layer", "hstu_layer_stack", "mfalcon_score",
+    "silu", "round_storage", "floor_log2", "pos_bucket", "time_bucket", "bias_matrix", "attention_one_head",
+    "hstu_attention", "hstu_attention_rows", "layer_norm_rows", "hstu_layer", "hstu_layer_stack", "mfalcon_score",
     "mfalcon_by_definition", "candidate_attention", "attention_pairs", "attention_flops",
 ]
 
 
 def _f64(a):
     return None if a is None else np.asarray(a, dtype=np.float64)
+
+
+def round_storage(x, storage):
+    """Round to the storage format of a stored intermediate. storage=None keeps fp64.
+    storage="bf16" rounds to the nearest bfloat16 value (ties to even): first to fp32
+    (nearest), then keep the top 16 bits of the fp32 pattern, rounding half to even."""
+    x = _f64(x)
+    if storage is None:
+        return x
+    if storage != "bf16":
+        raise ValueError(storage)
+    f = np.ascontiguousarray(x, dtype=np.float32)
+    bits = f.view(np.uint32).astype(np.uint64)
+    keep = (bits + 0x7FFF + ((bits >> 16) & 1)) >> 16
+    out = (keep.astype(np.uint32) << 16).view(np.float32)
+    out = np.where(np.isnan(f), np.float32(np.nan), out)
+    return out.astype(np.float64)
 
 
 # ---------------------------------------------------------------------------
@@ -151,6 +168,29 @@ def hstu_attention(offsets, ts, q, k, v, rab_pos, rab_time, N, u=None, gamma=Non
     return (z * _f64(u).reshape(Ttot, H * dv)).reshape(Ttot, H, dv)
 
 
+def hstu_attention_rows(offsets, ts, q, k, v, rab_pos, rab_time, N, rows):
+    """Selected rows of hstu_attention (without the gate), each computed on its own from
+    its sequence prefix: row r at position i of sequence b attends keys 0..i of b.
+    rows are global token indices. Returns fp64 [len(rows), H, d_v]."""
+    offsets = np.asarray(offsets, dtype=np.int64)
+    H, dv = v.shape[1], v.shape[2]
+    out = np.zeros((len(rows), H, dv), dtype=np.float64)
+    for idx, r in enumerate(rows):
+        r = int(r)
+        b = int(np.searchsorted(offsets, r, side="right")) - 1
+        s = int(offsets[b])
+        i = r - s
+        kpos = np.arange(i + 1, dtype=np.int64)
+        qts = None if ts is None else np.asarray(ts, np.int64)[r:r + 1]
+        kts = None if ts is None else np.asarray(ts, np.int64)[s:r + 1]
+        vis = np.ones((1, i + 1), dtype=bool)
+        for h in range(H):
+            bias = bias_matrix(h, np.array([i]), kpos, qts, kts, rab_pos, rab_time)
+            out[idx, h] = attention_one_head(_f64(q[r:r + 1, h]), _f64(k[s:r + 1, h]),
+                                             _f64(v[s:r + 1, h]), vis, bias, N)[0]
+    return out
+
+
 def layer_norm_rows(z, gamma=None, beta=None, eps=1e-5):
     """LayerNorm of each row: (z - mean) / sqrt(var + eps) * gamma + beta, biased variance."""
     z = _f64(z)
@@ -174,9 +214,9 @@ def _affine(x, w, b):
     return y
 
 
-def _split_uvqk(x, w, H, d_qk, d_v):
+def _split_uvqk(x, w, H, d_qk, d_v, storage=None):
     """eq. 1: SiLU(f1(X)), split into the row blocks [U | V | Q | K]."""
-    z = silu(_affine(x, w.w1, w.b1))
+    z = round_storage(silu(_affine(x, w.w1, w.b1)), storage)
     n = z.shape[0]
     cu = H * d_v
     cq = H * d_qk
@@ -187,23 +227,31 @@ def _split_uvqk(x, w, H, d_qk, d_v):
     return U, V, Q, K
 
 
-def hstu_layer(offsets, ts, x, w, H, d_qk, d_v, N, eps=1e-5, residual=0):
+def hstu_layer(offsets, ts, x, w, H, d_qk, d_v, N, eps=1e-5, residual=0, storage=None):
     """One HSTU layer over a jagged batch: eq. 1, causal eq. 2, then eq. 3 with
-    f2(G) = G W2^T + b2 (+ X when residual is set)."""
-    U, V, Q, K = _split_uvqk(x, w, H, d_qk, d_v)
+    f2(G) = G W2^T + b2 (+ X when residual is set).
+
+    storage=None computes in fp64 throughout. storage="bf16" rounds the tensors that a
+    bf16 implementation stores between its steps (U, V, Q, K after eq. 1, the gated
+    G, and Y) to bf16. The HSTU chapter sizes a layer's activation state in bfloat16
+    ("Gating instead of a separate FFN"). This variant measures how much storage
+    rounding alone moves each output row."""
+    U, V, Q, K = _split_uvqk(x, w, H, d_qk, d_v, storage)
     g = hstu_attention(offsets, ts, Q, K, V, w.rab_pos, w.rab_time, N, u=U, gamma=w.gamma,
                        beta=w.beta, eps=eps)
-    y = _affine(g.reshape(g.shape[0], H * d_v), w.w2, w.b2)
+    g = round_storage(g.reshape(g.shape[0], H * d_v), storage)
+    y = _affine(g, w.w2, w.b2)
     if residual:
         y = y + _f64(x)
-    return y
+    return round_storage(y, storage)
 
 
-def hstu_layer_stack(offsets, ts, x, layers, H, d_qk, d_v, N, eps=1e-5, residual=0):
+def hstu_layer_stack(offsets, ts, x, layers, H, d_qk, d_v, N, eps=1e-5, residual=0,
+                     storage=None):
     """X_{l+1} = layer_l(X_l) for each layer in order."""
     y = _f64(x)
     for w in layers:
-        y = hstu_layer(offsets, ts, y, w, H, d_qk, d_v, N, eps, residual)
+        y = hstu_layer(offsets, ts, y, w, H, d_qk, d_v, N, eps, residual, storage)
     return y
 
 
@@ -238,7 +286,7 @@ def candidate_attention(Qc, Kc, Vc, Kh, Vh, cand_ts, hist_ts, rab_pos, rab_time,
 
 
 def mfalcon_score(hist_offsets, hist_ts, hist_x, cand_offsets, cand_ts, cand_x, layers, H, d_qk,
-                  d_v, N, microbatch, w_head=None, eps=1e-5, residual=0):
+                  d_v, N, microbatch, w_head=None, eps=1e-5, residual=0, storage=None):
     """M-FALCON as the pages describe it: for each user, compute the history once
     per layer and keep that layer's history K and V. Then score the candidates in
     microbatches. Each candidate attends to all n_h cached history keys at
@@ -259,9 +307,9 @@ def mfalcon_score(hist_offsets, hist_ts, hist_x, cand_offsets, cand_ts, cand_x, 
         xh = _f64(hist_x[hs:he])
         cache = []
         for w in layers:
-            U, V, Q, K = _split_uvqk(xh, w, H, d_qk, d_v)
+            U, V, Q, K = _split_uvqk(xh, w, H, d_qk, d_v, storage)
             cache.append((K, V))
-            xh = hstu_layer(h_off, hts, xh, w, H, d_qk, d_v, N, eps, residual)
+            xh = hstu_layer(h_off, hts, xh, w, H, d_qk, d_v, N, eps, residual, storage)
         # candidate microbatches against the cache
         cs, ce = int(cand_offsets[b]), int(cand_offsets[b + 1])
         for m0 in range(cs, ce, max(1, int(microbatch))):
@@ -270,14 +318,14 @@ def mfalcon_score(hist_offsets, hist_ts, hist_x, cand_offsets, cand_ts, cand_x, 
             cts = None if cand_ts is None else np.asarray(cand_ts, np.int64)[m0:m1]
             nc = m1 - m0
             for w, (Kh, Vh) in zip(layers, cache):
-                U, V, Q, K = _split_uvqk(xc, w, H, d_qk, d_v)
+                U, V, Q, K = _split_uvqk(xc, w, H, d_qk, d_v, storage)
                 o = candidate_attention(Q, K, V, Kh, Vh, cts, hts, w.rab_pos, w.rab_time, N)
                 z = layer_norm_rows(o.reshape(nc, H * d_v), w.gamma, w.beta, eps)
-                g = z * U.reshape(nc, H * d_v)
+                g = round_storage(z * U.reshape(nc, H * d_v), storage)
                 y = _affine(g, w.w2, w.b2)
                 if residual:
                     y = y + xc
-                xc = y
+                xc = round_storage(y, storage)
             out[m0:m1] = xc
     logits = None if w_head is None else out @ _f64(w_head)
     return out, logits

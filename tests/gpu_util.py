@@ -1,0 +1,101 @@
+"""Helpers for the GPU parity tests: move the seeded inputs to the device, call the
+C ABI through the ctypes binding, and compare with the oracle per output row."""
+import sys
+
+import numpy as np
+import torch
+
+
+def announce(msg: str):
+    """Name the case before a GPU step (flushed), so a failing run says which case it was."""
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def dev(a, dtype=None):
+    if a is None:
+        return None
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.to("cuda")
+
+
+def act_dtype(name: str):
+    return torch.bfloat16 if name == "bf16" else torch.float32
+
+
+def to_np(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def row_errors(g, o):
+    """Per output row: max|g - o| / max|o|. The rows are the first axis; the rest is flattened."""
+    g = np.asarray(g, np.float64).reshape(len(g), -1)
+    o = np.asarray(o, np.float64).reshape(len(o), -1)
+    num = np.abs(g - o).max(axis=1) if g.size else np.zeros(0)
+    den = np.abs(o).max(axis=1) if o.size else np.zeros(0)
+    return num, den
+
+
+def assert_rows_close(g, o, tol, what=""):
+    """Relative error per row (infinity norm) <= tol. Where the oracle row is exactly zero,
+    the GPU row must be exactly zero too."""
+    assert np.all(np.isfinite(g)), f"{what}: non-finite output"
+    num, den = row_errors(g, o)
+    zero = den == 0
+    assert np.all(num[zero] == 0), f"{what}: rows that must be zero are not"
+    rel = num[~zero] / den[~zero]
+    worst = float(rel.max()) if rel.size else 0.0
+    assert worst <= tol, f"{what}: worst row error {worst:.3e} > {tol:.1e} (p99 " \
+                         f"{float(np.quantile(rel, 0.99)) if rel.size else 0:.3e})"
+    return worst
+
+
+def attn_on_gpu(x, with_u=False, out_dtype=None, rab_pos="x", rab_time="x", ts="x", q=None):
+    dt = act_dtype(x.dtype)
+    from hstu_jagged_pointwise_amd import ops
+    rp = x.rab_pos if isinstance(rab_pos, str) else rab_pos
+    rt = x.rab_time if isinstance(rab_time, str) else rab_time
+    tsv = x.ts if isinstance(ts, str) else ts
+    qv = x.q if q is None else q
+    out = ops.hstu_attn_fwd(dev(x.offsets), dev(tsv), dev(qv, dt), dev(x.k, dt), dev(x.v, dt),
+                            dev(rp), dev(rt), max_seq_len=x.max_seq_len,
+                            num_pos_buckets=x.num_pos_buckets, num_time_buckets=x.num_time_buckets,
+                            u=dev(x.u, dt) if with_u else None,
+                            ln_gamma=dev(x.gamma) if with_u else None,
+                            ln_beta=dev(x.beta) if with_u else None, ln_eps=x.eps,
+                            seq_offsets_host=x.offsets)
+    torch.cuda.synchronize()
+    return out
+
+
+def layer_weights_on_gpu(layers, dtype_name):
+    from hstu_jagged_pointwise_amd import ops
+    dt = act_dtype(dtype_name)
+    return [ops.LayerWeights(w1=dev(w.w1, dt), w2=dev(w.w2, dt), b1=dev(w.b1), b2=dev(w.b2),
+                             rab_pos=dev(w.rab_pos), rab_time=dev(w.rab_time),
+                             ln_gamma=dev(w.gamma), ln_beta=dev(w.beta)) for w in layers]
+
+
+def assert_rows_close_storage(g, o, o_storage, tol, k=4.0, what=""):
+    """bf16 multi-step paths: per row, |g - o|_inf <= max(tol |o|_inf, k |o_s - o|_inf).
+    Here o is the fp64 oracle and o_s is the oracle with bf16 storage of the tensors
+    that the library stores between steps. In well-conditioned rows the first term
+    applies. Where storage rounding alone moves a row by more than tol, the bound
+    follows the size of that move. The median row must also meet tol."""
+    assert np.all(np.isfinite(g)), f"{what}: non-finite output"
+    g = np.asarray(g, np.float64).reshape(len(g), -1)
+    o = np.asarray(o, np.float64).reshape(len(o), -1)
+    s = np.asarray(o_storage, np.float64).reshape(len(o), -1)
+    num = np.abs(g - o).max(axis=1)
+    den = np.abs(o).max(axis=1)
+    sens = np.abs(s - o).max(axis=1)
+    bound = np.maximum(tol * den, k * sens)
+    bad = num > bound
+    assert not bad.any(), f"{what}: {int(bad.sum())} rows outside the bound; worst excess " \
+                          f"{float((num / np.maximum(bound, 1e-300)).max()):.3f}"
+    live = den > 0
+    med = float(np.median(num[live] / den[live])) if live.any() else 0.0
+    assert med <= tol, f"{what}: median row error {med:.3e} > {tol}"
+    return float((num[live] / den[live]).max()) if live.any() else 0.0

@@ -52,6 +52,30 @@ def test_floor_log2_matches_python_bit_length():
     assert np.array_equal(got, want)
 
 
+def test_round_storage_matches_torch_bfloat16():
+    rng = np.random.default_rng(17)
+    x = np.concatenate([rng.standard_normal(20000) * 10.0 ** rng.integers(-30, 30, size=20000),
+                        [0.0, -0.0, 1.0, 1.00390625, 1.01171875, 65504.0, 3.0e38, np.inf, -np.inf,
+                         1e-40, -1e-42]]).astype(np.float32)
+    # exact ties: fp32 patterns whose low 16 bits are 0x8000
+    ties = (np.arange(1000, dtype=np.uint32) << 16 | 0x8000).astype(np.uint32).view(np.float32)
+    x = np.concatenate([x, ties[np.isfinite(ties)]])
+    want = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    got = O.round_storage(x.astype(np.float64), "bf16")
+    np.testing.assert_array_equal(got, want)
+    assert O.round_storage(np.array([1.5]), None)[0] == 1.5
+
+
+def test_bf16_storage_variant_changes_only_by_rounding():
+    x = synth.make_layer(14, lambda r: synth.lengths_uniform(r, 3, 1, 30), 2, 32, 32, 64, 16, 16,
+                         "f32", num_layers=2, w_std=0.2)
+    a = O.hstu_layer_stack(x.offsets, x.ts, x.x, x.layers, 2, 32, 32, x.max_seq_len)
+    b = O.hstu_layer_stack(x.offsets, x.ts, x.x, x.layers, 2, 32, 32, x.max_seq_len, storage="bf16")
+    assert np.array_equal(O.round_storage(b, "bf16"), b)  # outputs are bf16 values
+    rel = np.abs(a - b).max(1) / np.abs(a).max(1)
+    assert 0 < rel.max() < 0.05
+
+
 # ---------------------------------------------------------------- SiLU / LayerNorm
 def test_silu_against_torch_and_identities():
     x = np.linspace(-60, 60, 4001)
@@ -165,6 +189,14 @@ def test_attention_matches_padded_torch_route():
         s0, e0 = x.offsets[b], x.offsets[b + 1]
         want[s0:e0] = o[b, :, : e0 - s0].transpose(0, 1).numpy()
     np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-13)
+
+
+def test_sampled_rows_equal_full_attention():
+    x = synth.make_attn(13, lambda r: synth.lengths_uniform(r, 4, 0, 50), 2, 8, 6, 16, 16, "f32")
+    full = O.hstu_attention(x.offsets, x.ts, x.q, x.k, x.v, x.rab_pos, x.rab_time, 60)
+    rows = np.arange(int(x.offsets[-1]))[::3]
+    got = O.hstu_attention_rows(x.offsets, x.ts, x.q, x.k, x.v, x.rab_pos, x.rab_time, 60, rows)
+    np.testing.assert_allclose(got, full[rows], rtol=1e-12, atol=1e-14)
 
 
 # ---------------------------------------------------------------- closed forms

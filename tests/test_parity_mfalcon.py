@@ -1,0 +1,131 @@
+"""GPU parity of mfalcon_score against the fp64 oracle, and its invariants.
+
+A candidate's output must not depend on the other candidates. So permuting
+candidates permutes outputs, adding one leaves the others unchanged, and the
+microbatch size does not matter. On the GPU these hold bit for bit, because
+every output row has a fixed reduction order."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import hstu_oracle as O
+from hstu_jagged_pointwise_amd import synth
+from gpu_util import (announce, assert_rows_close, assert_rows_close_storage, dev, act_dtype,
+                      layer_weights_on_gpu, to_np)
+
+pytestmark = pytest.mark.gpu
+TOL = {"f32": 1e-5, "bf16": 2e-2}
+
+
+def mf_on_gpu(x, microbatch=None, cand_x=None, cand_ts=None, cand_offsets=None):
+    from hstu_jagged_pointwise_amd import ops
+    dt = act_dtype(x.dtype)
+    cx = x.cand_x if cand_x is None else cand_x
+    cts = x.cand_ts if cand_ts is None else cand_ts
+    coff = x.cand_offsets if cand_offsets is None else cand_offsets
+    out, logit = ops.mfalcon_score(dev(x.hist_offsets), dev(x.hist_ts), dev(x.hist_x, dt),
+                                   dev(coff), dev(cts), dev(cx, dt),
+                                   layer_weights_on_gpu(x.layers, x.dtype), num_heads=x.num_heads,
+                                   d_qk=x.d_qk, d_v=x.d_v, max_seq_len=x.max_seq_len,
+                                   microbatch=microbatch or x.microbatch, w_head=dev(x.w_head),
+                                   ln_eps=x.eps, residual=x.residual,
+                                   hist_offsets_host=x.hist_offsets, cand_offsets_host=coff)
+    torch.cuda.synchronize()
+    return out, logit
+
+
+def mf_oracle(x, storage=None):
+    return O.mfalcon_score(x.hist_offsets, x.hist_ts, x.hist_x, x.cand_offsets, x.cand_ts,
+                           x.cand_x, x.layers, x.num_heads, x.d_qk, x.d_v, x.max_seq_len,
+                           x.microbatch, x.w_head, x.eps, x.residual, storage)
+
+
+def check_rows(g, x, want, want_s, what):
+    if x.dtype == "f32":
+        return assert_rows_close(g, want, TOL["f32"], what)
+    return assert_rows_close_storage(g, want, want_s, TOL["bf16"], what=what)
+
+
+def _check_logits(lg, want_out, x, tol):
+    """Logit tolerance relative to |y_c| |w_head| (the logit can cancel to ~0)."""
+    lg = lg.cpu().numpy().astype(np.float64)
+    want = want_out @ x.w_head.astype(np.float64)
+    scale = np.linalg.norm(want_out, axis=1) * np.linalg.norm(x.w_head)
+    assert np.all(np.abs(lg - want) <= tol * scale + 1e-30)
+
+
+def _small(dt, L, seed=1, shared=False, mb=5, hist=(37, 0, 140, 9), cands=(6, 4, 13, 0)):
+    return synth.make_mfalcon(seed, list(hist), list(cands), 2, 64, 64, 64, 32, 16, dt,
+                              num_layers=L, microbatch=mb, shared_request_time=shared, w_std=0.1,
+                              random_bias=True, with_ln_affine=True)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("L", [1, 2, 3])
+@pytest.mark.parametrize("shared", [True, False])
+def test_small_multi_user(dt, L, shared):
+    x = _small(dt, L, shared=shared)
+    announce(f"mfalcon small {dt} L={L} shared_ts={shared}")
+    out, lg = mf_on_gpu(x)
+    want, _ = mf_oracle(x)
+    want_s = mf_oracle(x, "bf16")[0] if dt == "bf16" else None
+    check_rows(to_np(out), x, want, want_s, f"mfalcon {dt} L={L}")
+    _check_logits(lg, want if dt == "f32" else want_s, x, TOL[dt])
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_candidates_are_independent_bit_exact(dt):
+    x = _small(dt, 2, seed=5, hist=(200,), cands=(150,), mb=64)
+    announce(f"mfalcon invariants {dt}")
+    base, _ = mf_on_gpu(x)
+    base = base.float().cpu().numpy()
+    # microbatch size does not change any result
+    for mb in (1, 7, 150, 1000):
+        o, _ = mf_on_gpu(x, microbatch=mb)
+        assert np.array_equal(o.float().cpu().numpy(), base), f"microbatch {mb}"
+    # permuting candidates permutes outputs
+    perm = np.random.default_rng(0).permutation(150)
+    o, _ = mf_on_gpu(x, cand_x=x.cand_x[perm], cand_ts=x.cand_ts[perm])
+    assert np.array_equal(o.float().cpu().numpy(), base[perm])
+    # adding candidates leaves the others unchanged
+    extra = np.concatenate([x.cand_x, x.cand_x[:9] * -2.0])
+    extra_ts = np.concatenate([x.cand_ts, x.cand_ts[:9] + 11])
+    o, _ = mf_on_gpu(x, cand_x=extra, cand_ts=extra_ts, cand_offsets=np.array([0, 159]))
+    assert np.array_equal(o.float().cpu().numpy()[:150], base)
+
+
+def test_candidate_equals_last_row_of_causal_layer_on_gpu():
+    """Candidate c of the GPU M-FALCON path equals the last row of the GPU causal layer
+    stack run on (history, c), to the bf16 tolerance (the two use different kernels)."""
+    from test_parity_layer import layer_on_gpu
+    x = _small("bf16", 2, seed=7, hist=(100,), cands=(5,), mb=5)
+    out, _ = mf_on_gpu(x)
+    out = to_np(out)
+    for c in range(5):
+        lx = synth.LayerInputs(np.array([0, 101]), np.concatenate([x.hist_ts, x.cand_ts[c:c + 1]]),
+                               np.concatenate([x.hist_x, x.cand_x[c:c + 1]]), x.layers, 2, 64, 64,
+                               64, 32, 16, x.max_seq_len, "bf16")
+        y = layer_on_gpu(lx)
+        assert_rows_close(out[c:c + 1], y[-1:], TOL["bf16"], f"candidate {c} vs causal")
+
+
+def test_mfalcon_workload_sampled_candidates():
+    """History 4096, 16,384 candidates in microbatches of 1024, H=8, d=64, d_model 512, bf16:
+    the launch configuration the benchmark times. 96 sampled candidates are checked against
+    the oracle (candidates are independent, so the oracle scores just those)."""
+    x = synth.workload_mfalcon()
+    announce("mfalcon workload 4096 history x 16384 candidates")
+    out, lg = mf_on_gpu(x)
+    g = to_np(out)
+    assert np.all(np.isfinite(g))
+    rows = np.unique(np.concatenate([np.arange(0, 16384, 1024), np.arange(1023, 16384, 1024),
+                                     np.random.default_rng(4).integers(0, 16384, size=64)]))
+    args = (x.hist_offsets, x.hist_ts, x.hist_x, np.array([0, len(rows)]), x.cand_ts[rows],
+            x.cand_x[rows], x.layers, x.num_heads, x.d_qk, x.d_v, x.max_seq_len, x.microbatch,
+            x.w_head)
+    want, _ = O.mfalcon_score(*args)
+    want_s, _ = O.mfalcon_score(*args, storage="bf16")
+    assert_rows_close_storage(g[rows], want, want_s, TOL["bf16"], what="mfalcon sampled")
+    lgn = lg.cpu().numpy()[rows].astype(np.float64)
+    scale = np.linalg.norm(want, axis=1) * np.linalg.norm(x.w_head)
+    assert np.all(np.abs(lgn - want @ x.w_head.astype(np.float64)) <= 2e-2 * scale)
