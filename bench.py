@@ -1,0 +1,299 @@
+"""Benchmark of the HSTU jagged pointwise-attention hot path on one MI355X.
+
+A step is one hstu_attn_fwd call on the long-sequence workload: B=8 jagged
+sequences, lengths uniform in [4096, 8192] with one of exactly 8192, 4 heads,
+d_qk = d_v = 128, bf16 in with fp32 accumulation, 128 position and 64 time
+buckets, causal. That call plans the tiles on the device and runs the fused
+attention kernel. `value` is attention TFLOP/s, counting useful pairs only:
+H * sum_b n_b (n_b + 1) / 2 * 2 (d_qk + d_v) FLOPs per call. All inputs are
+resident in HBM before the timed region. The same run also times:
+  * M-FALCON: history 4096, 16,384 candidates in microbatches of 1024, H=8,
+    d=64, d_model=512, 1 layer (candidates/s over the whole call, history pass
+    included);
+  * the short-history layer (B=256, lengths 20..200, d_model 128) and the
+    heavy-tailed 4-layer stack (B=32, power-law lengths 64..4096, d_model 512);
+  * the fp64 CPU oracle on a bounded sample of the attention workload.
+One JSON line goes to stdout. Progress goes to stderr.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only attn,mfalcon,layers,copy]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "HSTU attn TFLOP/s + % bf16 MFMA peak at len 8192; M-FALCON candidates/sec"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA (published)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E (published)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_long_traffic.json")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    """Hash of the attention kernel sources; counter data is valid only for this hash."""
+    h = hashlib.sha256()
+    for f in ("attn_mfma.hip", "attn_common.h", "common.h", "plan.hip"):
+        with open(os.path.join(ROOT, "hstu_jagged_pointwise_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def time_calls(fn, stream, steps, warmup):
+    """Per-call durations (ms) from HIP events recorded on the library's stream."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        fn()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return np.array([s.elapsed_time(e) for s, e in zip(starts, ends)]), wall
+
+
+def leg_attention(steps, warmup):
+    import torch
+    from hstu_jagged_pointwise_amd import ops, synth
+    from hstu_jagged_pointwise_amd.device import attn_to_device
+    x = synth.workload_long_attention()
+    d = attn_to_device(x)
+    stream = torch.cuda.Stream()
+    desc = ops.attn_desc(len(x.offsets) - 1, x.num_heads, x.d_qk, x.d_v, x.max_seq_len,
+                         x.num_pos_buckets, x.num_time_buckets, ops.HSTU_BF16)
+    ws_bytes = ops.hstu_attn_workspace_size(desc, x.offsets)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(d["v"])
+
+    def call():
+        ops.hstu_attn_fwd(d["offsets"], d["ts"], d["q"], d["k"], d["v"], d["rab_pos"],
+                          d["rab_time"], max_seq_len=x.max_seq_len, out=out, workspace=ws,
+                          seq_offsets_host=x.offsets, stream=stream)
+
+    with torch.cuda.stream(stream):
+        ms, wall = time_calls(call, stream, steps, warmup)
+    pairs = int(np.sum(x.lengths * (x.lengths + 1) // 2))
+    flops = pairs * x.num_heads * 2 * (x.d_qk + x.d_v)
+    mean = float(ms.mean())
+    return dict(x=x, ms=ms, wall=wall, flops=flops, pairs=pairs, tflops=flops / (mean * 1e-3) / 1e12,
+                out=out)
+
+
+def leg_mfalcon(steps, warmup):
+    import torch
+    from hstu_jagged_pointwise_amd import ops, synth
+    from hstu_jagged_pointwise_amd.device import mfalcon_to_device
+    x = synth.workload_mfalcon()
+    d = mfalcon_to_device(x)
+    stream = torch.cuda.Stream()
+    ld = ops.layer_desc(d["layers"], 1, x.num_heads, x.d_qk, x.d_v, x.d_model, x.max_seq_len,
+                        ops.HSTU_BF16)
+    desc = ops.mfalcon_desc(ld, x.microbatch)
+    ws = torch.empty(ops.mfalcon_workspace_size(desc, x.hist_offsets, x.cand_offsets),
+                     dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(d["cand_x"])
+    logit = torch.empty(out.shape[0], dtype=torch.float32, device="cuda")
+
+    def call():
+        ops.mfalcon_score(d["hist_offsets"], d["hist_ts"], d["hist_x"], d["cand_offsets"],
+                          d["cand_ts"], d["cand_x"], d["layers"], num_heads=x.num_heads,
+                          d_qk=x.d_qk, d_v=x.d_v, max_seq_len=x.max_seq_len,
+                          microbatch=x.microbatch, w_head=d["w_head"], out=out, logit=logit,
+                          workspace=ws, hist_offsets_host=x.hist_offsets,
+                          cand_offsets_host=x.cand_offsets, stream=stream)
+
+    with torch.cuda.stream(stream):
+        ms, wall = time_calls(call, stream, max(3, steps // 2), max(1, warmup // 2))
+    C = int(x.cand_offsets[-1])
+    mean = float(ms.mean())
+    n_h = int(x.hist_offsets[-1])
+    hd = x.num_heads
+    attn_flops = C * (n_h + 1) * hd * 2 * (x.d_qk + x.d_v)
+    proj_flops = C * 2 * x.d_model * (2 * hd * (x.d_qk + x.d_v) + hd * x.d_v)
+    hist_flops = n_h * 2 * x.d_model * 2 * hd * (x.d_qk + x.d_v)
+    return dict(candidates=C, ms=mean, candidates_per_s=C / (mean * 1e-3),
+                tflops=(attn_flops + proj_flops + hist_flops) / (mean * 1e-3) / 1e12,
+                microbatch=x.microbatch, history=n_h, layers=1)
+
+
+def leg_layers(steps, warmup):
+    import torch
+    from hstu_jagged_pointwise_amd import ops, synth
+    from hstu_jagged_pointwise_amd.device import layer_to_device
+    res = {}
+    for name, x in (("short_history_layer", synth.workload_short_history_layer()),
+                    ("heavy_tail_4_layer_stack", synth.workload_heavy_tail_stack())):
+        d = layer_to_device(x)
+        stream = torch.cuda.Stream()
+        desc = ops.layer_desc(d["layers"], len(x.offsets) - 1, x.num_heads, x.d_qk, x.d_v,
+                              x.d_model, x.max_seq_len, ops.HSTU_BF16)
+        ws = torch.empty(ops.hstu_layer_workspace_size(desc, x.offsets), dtype=torch.uint8,
+                         device="cuda")
+        y = torch.empty_like(d["x"])
+
+        def call():
+            ops.hstu_layer_fwd(d["offsets"], d["ts"], d["x"], d["layers"], num_heads=x.num_heads,
+                               d_qk=x.d_qk, d_v=x.d_v, max_seq_len=x.max_seq_len, out=y,
+                               workspace=ws, seq_offsets_host=x.offsets, stream=stream)
+
+        with torch.cuda.stream(stream):
+            ms, _ = time_calls(call, stream, steps, warmup)
+        L = len(x.layers)
+        T = int(x.offsets[-1])
+        pairs = int(np.sum(x.lengths * (x.lengths + 1) // 2))
+        f1 = T * 2 * x.d_model * 2 * x.num_heads * (x.d_qk + x.d_v)
+        f2 = T * 2 * x.num_heads * x.d_v * x.d_model
+        at = pairs * x.num_heads * 2 * (x.d_qk + x.d_v)
+        mean = float(ms.mean())
+        res[name] = dict(tokens=T, layers=L, ms_per_call=mean, us_per_layer=mean * 1e3 / L,
+                         tflops=L * (f1 + f2 + at) / (mean * 1e-3) / 1e12)
+    return res
+
+
+def leg_copy():
+    """A plain 1 GiB device copy: the calibration for the HBM byte counters."""
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    return dict(bytes_read=n, bytes_written=n, launches=3)
+
+
+def cpu_baseline(x, budget_s=25.0):
+    """The fp64 oracle on a bounded sample: whole heads of the longest sequence, as many
+    as fit in about budget_s of host time (at least one)."""
+    from oracle import hstu_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = len(os.sched_getaffinity(0))
+    s, e = int(x.offsets[0]), int(x.offsets[1])
+    n = e - s
+    done, flops, t_total = 0, 0, 0.0
+    for h in range(x.num_heads):
+        sub_q = x.q[s:e, h:h + 1]
+        t0 = time.perf_counter()
+        O.hstu_attention(np.array([0, n]), x.ts[s:e], sub_q, x.k[s:e, h:h + 1], x.v[s:e, h:h + 1],
+                         x.rab_pos[h:h + 1], x.rab_time[h:h + 1], x.max_seq_len)
+        t_total += time.perf_counter() - t0
+        done += 1
+        flops += n * (n + 1) // 2 * 2 * (x.d_qk + x.d_v)
+        if t_total > budget_s * (done - 0.5) / done or t_total > budget_s:
+            break
+    try:
+        cpu = [l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo") if l.startswith("model name")][0]
+    except Exception:  # noqa: BLE001
+        cpu = "unknown"
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"sequence 0 (length {n}), {done} of {x.num_heads} heads, fp64 numpy; "
+                      f"{t_total:.1f} s; host CPU {cpu}; {len(os.sched_getaffinity(0))} cores visible"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--only", default="attn,mfalcon,layers,cpu")
+    ap.add_argument("--cpu-budget", type=float, default=25.0)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+    legs = set(args.only.split(","))
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    from hstu_jagged_pointwise_amd import ops  # noqa: F401  (fails loudly without libhstu.so)
+
+    if legs == {"copy"}:
+        log("copy calibration leg")
+        print(json.dumps({"copy": leg_copy()}))
+        return
+    result = {}
+    attn = None
+    if "attn" in legs:
+        log("attention leg (length-8192 workload)")
+        attn = leg_attention(args.steps, args.warmup)
+        log(f"attention: {attn['ms'].mean():.3f} ms/call, {attn['tflops']:.1f} TFLOP/s")
+    if "mfalcon" in legs:
+        log("M-FALCON leg")
+        result["mfalcon"] = leg_mfalcon(args.steps, args.warmup)
+        log(f"M-FALCON: {result['mfalcon']['candidates_per_s']:.3e} candidates/s")
+    if "layers" in legs:
+        log("layer legs")
+        result["layers"] = leg_layers(args.steps, args.warmup)
+    if attn is None:
+        print(json.dumps(result))
+        return
+    x = attn["x"]
+    mean = float(attn["ms"].mean())
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        rec = json.load(open(TRAFFIC_FILE))
+        if rec.get("source_hash") == source_hash():
+            traffic = rec.get("bytes_per_launch")
+    line = {
+        "metric": METRIC,
+        "value": round(attn["tflops"], 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(mean, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "long-sequence jagged HSTU attention: B=8, lengths uniform in [4096,8192] "
+                        "with one of 8192, H=4, d_qk=d_v=128, bf16 in / fp32 accumulate, "
+                        "128 position + 64 time buckets, causal, 1/N with N=8192",
+            "batch": int(len(x.offsets) - 1), "tokens": int(x.offsets[-1]),
+            "lengths": [int(v) for v in x.lengths], "heads": x.num_heads, "d_qk": x.d_qk,
+            "d_v": x.d_v, "useful_pairs_per_head": attn["pairs"], "flops_per_call": attn["flops"],
+        },
+        "timing": {"ms_p10": round(float(np.quantile(attn["ms"], 0.1)), 4),
+                   "ms_p50": round(float(np.median(attn["ms"])), 4),
+                   "ms_p90": round(float(np.quantile(attn["ms"], 0.9)), 4),
+                   "wall_s": round(attn["wall"], 4),
+                   "note": "per-call HIP events on the library's stream; a call is the tile "
+                           "planner plus the attention kernel"},
+        "roofline": {"bound": "mfma", "achieved": round(attn["tflops"], 3),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(attn["tflops"] / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
+    }
+    line.update(result)
+    if "cpu" in legs:
+        log("CPU oracle baseline (bounded sample)")
+        line["cpu_baseline"] = cpu_baseline(x, args.cpu_budget)
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -8,27 +8,42 @@
 // contraction.
 //
 // Work decomposition. A workgroup (4 wavefronts) owns 128 query rows of one
-// head. Each wavefront owns 32 rows. Keys stream through LDS in tiles of 64.
-// Per 32-key block a wavefront runs:
+// head. Each wavefront owns 32 rows. Keys stream through a double-buffered LDS
+// tile of 64: the next tile's global loads are in flight while the current
+// tile is computed, with one barrier per tile. Per 32-key block a wavefront runs:
 //   S^T = K Q^T  with v_mfma_f32_32x32x16_bf16. Q stays in registers as the B
-//                operand. The accumulator then holds one query row per lane
+//                operand. The accumulator holds one query row per lane
 //                (lane % 32) and 16 keys per lane.
-//   P = SiLU(S + bias), masked, on the vector ALU. The bias comes from
-//                LDS-resident tables. The time bucket is a count of leading
-//                zeros on the 32-bit elapsed time, with a 64-bit path for
-//                tiles whose span is too wide.
+//   P = SiLU(S + bias), on the vector ALU.
 //   O += P V     again with the 32x32x16 MFMA. P goes in as the A operand
-//                straight from registers, with no LDS round trip: the key order
-//                held in the accumulator defines the contraction order, and V
-//                is read in that same order with ds_read_b64_tr_b16, which
-//                transposes row-major V on the way out of LDS.
-// Under the causal mask a wavefront skips key blocks that lie entirely above
-// its rows, and applies the mask select only on blocks that cross the
-// diagonal. The mask is a select after SiLU (SiLU(-inf) would be NaN).
+//                straight from registers; the key order of the accumulator
+//                defines the contraction order, and V is read in that order
+//                with ds_read_b64_tr_b16, which transposes row-major V on the
+//                way out of LDS.
+// Both 32-key blocks of a tile issue their S MFMAs first, so the matrix core
+// works on block 1 while the vector ALU activates block 0.
+//
+// Bias classes, decided per (wavefront, 32-key block) from exact integer
+// ranges:
+//   * The position bucket min(i-j, P-1) is one constant when every i-j >= P-1.
+//   * The time bucket is one constant when its value agrees at both ends of the
+//     block's elapsed-time range [min t_i - max t_j, max t_i - min t_j]. The
+//     bucket is monotone in the elapsed time, so agreement at both ends means
+//     it holds everywhere.
+//   * A constant bias becomes the accumulator's initial value, at no cost per
+//     element. Otherwise each element gathers from LDS-resident tables. The
+//     time bucket is then the count of leading zeros of the 32-bit elapsed time
+//     + 1 (a 64-bit path covers spans past 2^31 s).
+// Masking is a select after SiLU (SiLU(-inf) would be NaN). It runs only on
+// blocks that cross the causal diagonal (or the history tail for candidates).
+// Blocks entirely above the diagonal are skipped.
+//
 // Candidate mode (M-FALCON): the queries are one user's candidates, all at
 // position n_h. The keys are that user's history, all visible. Each
 // candidate's own key and value are added in the epilogue.
 #include "attn_common.h"
+
+#include <type_traits>
 
 namespace hstu {
 
@@ -46,6 +61,38 @@ __device__ __forceinline__ bf16x4 tr_read(const bf16* lds_ptr) {
       (__attribute__((address_space(3))) s16x4*)(lds_ptr));
   return __builtin_bit_cast(bf16x4, r);
 }
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Element offset of (row, col) in a 64-row K or V tile. For d=128 the 16-byte
+// chunks of a row are XOR-swizzled with ((row & 7) << 1) | ((row >> 3) & 1). Then
+// the 16 rows read by one row-fragment load, and the 4 rows x 32 bytes of one
+// transposing read, each land in distinct banks. For d <= 64, padding each row
+// by 8 elements does the same.
+template <int D>
+__device__ __forceinline__ int tile_off(int row, int col) {
+  if constexpr (D == 128) {
+    const int f = ((row & 7) << 1) | ((row >> 3) & 1);
+    return row * 128 + ((((col >> 3) ^ f)) << 3) + (col & 7);
+  } else {
+    return row * (D + 8) + col;
+  }
+}
+template <int D>
+constexpr int tile_elems() {
+  return D == 128 ? MBN * 128 : MBN * (D + 8) + 64 * 8;  // + slack for the last DMA span
+}
+
+// exact time bucket of a non-negative elapsed time, clamped to the table
+__device__ __forceinline__ int bucket_of(int64_t dt, int T) {
+  dt = dt < 0 ? 0 : dt;
+  const int b = 63 - __builtin_clzll((uint64_t)dt + 1ull);
+  return b < T - 1 ? b : T - 1;
+}
 }  // namespace
 
 bool attn_mfma_supported(int dtype_bf16, int d_qk, int d_v, int P, int T) {
@@ -55,17 +102,22 @@ bool attn_mfma_supported(int dtype_bf16, int d_qk, int d_v, int P, int T) {
 
 template <int D, bool CAND>
 __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
-  constexpr int LDK = D + 8;  // padded LDS row, in elements (keeps 16-byte alignment)
-  constexpr int NKK = D / 16; // k-steps of the S^T contraction
-  constexpr int NC = D / 32;  // 32-wide output column blocks
-  __shared__ __attribute__((aligned(16))) bf16 Ks[MBN * LDK];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[MBN * LDK];
-  __shared__ uint32_t tk_lo[MBN];
-  __shared__ int64_t tk64[MBN];
+  constexpr int NKK = D / 16;       // k-steps of the S^T contraction
+  constexpr int NC = D / 32;        // 32-wide output column blocks
+  constexpr int CPR = D / 8;        // 16-byte chunks per row
+  constexpr int TE = tile_elems<D>();
+  // two LDS buffers per matrix as separate objects, so that alias analysis can tell
+  // the in-flight DMA target from the buffer being read (no conservative waits)
+  __shared__ __attribute__((aligned(16))) bf16 Ks0[TE];
+  __shared__ __attribute__((aligned(16))) bf16 Ks1[TE];
+  __shared__ __attribute__((aligned(16))) bf16 Vs0[TE];
+  __shared__ __attribute__((aligned(16))) bf16 Vs1[TE];
+  __shared__ __attribute__((aligned(16))) uint32_t tk_lo[2][MBN];
+  __shared__ int64_t tk64[2][MBN];
+  __shared__ int64_t kstat[2][2][2];  // [buffer][32-key block][min, max]
   __shared__ float rp[kMaxP];
   __shared__ float rt[kTimeTab];
   __shared__ float rtc[32];
-  __shared__ int64_t kstat[2];
   __shared__ float pself[4][32];
 
   const TileDecode t = decode<CAND>(a, MBM);
@@ -107,10 +159,11 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
   }
   const int64_t tq = (has_time && row_ok) ? a.ts_q[t.q_base + wrow] : 0;
   const uint32_t tq1 = (uint32_t)tq + 1u;
-  const int64_t qmin = wave_min64(row_ok ? tq : INT64_MAX);
-  const int64_t qmax = wave_max64(row_ok ? tq : INT64_MIN);
+  const int64_t qmin = uniform64(wave_min64(row_ok ? tq : INT64_MAX));
+  const int64_t qmax = uniform64(wave_max64(row_ok ? tq : INT64_MIN));
   const int64_t qpos = CAND ? t.qpos0 : t.qpos0 + wrow;
   const int64_t wrow0 = t.qpos0 + 32 * w;  // causal position of the wavefront's first row
+  const int64_t wlast = t.qpos0 + (int64_t)min(32 * w + 31, t.rows - 1);  // its last live row
 
   f32x16 o[NC];
 #pragma unroll
@@ -118,96 +171,223 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[c][r] = 0.f;
 
-  const int64_t nkt = (t.kend + MBN - 1) / MBN;
-  for (int64_t kt = 0; kt < nkt; ++kt) {
-    const int64_t k0 = kt * MBN;
-    __syncthreads();
-    // stage K and V (64 keys x D) into LDS, zero past the data so that hidden
-    // lanes multiply finite values
+  // ---- key tiles go global -> LDS directly (global_load_lds_dwordx4): lane L of one
+  // instruction fills 16-byte slot L of a contiguous 1 KiB span, so the layout is
+  // chosen by which source chunk each lane fetches (the swizzle or the padding of
+  // tile_off). Rows past the data repeat the last valid row: their scores are
+  // masked and multiply finite values.
+  constexpr int SPR = D == 128 ? CPR : CPR + 1;       // 16-byte slots per LDS row
+  constexpr int NSLOT = MBN * SPR;                     // slots per matrix tile
+  constexpr int NINSTR = (NSLOT + 63) / 64;            // wave-instructions per matrix tile
+  int64_t ptk = 0;
+  auto issue_tile = [&](auto bufc, int64_t k0) {
+    constexpr int buf = decltype(bufc)::value;
+    bf16* Kd = buf ? Ks1 : Ks0;
+    bf16* Vd = buf ? Vs1 : Vs0;
+    const int64_t last = t.nk - 1;
 #pragma unroll
-    for (int c = tid; c < MBN * D / 8; c += 256) {
-      const int key = c / (D / 8), col = (c % (D / 8)) * 8;
-      const bool ok = k0 + key < t.nk;
-      bf16x8 kv, vv;
-      if (ok) {
-        const int64_t grow = t.k_base + k0 + key;
-        kv = load_bf16x8(k + grow * a.ld_k + (int64_t)h * D + col);
-        vv = load_bf16x8(v + grow * a.ld_v + (int64_t)h * D + col);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) { kv[i] = (bf16)0.f; vv[i] = (bf16)0.f; }
+    for (int i = w; i < NINSTR; i += 4) {
+      const int slot = 64 * i + lane;
+      if (slot < NSLOT) {
+        const int row = slot / SPR, pc = slot % SPR;
+        int c;
+        if constexpr (D == 128)
+          c = pc ^ (((row & 7) << 1) | ((row >> 3) & 1));
+        else
+          c = pc < CPR ? pc : 0;  // padding slot: any in-bounds chunk
+        const int64_t grow = t.k_base + min(k0 + row, last);
+        const bf16* gk = k + grow * a.ld_k + (int64_t)h * D + 8 * c;
+        const bf16* gv = v + grow * a.ld_v + (int64_t)h * D + 8 * c;
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)gk,
+                                         (__attribute__((address_space(3))) void*)(&Kd[512 * i]),
+                                         16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)gv,
+                                         (__attribute__((address_space(3))) void*)(&Vd[512 * i]),
+                                         16, 0, 0);
       }
-      *reinterpret_cast<bf16x8*>(&Ks[key * LDK + col]) = kv;
-      *reinterpret_cast<bf16x8*>(&Vs[key * LDK + col]) = vv;
     }
+    if (has_time && tid < MBN) ptk = (k0 + tid < t.nk) ? a.ts_k[t.k_base + k0 + tid] : 0;
+  };
+  auto finish_tile = [&](auto bufc, int64_t k0) {
+    constexpr int buf = decltype(bufc)::value;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (has_time && tid < MBN) {
       const bool ok = k0 + tid < t.nk;
-      const int64_t tk = ok ? a.ts_k[t.k_base + k0 + tid] : 0;
-      tk_lo[tid] = (uint32_t)tk;
-      tk64[tid] = tk;
-      const int64_t mn = wave_min64(ok ? tk : INT64_MAX);
-      const int64_t mx = wave_max64(ok ? tk : INT64_MIN);
-      if (tid == 0) { kstat[0] = mn; kstat[1] = mx; }
+      tk_lo[buf][tid] = (uint32_t)ptk;
+      tk64[buf][tid] = ptk;
+      // min and max over each half-wavefront (one 32-key block each)
+      int64_t mn = ok ? ptk : INT64_MAX, mx = ok ? ptk : INT64_MIN;
+#pragma unroll
+      for (int o2 = 16; o2 >= 1; o2 >>= 1) {
+        const int64_t a1 = __shfl_xor(mn, o2, 64), a2 = __shfl_xor(mx, o2, 64);
+        mn = a1 < mn ? a1 : mn;
+        mx = a2 > mx ? a2 : mx;
+      }
+      if ((tid & 31) == 0) {
+        kstat[buf][tid >> 5][0] = mn;
+        kstat[buf][tid >> 5][1] = mx;
+      }
     }
-    __syncthreads();
-    if (!wave_live) continue;
-    const bool fast = !has_time || time_fast_ok(qmin, qmax, kstat[0], kstat[1]);
+  };
+
+  const int64_t nkt = (t.kend + MBN - 1) / MBN;
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  if (nkt > 0) {
+    issue_tile(B0{}, 0);
+    finish_tile(B0{}, 0);
+  }
+  __syncthreads();
+
+  // per-lane key offset inside a 32-key block for accumulator slot r
+  // keyoff(r) = 8*(r/4) + 4*hl + (r%4)
+  auto tile_step = [&](auto bufc, int64_t kt) {
+    constexpr int buf = decltype(bufc)::value;
+    using BN_ = std::integral_constant<int, 1 - buf>;
+    const int64_t k0 = kt * MBN;
+    if (kt + 1 < nkt) issue_tile(BN_{}, k0 + MBN);
+
+    if (wave_live) {
+      const bf16* Kt = buf ? Ks1 : Ks0;
+      const bf16* Vt = buf ? Vs1 : Vs0;
+      // ---- classify both 32-key blocks (wave-uniform scalars)
+      bool act[2], need_mask[2], uni[2], pos_c[2], time_c[2], time_fast[2], time_sorted[2];
+      float ubias[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int64_t kb0 = k0 + 32 * kb;
+        act[kb] = kb0 < t.kend && (CAND || kb0 <= wlast);
+        need_mask[kb] = CAND ? (kb0 + 32 > t.nk) : (kb0 + 31 > wrow0);
+        const int64_t min_dpos = (CAND ? t.qpos0 : wrow0) - (kb0 + 31);
+        pos_c[kb] = !has_pos || min_dpos >= P - 1;
+        float b = has_pos && pos_c[kb] ? rp[P - 1] : 0.f;
+        time_c[kb] = true;
+        time_fast[kb] = true;
+        time_sorted[kb] = true;
+        if (has_time && act[kb]) {
+          const int64_t kmin = uniform64(kstat[buf][kb][0]);
+          const int64_t kmax = uniform64(kstat[buf][kb][1]);
+          const int64_t lo = qmin - kmax, hi = qmax - kmin;  // elapsed-time range
+          const int blo = bucket_of(lo, T), bhi = bucket_of(hi, T);
+          time_c[kb] = blo == bhi;
+          if (time_c[kb]) b += rt[blo < 63 ? blo : 63];
+          time_fast[kb] = time_fast_ok(qmin, qmax, kmin, kmax);
+          time_sorted[kb] = lo >= 0;
+        }
+        uni[kb] = pos_c[kb] && time_c[kb];
+        ubias[kb] = b;
+      }
+
+      // ---- S^T for both blocks first (the matrix core runs ahead of the ALU work)
+      f32x16 s[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        if (!act[kb]) continue;
+        const float init = uni[kb] ? ubias[kb] : 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][r] = init;
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+          const bf16x8 kf = load_bf16x8(&Kt[tile_off<D>(32 * kb + l32, 16 * kk + 8 * hl)]);
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s[kb], 0, 0, 0);
+        }
+      }
 
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int64_t kb0 = k0 + 32 * kb;
-      if (kb0 >= t.kend) continue;
-      if (!CAND && kb0 > wrow0 + 31) continue;  // every key above every row of this wavefront
-      f32x16 s;
+      for (int kb = 0; kb < 2; ++kb) {
+        if (!act[kb]) continue;
+        const int64_t kb0 = k0 + 32 * kb;
+        f32x16 x = s[kb];
+        if (!uni[kb]) {
+          // per-element bias for this block
+          const int dbase = (int)(qpos - kb0) - 4 * hl;  // i - j = dbase - (8*(r/4) + r%4)
+          float bpos = pos_c[kb] ? ubias[kb] : 0.f;
+          if (!pos_c[kb]) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = 0.f;
+            for (int r = 0; r < 16; ++r) {
+              int d = dbase - (8 * (r >> 2) + (r & 3));
+              d = d < 0 ? 0 : (d < P - 1 ? d : P - 1);
+              x[r] += rp[d];
+            }
+          } else if (!time_c[kb]) {
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        const bf16x8 kf = load_bf16x8(&Ks[(32 * kb + l32) * LDK + 16 * kk + 8 * hl]);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s, 0, 0, 0);
-      }
-      // s[r] = S[query wrow][key 32kb + 8(r/4) + 4hl + r%4]
-      const bool need_mask = CAND ? (kb0 + 32 > t.nk) : (kb0 + 31 > wrow0);
-      bf16x8 pa[2];
+            for (int r = 0; r < 16; ++r) x[r] += bpos;
+          }
+          if (has_time) {
+            if (time_c[kb]) {
+              if (!pos_c[kb]) {
+                const float tb = ubias[kb];  // the constant time term alone
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int keyl = 32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3);
-        const int64_t j = k0 + keyl;
-        const int dpos = (int)(qpos - j);
-        float x = s[r];
-        if (has_pos) x += rp[pos_bucket(dpos, P)];
-        if (has_time) {
-          if (fast) {
-            x += rtc[time_clz_fast(tq1, tk_lo[keyl])];
-          } else {
-            const int bt = time_bucket64(tq, tk64[keyl]);
-            x += rt[bt < 63 ? bt : 63];
+                for (int r = 0; r < 16; ++r) x[r] += tb;
+              }
+            } else {
+              const uint32_t* tkl = tk_lo[buf] + 32 * kb + 4 * hl;
+              if (time_fast[kb] && time_sorted[kb]) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                  const u32x4 tk4 = *reinterpret_cast<const u32x4*>(tkl + 8 * g);
+#pragma unroll
+                  for (int e = 0; e < 4; ++e)
+                    x[4 * g + e] += rtc[__builtin_clz((tq1 - tk4[e]) | 1u)];
+                }
+              } else if (time_fast[kb]) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                  const u32x4 tk4 = *reinterpret_cast<const u32x4*>(tkl + 8 * g);
+#pragma unroll
+                  for (int e = 0; e < 4; ++e) x[4 * g + e] += rtc[time_clz_fast(tq1, tk4[e])];
+                }
+              } else {
+                const int64_t* tk = tk64[buf] + 32 * kb + 4 * hl;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                  const int bt = time_bucket64(tq, tk[8 * (r >> 2) + (r & 3)]);
+                  x[r] += rt[bt < 63 ? bt : 63];
+                }
+              }
+            }
           }
         }
-        float p = silu_fast(x);
-        if (need_mask) {
-          const bool vis = CAND ? (j < t.nk) : (dpos >= 0);
-          p = vis ? p : 0.f;
+        // SiLU, then the mask on blocks that cross the diagonal or the history tail
+        float p[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) p[r] = silu_fast(x[r]);
+        if (need_mask[kb]) {
+          const int dbase = (int)(qpos - kb0) - 4 * hl;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int keyoff = 8 * (r >> 2) + 4 * hl + (r & 3);
+            const bool vis = CAND ? (kb0 + keyoff < t.nk) : (dbase - (8 * (r >> 2) + (r & 3)) >= 0);
+            p[r] = vis ? p[r] : 0.f;
+          }
         }
-        pa[r >> 3][r & 7] = (bf16)p;
-      }
-      // O += P V; the k-slot (hl, i) of step s2 is key 16*s2 + 8*(i/4) + 4*hl + i%4
-      const int g = lane >> 4, rho = lane & 15;
+        bf16x8 pa[2];
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const int kbase = 32 * kb + 16 * s2 + 4 * hl + (rho >> 2);
+        for (int r = 0; r < 16; ++r) pa[r >> 3][r & 7] = (bf16)p[r];
+        // O += P V; the k-slot (hl, i) of step s2 is key 16*s2 + 8*(i/4) + 4*hl + i%4
+        const int g = lane >> 4, rho = lane & 15;
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          const int col = c * 32 + 16 * (g & 1) + 4 * (rho & 3);
-          const bf16x4 v1 = tr_read(&Vs[kbase * LDK + col]);
-          const bf16x4 v2 = tr_read(&Vs[(kbase + 8) * LDK + col]);
-          bf16x8 bv;
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const int krow = 32 * kb + 16 * s2 + 4 * hl + (rho >> 2);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) { bv[i] = v1[i]; bv[4 + i] = v2[i]; }
-          o[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[s2], bv, o[c], 0, 0, 0);
+          for (int c = 0; c < NC; ++c) {
+            const int col = c * 32 + 16 * (g & 1) + 4 * (rho & 3);
+            const bf16x4 v1 = tr_read(&Vt[tile_off<D>(krow, col)]);
+            const bf16x4 v2 = tr_read(&Vt[tile_off<D>(krow + 8, col)]);
+            bf16x8 bv;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) { bv[i] = v1[i]; bv[4 + i] = v2[i]; }
+            o[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[s2], bv, o[c], 0, 0, 0);
+          }
         }
       }
     }
+    if (kt + 1 < nkt) finish_tile(BN_{}, k0 + MBN);
+    __syncthreads();
+  };
+  for (int64_t kt = 0; kt < nkt; kt += 2) {
+    tile_step(B0{}, kt);
+    if (kt + 1 < nkt) tile_step(B1{}, kt + 1);
   }
 
   if (CAND) {

@@ -154,6 +154,10 @@ class LayerInputs:
     eps: float = 1e-5
     residual: int = 0
 
+    @property
+    def lengths(self):
+        return np.diff(self.offsets)
+
 
 @dataclass
 class MfalconInputs:
