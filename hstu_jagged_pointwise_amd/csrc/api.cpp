@@ -123,7 +123,11 @@ int attn_tile_rows(const hstu_attn_desc* d) {
 hipError_t run_attention(const hstu_attn_desc* d, const AttnArgs& a, bool cand, hipStream_t s) {
   const bool mfma = attn_mfma_supported(d->dtype == HSTU_BF16, d->d_qk, d->d_v,
                                         d->num_pos_buckets, d->num_time_buckets);
-  return mfma ? launch_attn_mfma(a, cand, s) : launch_attn_simple(a, d->dtype == HSTU_BF16, cand, s);
+  if (!mfma) return launch_attn_simple(a, d->dtype == HSTU_BF16, cand, s);
+  // work items were planned for the MFMA kernel's tile; every caller here passes
+  // equal K and V strides (d_qk == d_v), which that kernel's key-tile DMA needs
+  if (!attn_mfma_strides_ok(a)) return hipErrorInvalidValue;
+  return launch_attn_mfma(a, cand, s);
 }
 
 AttnArgs base_args(const hstu_attn_desc* d) {
@@ -274,8 +278,8 @@ hstu_status layer_once(const hstu_layer_desc* d, const int64_t* off_dev, const i
   aa.items = b.items;
   aa.n_items = (int)j.items;
   HSTU_TRY(run_attention(&a, aa, false, s), "attention");
-  HSTU_TRY(launch_ln_gate(b.o, hv, vw.u, vw.ld, w.ln_gamma, w.ln_beta, a.ln_eps, b.g, hv, rows, hv,
-                          bf, s),
+  HSTU_TRY(launch_ln_gate(b.o, hv, 1, 0, vw.u, vw.ld, w.ln_gamma, w.ln_beta, a.ln_eps, b.g, hv, rows,
+                          hv, bf, s),
            "layer norm gate");
   HSTU_TRY(launch_gemm(b.g, hv, w.w2, hv, w.b2, d->residual ? x : nullptr, d->d_model, y,
                        d->d_model, rows, d->d_model, hv, 0, bf, s),
@@ -287,8 +291,13 @@ hstu_status layer_once(const hstu_layer_desc* d, const int64_t* off_dev, const i
 struct MfPlan {
   Jagged hist;
   int64_t cand_total = 0;
+  int kv_splits = 1;          // key-range splits of the candidate attention (MFMA kernel only)
+  int64_t keys_per_split = 0;
   size_t ws = 0;
 };
+
+constexpr int64_t kKeysPerSplit = 512;  // history keys per candidate-attention workgroup
+constexpr int kMaxSplits = 16;
 
 struct MfBufs {
   LayerBufs hist;             // history scratch (items, uvqk of the current layer unused)
@@ -316,7 +325,7 @@ void carve_mfalcon(Carver& c, const mfalcon_desc* d, const MfPlan& p, MfBufs* b)
   b->hx[0] = ld.num_layers > 1 ? c.take((size_t)nh * ld.d_model * es) : nullptr;
   b->hx[1] = ld.num_layers > 2 ? c.take((size_t)nh * ld.d_model * es) : nullptr;
   b->c_uvqk = c.take((size_t)m * f1 * es);
-  b->c_o = (float*)c.take((size_t)m * hv * sizeof(float));
+  b->c_o = (float*)c.take((size_t)p.kv_splits * m * hv * sizeof(float));
   b->c_g = c.take((size_t)m * hv * es);
   b->cx[0] = ld.num_layers > 1 ? c.take((size_t)m * ld.d_model * es) : nullptr;
   b->cx[1] = ld.num_layers > 2 ? c.take((size_t)m * ld.d_model * es) : nullptr;
@@ -342,6 +351,15 @@ hstu_status plan_mfalcon(const mfalcon_desc* d, const int64_t* hoff, const int64
                   (long long)nh, a.max_seq_len);
   }
   p->cand_total = cj.total;
+  // The MFMA kernel splits the history into key ranges of kKeysPerSplit (more when
+  // the history is long), so that a microbatch of ~1k candidates still fills the
+  // device. The geometry depends on the history lengths only.
+  if (attn_mfma_supported(a.dtype == HSTU_BF16, a.d_qk, a.d_v, a.num_pos_buckets,
+                          a.num_time_buckets) && p->hist.max_len > kKeysPerSplit) {
+    p->kv_splits = (int)std::min<int64_t>(kMaxSplits,
+                                          (p->hist.max_len + kKeysPerSplit - 1) / kKeysPerSplit);
+    p->keys_per_split = ((p->hist.max_len + p->kv_splits - 1) / p->kv_splits + 63) / 64 * 64;
+  }
   if ((int64_t)p->hist.items * a.num_heads >= (int64_t(1) << 31))
     return fail(HSTU_UNSUPPORTED, "too many history tiles for one launch");
   Carver c{nullptr};
@@ -426,8 +444,8 @@ hstu_status hstu_attn_fwd(const hstu_attn_desc* desc, const int64_t* seq_offsets
   HSTU_TRY(run_attention(desc, a, false, s), "attention");
   if (u) {
     const int hv = desc->num_heads * desc->d_v;
-    HSTU_TRY(launch_ln_gate(o32, hv, u, hv, ln_gamma, ln_beta, desc->ln_eps, out, hv, p.j.total, hv,
-                            desc->dtype == HSTU_BF16, s),
+    HSTU_TRY(launch_ln_gate(o32, hv, 1, 0, u, hv, ln_gamma, ln_beta, desc->ln_eps, out, hv,
+                            p.j.total, hv, desc->dtype == HSTU_BF16, s),
              "layer norm gate");
   }
   return HSTU_OK;
@@ -588,13 +606,18 @@ hstu_status mfalcon_score(const mfalcon_desc* desc, const int64_t* hist_offsets_
       aa.row_begin = m0;
       aa.row_end = m1;
       aa.max_user_rows = max_rows;
+      // key-range splits of the history: fixed by the history lengths alone, so a
+      // candidate's reduction order never depends on the microbatch around it
+      aa.kv_splits = p.kv_splits;
+      aa.keys_per_split = p.keys_per_split;
+      aa.part_stride = rows * hv;
       for (int u0 = ub; u0 < ue; u0 += 65535) {
         aa.user_begin = u0;
         aa.n_users = std::min(ue - u0, 65535);
         HSTU_TRY(run_attention(&a, aa, true, s), "candidate attention");
       }
-      HSTU_TRY(launch_ln_gate(b.c_o, hv, cv.u, cv.ld, w.ln_gamma, w.ln_beta, a.ln_eps, b.c_g, hv,
-                              rows, hv, bf, s),
+      HSTU_TRY(launch_ln_gate(b.c_o, hv, aa.kv_splits, aa.part_stride, cv.u, cv.ld, w.ln_gamma,
+                              w.ln_beta, a.ln_eps, b.c_g, hv, rows, hv, bf, s),
                "candidate layer norm gate");
       HSTU_TRY(launch_gemm(b.c_g, hv, w.w2, hv, w.b2, ld.residual ? in : nullptr, dm, out, dm, rows,
                            dm, hv, 0, bf, s),

@@ -12,6 +12,7 @@ struct TileDecode {
   int rows;         // valid query rows in the tile
   int64_t k_base;   // global row of key 0
   int64_t nk;       // keys that hold data (causal: whole sequence; candidates: history)
+  int64_t kbeg;     // first key of this work item (candidate splits), else 0
   int64_t kend;     // keys that can be visible (causal: up to the last row of the tile)
   int64_t qpos0;    // position of tile row 0 (causal) or of every candidate (n_h)
   bool valid;
@@ -36,6 +37,7 @@ __device__ __forceinline__ TileDecode decode(const AttnArgs& a, int bm) {
     d.q_local = d.q_base;
     d.k_base = s0;
     d.nk = n;
+    d.kbeg = 0;
     d.kend = r0 + d.rows;
     d.qpos0 = r0;
   } else {
@@ -52,8 +54,14 @@ __device__ __forceinline__ TileDecode decode(const AttnArgs& a, int bm) {
     d.q_local = r0 - a.row_begin;
     d.k_base = a.k_offsets[b];
     d.nk = a.k_offsets[b + 1] - d.k_base;
+    d.kbeg = 0;
     d.kend = d.nk;
     d.qpos0 = d.nk;
+    if (a.kv_splits > 1) {
+      const int64_t lo = (int64_t)blockIdx.z * a.keys_per_split;
+      d.kbeg = lo < d.nk ? lo : d.nk;
+      d.kend = lo + a.keys_per_split < d.nk ? lo + a.keys_per_split : d.nk;
+    }
   }
   d.valid = true;
   return d;

@@ -68,23 +68,17 @@ __device__ __forceinline__ int64_t uniform64(int64_t v) {
   return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
-// Element offset of (row, col) in a 64-row K or V tile. For d=128 the 16-byte
-// chunks of a row are XOR-swizzled with ((row & 7) << 1) | ((row >> 3) & 1). Then
-// the 16 rows read by one row-fragment load, and the 4 rows x 32 bytes of one
-// transposing read, each land in distinct banks. For d <= 64, padding each row
-// by 8 elements does the same.
+// Element offset of (row, col) in a 64-row K or V tile: rows padded by 8 elements.
+// With a row stride of D+8 elements the 16 rows of one row-fragment load
+// (ds_read_b128) fall in distinct banks, and every read address is one base
+// register plus an immediate, which keeps register pressure down.
 template <int D>
 __device__ __forceinline__ int tile_off(int row, int col) {
-  if constexpr (D == 128) {
-    const int f = ((row & 7) << 1) | ((row >> 3) & 1);
-    return row * 128 + ((((col >> 3) ^ f)) << 3) + (col & 7);
-  } else {
-    return row * (D + 8) + col;
-  }
+  return row * (D + 8) + col;
 }
 template <int D>
 constexpr int tile_elems() {
-  return D == 128 ? MBN * 128 : MBN * (D + 8) + 64 * 8;  // + slack for the last DMA span
+  return MBN * (D + 8) + 64 * 8;  // + slack for the last DMA span
 }
 
 // exact time bucket of a non-negative elapsed time, clamped to the table
@@ -98,6 +92,11 @@ __device__ __forceinline__ int bucket_of(int64_t dt, int T) {
 bool attn_mfma_supported(int dtype_bf16, int d_qk, int d_v, int P, int T) {
   (void)T;
   return dtype_bf16 && d_qk == d_v && (d_qk == 32 || d_qk == 64 || d_qk == 128) && P <= kMaxP;
+}
+
+bool attn_mfma_strides_ok(const AttnArgs& a) {
+  // the key-tile DMA shares one per-lane offset between K and V; offsets are 32-bit
+  return a.ld_k == a.ld_v && a.ld_k > 0 && (int64_t)(MBN + 1) * a.ld_k < (int64_t(1) << 31);
 }
 
 template <int D, bool CAND>
@@ -165,6 +164,11 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
   const int64_t wrow0 = t.qpos0 + 32 * w;  // causal position of the wavefront's first row
   const int64_t wlast = t.qpos0 + (int64_t)min(32 * w + 31, t.rows - 1);  // its last live row
 
+  // constant A fragment for the bias k-step: A[key][0] = A[key][1] = 1
+  bf16x8 ones;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ones[i] = (bf16)((hl == 0 && i < 2) ? 1.f : 0.f);
+
   f32x16 o[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c)
@@ -172,36 +176,49 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
     for (int r = 0; r < 16; ++r) o[c][r] = 0.f;
 
   // ---- key tiles go global -> LDS directly (global_load_lds_dwordx4): lane L of one
-  // instruction fills 16-byte slot L of a contiguous 1 KiB span, so the layout is
-  // chosen by which source chunk each lane fetches (the swizzle or the padding of
-  // tile_off). Rows past the data repeat the last valid row: their scores are
-  // masked and multiply finite values.
-  constexpr int SPR = D == 128 ? CPR : CPR + 1;       // 16-byte slots per LDS row
+  // instruction fills 16-byte slot L of a contiguous 1 KiB span, so the padded
+  // layout comes from which source chunk each lane fetches. Rows past the data
+  // repeat the last valid row: their scores are masked and multiply finite values.
+  constexpr int SPR = CPR + 1;                         // 16-byte slots per LDS row
   constexpr int NSLOT = MBN * SPR;                     // slots per matrix tile
   constexpr int NINSTR = (NSLOT + 63) / 64;            // wave-instructions per matrix tile
   int64_t ptk = 0;
+  // Per-lane source offsets (elements from the tile's first row) of this wavefront's
+  // DMA instructions, computed once. K and V share the row stride. A full tile
+  // then needs only the uniform base pointer advanced; the tail tile clamps rows
+  // past the data to the last valid row.
+  constexpr int NIW = (NINSTR + 3) / 4;
+  uint32_t soff[NIW];
+#pragma unroll
+  for (int j = 0; j < NIW; ++j) {
+    const int slot = 64 * (w + 4 * j) + lane;
+    const int row = slot / SPR, pc = slot % SPR;
+    soff[j] = (uint32_t)(row * a.ld_k + 8 * (pc < CPR ? pc : 0));
+  }
   auto issue_tile = [&](auto bufc, int64_t k0) {
     constexpr int buf = decltype(bufc)::value;
     bf16* Kd = buf ? Ks1 : Ks0;
     bf16* Vd = buf ? Vs1 : Vs0;
     const int64_t last = t.nk - 1;
+    const bf16* kb = k + (t.k_base + k0) * a.ld_k + (int64_t)h * D;
+    const bf16* vb = v + (t.k_base + k0) * a.ld_v + (int64_t)h * D;
+    const bool full = k0 + MBN - 1 <= last;
 #pragma unroll
-    for (int i = w; i < NINSTR; i += 4) {
+    for (int j = 0; j < NIW; ++j) {
+      const int i = w + 4 * j;
+      if (i >= NINSTR) break;
       const int slot = 64 * i + lane;
       if (slot < NSLOT) {
-        const int row = slot / SPR, pc = slot % SPR;
-        int c;
-        if constexpr (D == 128)
-          c = pc ^ (((row & 7) << 1) | ((row >> 3) & 1));
-        else
-          c = pc < CPR ? pc : 0;  // padding slot: any in-bounds chunk
-        const int64_t grow = t.k_base + min(k0 + row, last);
-        const bf16* gk = k + grow * a.ld_k + (int64_t)h * D + 8 * c;
-        const bf16* gv = v + grow * a.ld_v + (int64_t)h * D + 8 * c;
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)gk,
+        uint32_t off = soff[j];
+        if (!full) {
+          const int row = slot / SPR, pc = slot % SPR;
+          const int64_t r = min(k0 + row, last) - k0;
+          off = (uint32_t)(r * a.ld_k + 8 * (pc < CPR ? pc : 0));
+        }
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kb + off),
                                          (__attribute__((address_space(3))) void*)(&Kd[512 * i]),
                                          16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)gv,
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vb + off),
                                          (__attribute__((address_space(3))) void*)(&Vd[512 * i]),
                                          16, 0, 0);
       }
@@ -230,12 +247,12 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
     }
   };
 
-  const int64_t nkt = (t.kend + MBN - 1) / MBN;
+  const int64_t nkt = (t.kend - t.kbeg + MBN - 1) / MBN;
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
   if (nkt > 0) {
-    issue_tile(B0{}, 0);
-    finish_tile(B0{}, 0);
+    issue_tile(B0{}, t.kbeg);
+    finish_tile(B0{}, t.kbeg);
   }
   __syncthreads();
 
@@ -244,7 +261,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
   auto tile_step = [&](auto bufc, int64_t kt) {
     constexpr int buf = decltype(bufc)::value;
     using BN_ = std::integral_constant<int, 1 - buf>;
-    const int64_t k0 = kt * MBN;
+    const int64_t k0 = t.kbeg + kt * MBN;
     if (kt + 1 < nkt) issue_tile(BN_{}, k0 + MBN);
 
     if (wave_live) {
@@ -257,7 +274,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
       for (int kb = 0; kb < 2; ++kb) {
         const int64_t kb0 = k0 + 32 * kb;
         act[kb] = kb0 < t.kend && (CAND || kb0 <= wlast);
-        need_mask[kb] = CAND ? (kb0 + 32 > t.nk) : (kb0 + 31 > wrow0);
+        need_mask[kb] = CAND ? (kb0 + 32 > t.kend) : (kb0 + 31 > wrow0);
         const int64_t min_dpos = (CAND ? t.qpos0 : wrow0) - (kb0 + 31);
         pos_c[kb] = !has_pos || min_dpos >= P - 1;
         float b = has_pos && pos_c[kb] ? rp[P - 1] : 0.f;
@@ -278,49 +295,173 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
         ubias[kb] = b;
       }
 
-      // ---- S^T for both blocks first (the matrix core runs ahead of the ALU work)
-      f32x16 s[2];
+      // ---- S^T. A uniform bias enters as one extra MFMA k-step: a constant all-ones
+      // A fragment (keys x {0,1}) times a B fragment holding bias_hi, bias_lo
+      // (bf16 split, exact to ~2^-16 relative) for every row. The accumulator then
+      // starts from the inline zero, and no vector instruction touches the bias.
+      auto qk = [&](int kb, bool with_bias, float bias) {
+        f32x16 acc;
+        const bf16x8 kf0 = load_bf16x8(&Kt[tile_off<D>(32 * kb + l32, 8 * hl)]);
+        if (with_bias) {
+          bf16x8 bfrag;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        if (!act[kb]) continue;
-        const float init = uni[kb] ? ubias[kb] : 0.f;
+          for (int i = 0; i < 8; ++i) bfrag[i] = (bf16)0.f;
+          const bf16 bhi = (bf16)bias;
+          if (hl == 0) {
+            bfrag[0] = bhi;
+            bfrag[1] = (bf16)(bias - (float)bhi);
+          }
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, bfrag, f32x16{}, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf0, qf[0], acc, 0, 0, 0);
+        } else {
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf0, qf[0], f32x16{}, 0, 0, 0);
+        }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][r] = init;
+        for (int kk = 1; kk < NKK; ++kk) {
+          const bf16x8 kf = load_bf16x8(&Kt[tile_off<D>(32 * kb + l32, 16 * kk + 8 * hl)]);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], acc, 0, 0, 0);
+        }
+        return acc;
+      };
+      // SiLU to bf16 A fragments, with the mask applied when asked
+      auto activate = [&](const f32x16& x, int kb, bool mask, bf16x8* pa) {
+        const int64_t kb0 = k0 + 32 * kb;
+        const int dbase = (int)(qpos - kb0) - 4 * hl;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float p = silu_fast(x[r]);
+          if (mask) {
+            const int keyoff = 8 * (r >> 2) + 4 * hl + (r & 3);
+            const bool vis = CAND ? (kb0 + keyoff < t.kend) : (dbase - (8 * (r >> 2) + (r & 3)) >= 0);
+            p = vis ? p : 0.f;
+          }
+          pa[r >> 3][r & 7] = (bf16)p;
+        }
+      };
+      // O += P V; the k-slot (hl, i) of step s2 is key 16*s2 + 8*(i/4) + 4*hl + i%4
+      auto pv = [&](int kb, const bf16x8* pa) {
+        const int g = lane >> 4, rho = lane & 15;
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const int krow = 32 * kb + 16 * s2 + 4 * hl + (rho >> 2);
+#pragma unroll
+          for (int c = 0; c < NC; ++c) {
+            const int col = c * 32 + 16 * (g & 1) + 4 * (rho & 3);
+            const bf16x4 v1 = tr_read(&Vt[tile_off<D>(krow, col)]);
+            const bf16x4 v2 = tr_read(&Vt[tile_off<D>(krow + 8, col)]);
+            bf16x8 bv;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) { bv[i] = v1[i]; bv[4 + i] = v2[i]; }
+            o[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[s2], bv, o[c], 0, 0, 0);
+          }
+        }
+      };
+
+      const bool fast = act[0] && act[1] && uni[0] && uni[1] && !need_mask[0] && !need_mask[1];
+      if (fast) {
+        // Common case: both blocks live, uniform bias, no mask. The instruction order
+        // is written out and fenced (sched_barrier) so that the in-order wavefront
+        // issues one MFMA (~40 cycles in the matrix core), then the independent
+        // vector work that fits under it:
+        //   block 0: S^T chain;
+        //   block 1: S^T chain, each step carrying the SiLU of ~2 of block 0's scores;
+        //   block 0: P V, each step carrying the SiLU of 2 of block 1's scores;
+        //   block 1: P V.
+        constexpr int NS = NKK + 1;  // S steps per block (bias step + NKK)
+        auto bias_frag = [&](float bias) {
+          bf16x8 bfrag;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) bfrag[i] = (bf16)0.f;
+          const bf16 bhi = (bf16)bias;
+          if (hl == 0) {
+            bfrag[0] = bhi;
+            bfrag[1] = (bf16)(bias - (float)bhi);
+          }
+          return bfrag;
+        };
+        auto kfrag = [&](int kb, int kk) {
+          return load_bf16x8(&Kt[tile_off<D>(32 * kb + l32, 16 * kk + 8 * hl)]);
+        };
+        const int g = lane >> 4, rho = lane & 15;
+        auto vfrag = [&](int kb, int m) {  // m = s2 * NC + c
+          const int s2 = m / NC, c = m % NC;
+          const int krow = 32 * kb + 16 * s2 + 4 * hl + (rho >> 2);
+          const int col = c * 32 + 16 * (g & 1) + 4 * (rho & 3);
+          const bf16x4 v1 = tr_read(&Vt[tile_off<D>(krow, col)]);
+          const bf16x4 v2 = tr_read(&Vt[tile_off<D>(krow + 8, col)]);
+          bf16x8 bv;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) { bv[i] = v1[i]; bv[4 + i] = v2[i]; }
+          return bv;
+        };
+        auto act_range = [&](const f32x16& x, bf16x8* pa, int r0, int r1) {
+#pragma unroll
+          for (int r = r0; r < r1; ++r) pa[r >> 3][r & 7] = (bf16)silu_fast(x[r]);
+        };
+        const bf16x8 bf0 = bias_frag(ubias[0]), bf1 = bias_frag(ubias[1]);
+        // block 0: S^T
+        bf16x8 kq[NKK];
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) kq[kk] = kfrag(0, kk);
+        f32x16 s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, bf0, f32x16{}, 0, 0, 0);
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk)
+          s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kq[kk], qf[kk], s0, 0, 0, 0);
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) kq[kk] = kfrag(1, kk);
+        __builtin_amdgcn_sched_barrier(0);
+        // block 1: S^T, carrying block 0's SiLU
+        bf16x8 pa0[2], pa1[2];
+        f32x16 s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, bf1, f32x16{}, 0, 0, 0);
+        act_range(s0, pa0, 0, 16 / NS);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
-          const bf16x8 kf = load_bf16x8(&Kt[tile_off<D>(32 * kb + l32, 16 * kk + 8 * hl)]);
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s[kb], 0, 0, 0);
+          s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kq[kk], qf[kk], s1, 0, 0, 0);
+          act_range(s0, pa0, (kk + 1) * 16 / NS, (kk + 2) * 16 / NS);
+          __builtin_amdgcn_sched_barrier(0);
         }
-      }
-
+        // block 0: P V, carrying block 1's SiLU
+        constexpr int NPV = 2 * NC;
+        bf16x8 vb = vfrag(0, 0);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        if (!act[kb]) continue;
-        const int64_t kb0 = k0 + 32 * kb;
-        f32x16 x = s[kb];
-        if (!uni[kb]) {
-          // per-element bias for this block
-          const int dbase = (int)(qpos - kb0) - 4 * hl;  // i - j = dbase - (8*(r/4) + r%4)
-          float bpos = pos_c[kb] ? ubias[kb] : 0.f;
-          if (!pos_c[kb]) {
+        for (int m = 0; m < NPV; ++m) {
+          const bf16x8 vnext = vfrag(m + 1 < NPV ? 0 : 1, (m + 1) % NPV);
+          o[m % NC] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa0[m / NC], vb, o[m % NC], 0, 0, 0);
+          act_range(s1, pa1, m * 16 / NPV, (m + 1) * 16 / NPV);
+          vb = vnext;
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // block 1: P V
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              int d = dbase - (8 * (r >> 2) + (r & 3));
-              d = d < 0 ? 0 : (d < P - 1 ? d : P - 1);
-              x[r] += rp[d];
-            }
-          } else if (!time_c[kb]) {
+        for (int m = 0; m < NPV; ++m) {
+          const bf16x8 vnext = vfrag(1, (m + 1) % NPV);
+          o[m % NC] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa1[m / NC], vb, o[m % NC], 0, 0, 0);
+          vb = vnext;
+        }
+      } else {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) x[r] += bpos;
-          }
-          if (has_time) {
-            if (time_c[kb]) {
-              if (!pos_c[kb]) {
-                const float tb = ubias[kb];  // the constant time term alone
+        for (int kb = 0; kb < 2; ++kb) {
+          if (!act[kb]) continue;
+          const int64_t kb0 = k0 + 32 * kb;
+          f32x16 x = qk(kb, uni[kb] && ubias[kb] != 0.f, ubias[kb]);
+          if (!uni[kb]) {
+            // per-element bias for this block
+            const int dbase = (int)(qpos - kb0) - 4 * hl;  // i - j = dbase - (8*(r/4) + r%4)
+            if (!pos_c[kb]) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) x[r] += tb;
+              for (int r = 0; r < 16; ++r) {
+                int d = dbase - (8 * (r >> 2) + (r & 3));
+                d = d < 0 ? 0 : (d < P - 1 ? d : P - 1);
+                x[r] += rp[d];
               }
-            } else {
+            }
+            // the constant part of the bias (position or time, whichever is constant)
+            if (pos_c[kb] != time_c[kb] && ubias[kb] != 0.f) {
+#pragma unroll
+              for (int r = 0; r < 16; ++r) x[r] += ubias[kb];
+            }
+            if (has_time && !time_c[kb]) {
               const uint32_t* tkl = tk_lo[buf] + 32 * kb + 4 * hl;
               if (time_fast[kb] && time_sorted[kb]) {
 #pragma unroll
@@ -347,38 +488,9 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
               }
             }
           }
-        }
-        // SiLU, then the mask on blocks that cross the diagonal or the history tail
-        float p[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) p[r] = silu_fast(x[r]);
-        if (need_mask[kb]) {
-          const int dbase = (int)(qpos - kb0) - 4 * hl;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int keyoff = 8 * (r >> 2) + 4 * hl + (r & 3);
-            const bool vis = CAND ? (kb0 + keyoff < t.nk) : (dbase - (8 * (r >> 2) + (r & 3)) >= 0);
-            p[r] = vis ? p[r] : 0.f;
-          }
-        }
-        bf16x8 pa[2];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) pa[r >> 3][r & 7] = (bf16)p[r];
-        // O += P V; the k-slot (hl, i) of step s2 is key 16*s2 + 8*(i/4) + 4*hl + i%4
-        const int g = lane >> 4, rho = lane & 15;
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          const int krow = 32 * kb + 16 * s2 + 4 * hl + (rho >> 2);
-#pragma unroll
-          for (int c = 0; c < NC; ++c) {
-            const int col = c * 32 + 16 * (g & 1) + 4 * (rho & 3);
-            const bf16x4 v1 = tr_read(&Vt[tile_off<D>(krow, col)]);
-            const bf16x4 v2 = tr_read(&Vt[tile_off<D>(krow + 8, col)]);
-            bf16x8 bv;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) { bv[i] = v1[i]; bv[4 + i] = v2[i]; }
-            o[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[s2], bv, o[c], 0, 0, 0);
-          }
+          bf16x8 pa[2];
+          activate(x, kb, need_mask[kb], pa);
+          pv(kb, pa);
         }
       }
     }
@@ -390,7 +502,8 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
     if (kt + 1 < nkt) tile_step(B1{}, kt + 1);
   }
 
-  if (CAND) {
+  const bool add_self = CAND && blockIdx.z == 0;
+  if (add_self) {
     // the candidate's own key and value: relative position 0, elapsed time 0
     const bf16* kc = (const bf16*)a.kc;
     float part = 0.f;
@@ -418,12 +531,13 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
     const int rw = 8 * (r >> 2) + 4 * hl + (r & 3);  // row within the wavefront
     const int rowl = 32 * w + rw;
     if (rowl >= t.rows) continue;
-    const int64_t orow = (t.q_local + rowl) * a.ld_o + (int64_t)h * D;
+    const int64_t orow = (CAND ? (int64_t)blockIdx.z * a.part_stride : 0) +
+                         (t.q_local + rowl) * a.ld_o + (int64_t)h * D;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const int col = c * 32 + l32;
       float val = o[c][r];
-      if (CAND)
+      if (add_self)
         val = fmaf(pself[w][rw], (float)vc[(t.q_local + rowl) * a.ld_vc + (int64_t)h * D + col], val);
       val *= a.inv_n;
       if (a.out_f32)
@@ -439,7 +553,8 @@ hipError_t launch_attn_mfma(const AttnArgs& a, bool cand, hipStream_t s) {
   if (!cand)
     grid = dim3((unsigned)a.n_items * (unsigned)a.H);
   else
-    grid = dim3((unsigned)((a.max_user_rows + MBM - 1) / MBM) * (unsigned)a.H, (unsigned)a.n_users);
+    grid = dim3((unsigned)((a.max_user_rows + MBM - 1) / MBM) * (unsigned)a.H, (unsigned)a.n_users,
+                (unsigned)(a.kv_splits > 1 ? a.kv_splits : 1));
   if (grid.x == 0 || grid.y == 0) return hipSuccess;
 #define HSTU_MFMA_CASE(DD)                                                                  \
   if (a.d_qk == DD) {                                                                       \

@@ -34,6 +34,12 @@ struct AttnArgs {
   int64_t row_begin, row_end;
   int user_begin, n_users;
   int64_t max_user_rows;      // most candidate rows any one user has in this microbatch
+  // candidate mode only: the history is split into kv_splits key ranges of
+  // keys_per_split (a multiple of 64); split s writes its partial output (already
+  // scaled by 1/N; split 0 also adds the self term) at out + s * part_stride
+  int kv_splits;
+  int64_t keys_per_split;
+  int64_t part_stride;
 };
 
 // Tile sizes (query rows per work item) of the two attention kernels.
@@ -43,16 +49,20 @@ constexpr int kSimpleRows = 64;
 // True when the MFMA kernel handles this shape (bf16, d_qk == d_v in {32,64,128}
 // and the bias tables fit its LDS).
 bool attn_mfma_supported(int dtype_bf16, int d_qk, int d_v, int P, int T);
+// True when the MFMA kernel can take these row strides (K and V strides equal).
+bool attn_mfma_strides_ok(const AttnArgs& a);
 
 hipError_t launch_plan_causal(const int64_t* offsets, int B, int tile_rows, int max_tiles,
                               int2* items, int n_items, hipStream_t s);
 hipError_t launch_attn_simple(const AttnArgs& a, int use_bf16, bool cand, hipStream_t s);
 hipError_t launch_attn_mfma(const AttnArgs& a, bool cand, hipStream_t s);
 
-// out[r, :] = (LN(o[r, :]) * gamma + beta) (.) u[r, :], width w, over `rows` rows.
-hipError_t launch_ln_gate(const float* o, int64_t ld_o, const void* u, int64_t ld_u,
-                          const float* gamma, const float* beta, float eps, void* out,
-                          int64_t ld_out, int64_t rows, int w, int use_bf16, hipStream_t s);
+// out[r, :] = (LN(o[r, :]) * gamma + beta) (.) u[r, :], width w, over `rows` rows, where
+// o[r, :] is the sum of nsplit partial rows o + s * split_stride (s = 0..nsplit-1, in order).
+hipError_t launch_ln_gate(const float* o, int64_t ld_o, int nsplit, int64_t split_stride,
+                          const void* u, int64_t ld_u, const float* gamma, const float* beta,
+                          float eps, void* out, int64_t ld_out, int64_t rows, int w, int use_bf16,
+                          hipStream_t s);
 
 // C[M,N] = epi(A[M,K] W[N,K]^T + bias[N]); epi = SiLU when silu, + R[M,N] when R.
 hipError_t launch_gemm(const void* A, int64_t lda, const void* W, int64_t ldw,

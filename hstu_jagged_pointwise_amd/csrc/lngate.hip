@@ -8,6 +8,8 @@
 // is at most 64 * 16 values wide it stays in registers, so it is read once;
 // otherwise three passes reread it (from L2). The statistics use two passes
 // over the values (mean, then squared deviations), not E[x^2] - E[x]^2.
+// The row may arrive as nsplit partial rows (attention split over key ranges),
+// which are summed here in split order, so the result never depends on timing.
 #include "common.h"
 #include "kernels.h"
 
@@ -15,6 +17,7 @@ namespace hstu {
 
 template <typename T, int NPL>
 __global__ __launch_bounds__(256) void ln_gate_reg_kernel(const float* __restrict__ o, int64_t ld_o,
+                                                          int nsplit, int64_t split_stride,
                                                           const T* __restrict__ u, int64_t ld_u,
                                                           const float* __restrict__ gamma,
                                                           const float* __restrict__ beta, float eps,
@@ -29,7 +32,10 @@ __global__ __launch_bounds__(256) void ln_gate_reg_kernel(const float* __restric
 #pragma unroll
   for (int i = 0; i < NPL; ++i) {
     const int c = lane + 64 * i;
-    x[i] = c < w ? orow[c] : 0.f;
+    float xv = 0.f;
+    if (c < w)
+      for (int sp = 0; sp < nsplit; ++sp) xv += orow[sp * split_stride + c];
+    x[i] = xv;
     sum += x[i];
   }
   const float mean = wave_sum(sum) / (float)w;
@@ -57,6 +63,7 @@ __global__ __launch_bounds__(256) void ln_gate_reg_kernel(const float* __restric
 
 template <typename T>
 __global__ __launch_bounds__(256) void ln_gate_loop_kernel(const float* __restrict__ o, int64_t ld_o,
+                                                           int nsplit, int64_t split_stride,
                                                            const T* __restrict__ u, int64_t ld_u,
                                                            const float* __restrict__ gamma,
                                                            const float* __restrict__ beta, float eps,
@@ -66,19 +73,24 @@ __global__ __launch_bounds__(256) void ln_gate_loop_kernel(const float* __restri
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
   const float* orow = o + row * ld_o;
+  auto val = [&](int c) {
+    float xv = 0.f;
+    for (int sp = 0; sp < nsplit; ++sp) xv += orow[sp * split_stride + c];
+    return xv;
+  };
   float sum = 0.f;
-  for (int c = lane; c < w; c += 64) sum += orow[c];
+  for (int c = lane; c < w; c += 64) sum += val(c);
   const float mean = wave_sum(sum) / (float)w;
   float sq = 0.f;
   for (int c = lane; c < w; c += 64) {
-    const float d = orow[c] - mean;
+    const float d = val(c) - mean;
     sq = fmaf(d, d, sq);
   }
   const float rstd = rsqrtf(wave_sum(sq) / (float)w + eps);
   const T* urow = u + row * ld_u;
   T* dst = out + row * ld_out;
   for (int c = lane; c < w; c += 64) {
-    float y = (orow[c] - mean) * rstd;
+    float y = (val(c) - mean) * rstd;
     if (gamma) y *= gamma[c];
     if (beta) y += beta[c];
     dst[c] = from_f32<T>(y * to_f32<T>(urow[c]));
@@ -86,7 +98,8 @@ __global__ __launch_bounds__(256) void ln_gate_loop_kernel(const float* __restri
 }
 
 template <typename T>
-static hipError_t ln_dispatch(const float* o, int64_t ld_o, const void* u, int64_t ld_u,
+static hipError_t ln_dispatch(const float* o, int64_t ld_o, int nsplit, int64_t split_stride,
+                              const void* u, int64_t ld_u,
                               const float* gamma, const float* beta, float eps, void* out,
                               int64_t ld_out, int64_t rows, int w, hipStream_t s) {
   const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
@@ -95,23 +108,27 @@ static hipError_t ln_dispatch(const float* o, int64_t ld_o, const void* u, int64
   const int npl = (w + 63) / 64;
 #define HSTU_LN_CASE(N)                                                                          \
   if (npl <= N) {                                                                                \
-    hipLaunchKernelGGL((ln_gate_reg_kernel<T, N>), grid, block, 0, s, o, ld_o, uu, ld_u, gamma,  \
-                       beta, eps, oo, ld_out, rows, w);                                          \
+    hipLaunchKernelGGL((ln_gate_reg_kernel<T, N>), grid, block, 0, s, o, ld_o, nsplit,           \
+                       split_stride, uu, ld_u, gamma, beta, eps, oo, ld_out, rows, w);           \
     return hipGetLastError();                                                                    \
   }
   HSTU_LN_CASE(1) HSTU_LN_CASE(2) HSTU_LN_CASE(4) HSTU_LN_CASE(8) HSTU_LN_CASE(16)
 #undef HSTU_LN_CASE
-  hipLaunchKernelGGL((ln_gate_loop_kernel<T>), grid, block, 0, s, o, ld_o, uu, ld_u, gamma, beta,
-                     eps, oo, ld_out, rows, w);
+  hipLaunchKernelGGL((ln_gate_loop_kernel<T>), grid, block, 0, s, o, ld_o, nsplit, split_stride, uu,
+                     ld_u, gamma, beta, eps, oo, ld_out, rows, w);
   return hipGetLastError();
 }
 
-hipError_t launch_ln_gate(const float* o, int64_t ld_o, const void* u, int64_t ld_u,
-                          const float* gamma, const float* beta, float eps, void* out,
-                          int64_t ld_out, int64_t rows, int w, int bf16flag, hipStream_t s) {
+hipError_t launch_ln_gate(const float* o, int64_t ld_o, int nsplit, int64_t split_stride,
+                          const void* u, int64_t ld_u, const float* gamma, const float* beta,
+                          float eps, void* out, int64_t ld_out, int64_t rows, int w, int bf16flag,
+                          hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  return bf16flag ? ln_dispatch<bf16>(o, ld_o, u, ld_u, gamma, beta, eps, out, ld_out, rows, w, s)
-                  : ln_dispatch<float>(o, ld_o, u, ld_u, gamma, beta, eps, out, ld_out, rows, w, s);
+  nsplit = nsplit < 1 ? 1 : nsplit;
+  return bf16flag ? ln_dispatch<bf16>(o, ld_o, nsplit, split_stride, u, ld_u, gamma, beta, eps, out,
+                                      ld_out, rows, w, s)
+                  : ln_dispatch<float>(o, ld_o, nsplit, split_stride, u, ld_u, gamma, beta, eps,
+                                       out, ld_out, rows, w, s);
 }
 
 }  // namespace hstu

@@ -129,3 +129,25 @@ def test_mfalcon_workload_sampled_candidates():
     lgn = lg.cpu().numpy()[rows].astype(np.float64)
     scale = np.linalg.norm(want, axis=1) * np.linalg.norm(x.w_head)
     assert np.all(np.abs(lgn - want @ x.w_head.astype(np.float64)) <= 2e-2 * scale)
+
+
+@pytest.mark.parametrize("L", [1, 2])
+def test_split_history_multi_user(L):
+    """Histories longer than one key range (512 keys) are split across workgroups and the
+    partials summed in a fixed order: parity against the oracle, and outputs bit-for-bit
+    independent of the microbatch size and of the candidate order."""
+    x = _small("bf16", L, seed=11, hist=(1300, 0, 700, 2000), cands=(37, 5, 20, 64), mb=50)
+    announce(f"mfalcon split history L={L}")
+    out, lg = mf_on_gpu(x)
+    want, _ = mf_oracle(x)
+    want_s = mf_oracle(x, "bf16")[0]
+    check_rows(to_np(out), x, want, want_s, f"mfalcon split L={L}")
+    _check_logits(lg, want_s, x, TOL["bf16"])
+    base = out.float().cpu().numpy()
+    for mb in (1, 17, 126, 4096):
+        o, _ = mf_on_gpu(x, microbatch=mb)
+        assert np.array_equal(o.float().cpu().numpy(), base), f"microbatch {mb}"
+    perm = np.concatenate([np.arange(0, 37)[::-1], np.arange(37, 42), np.arange(42, 62)[::-1],
+                           np.random.default_rng(1).permutation(np.arange(62, 126))])
+    o, _ = mf_on_gpu(x, cand_x=x.cand_x[perm], cand_ts=x.cand_ts[perm])
+    assert np.array_equal(o.float().cpu().numpy(), base[perm])
