@@ -28,16 +28,19 @@ __global__ __launch_bounds__(256) void ln_gate_reg_kernel(const float* __restric
   if (row >= rows) return;
   const float* orow = o + row * ld_o;
   float x[NPL];
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) x[i] = 0.f;
+  for (int sp = 0; sp < nsplit; ++sp) {  // all NPL loads of one split are independent
+    const float* op = orow + sp * split_stride;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      const int c = lane + 64 * i;
+      if (c < w) x[i] += op[c];
+    }
+  }
   float sum = 0.f;
 #pragma unroll
-  for (int i = 0; i < NPL; ++i) {
-    const int c = lane + 64 * i;
-    float xv = 0.f;
-    if (c < w)
-      for (int sp = 0; sp < nsplit; ++sp) xv += orow[sp * split_stride + c];
-    x[i] = xv;
-    sum += x[i];
-  }
+  for (int i = 0; i < NPL; ++i) sum += x[i];
   const float mean = wave_sum(sum) / (float)w;
   float sq = 0.f;
 #pragma unroll
