@@ -30,13 +30,22 @@ __global__ __launch_bounds__(256) void ln_gate_reg_kernel(const float* __restric
   float x[NPL];
 #pragma unroll
   for (int i = 0; i < NPL; ++i) x[i] = 0.f;
-  for (int sp = 0; sp < nsplit; ++sp) {  // all NPL loads of one split are independent
-    const float* op = orow + sp * split_stride;
+  // all loads of up to four splits are issued before any of them is summed
+  for (int sp0 = 0; sp0 < nsplit; sp0 += 4) {
+    float part[4][NPL];
 #pragma unroll
-    for (int i = 0; i < NPL; ++i) {
-      const int c = lane + 64 * i;
-      if (c < w) x[i] += op[c];
+    for (int q = 0; q < 4; ++q) {
+      const float* op = orow + (int64_t)(sp0 + q) * split_stride;
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) {
+        const int c = lane + 64 * i;
+        part[q][i] = (sp0 + q < nsplit && c < w) ? op[c] : 0.f;
+      }
     }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) x[i] += part[q][i];
   }
   float sum = 0.f;
 #pragma unroll
