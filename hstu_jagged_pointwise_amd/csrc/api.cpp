@@ -52,8 +52,8 @@ size_t elt_size(hstu_dtype t) { return t == HSTU_BF16 ? 2 : 4; }
 struct Carver {
   char* base;
   size_t off = 0;
-  void* take(size_t bytes) {
-    void* p = base ? base + off : nullptr;
+  void* take(size_t bytes) {  // NULL for an empty buffer
+    void* p = (base && bytes) ? base + off : nullptr;
     off += align_up(bytes);
     return p;
   }
@@ -113,20 +113,26 @@ hstu_status check_eps(float eps) {
   return HSTU_OK;
 }
 
-int attn_tile_rows(const hstu_attn_desc* d) {
+bool uses_mfma(const hstu_attn_desc* d);
+int attn_tile_rows(const hstu_attn_desc* d) { return uses_mfma(d) ? kMfmaRows : kSimpleRows; }
+
+bool uses_mfma(const hstu_attn_desc* d) {
   return attn_mfma_supported(d->dtype == HSTU_BF16, d->d_qk, d->d_v, d->num_pos_buckets,
-                             d->num_time_buckets)
-             ? kMfmaRows
-             : kSimpleRows;
+                             d->num_time_buckets);
+}
+
+// Workspace bytes of the per-32-key timestamp ranges (MFMA kernel only).
+size_t key_range_bytes(const hstu_attn_desc* d, int64_t total_keys) {
+  return uses_mfma(d) ? (size_t)key_range_slots(total_keys, d->batch) * sizeof(KeyRange) : 0;
 }
 
 hipError_t run_attention(const hstu_attn_desc* d, const AttnArgs& a, bool cand, hipStream_t s) {
-  const bool mfma = attn_mfma_supported(d->dtype == HSTU_BF16, d->d_qk, d->d_v,
-                                        d->num_pos_buckets, d->num_time_buckets);
-  if (!mfma) return launch_attn_simple(a, d->dtype == HSTU_BF16, cand, s);
+  if (!uses_mfma(d)) return launch_attn_simple(a, d->dtype == HSTU_BF16, cand, s);
   // work items were planned for the MFMA kernel's tile; every caller here passes
-  // equal K and V strides (d_qk == d_v), which that kernel's key-tile DMA needs
+  // equal K and V strides (d_qk == d_v), which that kernel's key-tile DMA needs,
+  // and the key ranges whenever the time bias is on
   if (!attn_mfma_strides_ok(a)) return hipErrorInvalidValue;
+  if (a.rab_time && a.ts_q && a.ts_k && !a.key_ranges) return hipErrorInvalidValue;
   return launch_attn_mfma(a, cand, s);
 }
 
@@ -157,6 +163,7 @@ hstu_status plan_attn(const hstu_attn_desc* d, const int64_t* off_host, bool gat
     return fail(HSTU_UNSUPPORTED, "too many query tiles for one launch");
   Carver c{nullptr};
   c.take((size_t)p->j.items * sizeof(int2));
+  c.take(key_range_bytes(d, p->j.total));
   if (gated) c.take((size_t)p->j.total * d->num_heads * d->d_v * sizeof(float));
   p->ws = c.off;
   return HSTU_OK;
@@ -196,6 +203,7 @@ hstu_status check_weights(const hstu_layer_weights* w, int L) {
 
 struct LayerBufs {
   int2* items;
+  KeyRange* kr;  // per 32-key timestamp ranges (MFMA kernel), else NULL
   void* uvqk;
   float* o;
   void* g;
@@ -208,6 +216,7 @@ void carve_layer(Carver& c, const hstu_layer_desc* d, int64_t rows, int64_t item
   const int64_t f1 = 2LL * a.num_heads * (a.d_v + a.d_qk);
   const int64_t hv = (int64_t)a.num_heads * a.d_v;
   b->items = (int2*)c.take((size_t)items * sizeof(int2));
+  b->kr = (KeyRange*)c.take(key_range_bytes(&a, rows));
   b->uvqk = c.take((size_t)rows * f1 * es);
   b->o = (float*)c.take((size_t)rows * hv * sizeof(float));
   b->g = c.take((size_t)rows * hv * es);
@@ -245,10 +254,23 @@ UVQK split_view(const void* base, const hstu_attn_desc& a) {
   return UVQK{p, p + hv * es, p + 2 * hv * es, p + (2 * hv + hq) * es, 2 * hv + 2 * hq};
 }
 
+// Work items and key ranges of the causal attention; they depend on the offsets
+// and timestamps only, so one call serves every layer.
+hstu_status plan_causal(const hstu_attn_desc& a, const int64_t* off_dev, const int64_t* ts,
+                        const Jagged& j, const LayerBufs& b, hipStream_t s) {
+  HSTU_TRY(launch_plan_causal(off_dev, a.batch, attn_tile_rows(&a), j.max_tiles, b.items,
+                              (int)j.items, s),
+           "tile planner");
+  if (ts && b.kr)
+    HSTU_TRY(launch_key_ranges(off_dev, ts, a.batch, j.max_len, b.kr, s), "key ranges");
+  return HSTU_OK;
+}
+
 // One layer over `rows` jagged rows: f1 -> causal attention -> LN gate -> f2.
+// The work items and key ranges in b come from plan_causal.
 hstu_status layer_once(const hstu_layer_desc* d, const int64_t* off_dev, const int64_t* ts,
                        const Jagged& j, const void* x, const hstu_layer_weights& w, void* y,
-                       const LayerBufs& b, bool items_ready, hipStream_t s, bool f1_only) {
+                       const LayerBufs& b, hipStream_t s, bool f1_only) {
   const hstu_attn_desc& a = d->attn;
   const int bf = a.dtype == HSTU_BF16;
   const int64_t rows = j.total;
@@ -258,10 +280,6 @@ hstu_status layer_once(const hstu_layer_desc* d, const int64_t* off_dev, const i
                        d->d_model, 1, bf, s),
            "f1 projection");
   if (f1_only) return HSTU_OK;
-  if (!items_ready)
-    HSTU_TRY(launch_plan_causal(off_dev, a.batch, attn_tile_rows(&a), j.max_tiles, b.items,
-                                (int)j.items, s),
-             "tile planner");
   const UVQK vw = split_view(b.uvqk, a);
   AttnArgs aa = base_args(&a);
   aa.q = vw.q;
@@ -275,6 +293,7 @@ hstu_status layer_once(const hstu_layer_desc* d, const int64_t* off_dev, const i
   aa.ts_q = aa.ts_k = ts;
   aa.rab_pos = w.rab_pos;
   aa.rab_time = w.rab_time;
+  aa.key_ranges = (ts && w.rab_time) ? b.kr : nullptr;
   aa.items = b.items;
   aa.n_items = (int)j.items;
   HSTU_TRY(run_attention(&a, aa, false, s), "attention");
@@ -318,6 +337,7 @@ void carve_mfalcon(Carver& c, const mfalcon_desc* d, const MfPlan& p, MfBufs* b)
   const int64_t nh = p.hist.total;
   const int64_t m = std::min<int64_t>(d->microbatch, std::max<int64_t>(p.cand_total, 1));
   b->hist.items = (int2*)c.take((size_t)p.hist.items * sizeof(int2));
+  b->hist.kr = (KeyRange*)c.take(key_range_bytes(&a, nh));
   b->hist.o = (float*)c.take((size_t)nh * hv * sizeof(float));
   b->hist.g = c.take((size_t)nh * hv * es);
   b->hist_uvqk.assign(ld.num_layers, nullptr);
@@ -422,10 +442,15 @@ hstu_status hstu_attn_fwd(const hstu_attn_desc* desc, const int64_t* seq_offsets
   hipStream_t s = (hipStream_t)stream;
   Carver c{(char*)workspace};
   int2* items = (int2*)c.take((size_t)p.j.items * sizeof(int2));
+  KeyRange* kr = (KeyRange*)c.take(key_range_bytes(desc, p.j.total));
   float* o32 = u ? (float*)c.take((size_t)p.j.total * desc->num_heads * desc->d_v * 4) : nullptr;
   HSTU_TRY(launch_plan_causal(seq_offsets, desc->batch, attn_tile_rows(desc), p.j.max_tiles, items,
                               (int)p.j.items, s),
            "tile planner");
+  const bool timed = rab_time && timestamps && kr;
+  if (timed)
+    HSTU_TRY(launch_key_ranges(seq_offsets, timestamps, desc->batch, p.j.max_len, kr, s),
+             "key ranges");
   AttnArgs a = base_args(desc);
   a.q = q;
   a.k = k;
@@ -439,6 +464,7 @@ hstu_status hstu_attn_fwd(const hstu_attn_desc* desc, const int64_t* seq_offsets
   a.ts_q = a.ts_k = timestamps;
   a.rab_pos = rab_pos;
   a.rab_time = rab_time;
+  a.key_ranges = timed ? kr : nullptr;
   a.items = items;
   a.n_items = (int)p.j.items;
   HSTU_TRY(run_attention(desc, a, false, s), "attention");
@@ -484,11 +510,12 @@ hstu_status hstu_layer_fwd(const hstu_layer_desc* desc, const int64_t* seq_offse
   LayerBufs b;
   carve_layer(c, desc, p.j.total, p.j.items, &b);
   const int L = desc->num_layers;
+  if ((st = plan_causal(desc->attn, seq_offsets, timestamps, p.j, b, s))) return st;
   const void* in = x;
   for (int l = 0; l < L; ++l) {
     // layer outputs alternate between y and tmp so that the last one lands in y
     void* out = ((L - 1 - l) % 2 == 0) ? y : b.tmp;
-    st = layer_once(desc, seq_offsets, timestamps, p.j, in, weights[l], out, b, l > 0, s, false);
+    st = layer_once(desc, seq_offsets, timestamps, p.j, in, weights[l], out, b, s, false);
     if (st) return st;
     in = out;
   }
@@ -546,11 +573,14 @@ hstu_status mfalcon_score(const mfalcon_desc* desc, const int64_t* hist_offsets_
   // history pass, once: layers 0..L-2 in full; layer L-1 only needs its K and V
   if (p.hist.total > 0) {
     LayerBufs hb = b.hist;
+    // the history's work items (layers 0..L-2) and key ranges (every layer,
+    // candidates included)
+    if ((st = plan_causal(a, hist_offsets, hist_ts, p.hist, hb, s))) return st;
     const void* in = hist_x;
     for (int l = 0; l < L; ++l) {
       hb.uvqk = b.hist_uvqk[l];
       void* out = (l < L - 1) ? b.hx[l % 2] : nullptr;
-      st = layer_once(&ld, hist_offsets, hist_ts, p.hist, in, weights[l], out, hb, l > 0, s,
+      st = layer_once(&ld, hist_offsets, hist_ts, p.hist, in, weights[l], out, hb, s,
                       l == L - 1);
       if (st) return st;
       in = out;
@@ -603,6 +633,7 @@ hstu_status mfalcon_score(const mfalcon_desc* desc, const int64_t* hist_offsets_
       aa.ts_k = hist_ts;
       aa.rab_pos = w.rab_pos;
       aa.rab_time = w.rab_time;
+      aa.key_ranges = (hist_ts && w.rab_time) ? b.hist.kr : nullptr;  // unread when no history
       aa.row_begin = m0;
       aa.row_end = m1;
       aa.max_user_rows = max_rows;

@@ -7,6 +7,7 @@ namespace hstu {
 
 struct TileDecode {
   int h;
+  int seq;          // sequence (causal) or user (candidate mode)
   int64_t q_base;   // global row of tile row 0 (candidate mode: global candidate row)
   int64_t q_local;  // row index into q/out/kc/vc of tile row 0
   int rows;         // valid query rows in the tile
@@ -26,10 +27,13 @@ __device__ __forceinline__ TileDecode decode(const AttnArgs& a, int bm) {
     const int item = blockIdx.x / a.H;
     d.h = blockIdx.x % a.H;
     if (item >= a.n_items) return d;
-    const int2 it = a.items[item];
+    // the (sequence, tile) pair as one 64-bit scalar load
+    const uint64_t raw = sload(reinterpret_cast<const uint64_t*>(a.items + item));
+    const int2 it = make_int2((int)(uint32_t)raw, (int)(uint32_t)(raw >> 32));
     if (it.x < 0 || it.x >= a.batch || it.y < 0) return d;
-    const int64_t s0 = a.q_offsets[it.x];
-    const int64_t n = a.q_offsets[it.x + 1] - s0;
+    d.seq = it.x;
+    const int64_t s0 = sload(a.q_offsets + it.x);
+    const int64_t n = sload(a.q_offsets + it.x + 1) - s0;
     const int64_t r0 = (int64_t)it.y * bm;
     if (r0 >= n) return d;
     d.rows = (int)(n - r0 < bm ? n - r0 : bm);
@@ -44,7 +48,8 @@ __device__ __forceinline__ TileDecode decode(const AttnArgs& a, int bm) {
     d.h = blockIdx.x % a.H;
     const int tile = blockIdx.x / a.H;
     const int b = a.user_begin + blockIdx.y;
-    int64_t cs = a.q_offsets[b], ce = a.q_offsets[b + 1];
+    d.seq = b;
+    int64_t cs = sload(a.q_offsets + b), ce = sload(a.q_offsets + b + 1);
     cs = cs > a.row_begin ? cs : a.row_begin;
     ce = ce < a.row_end ? ce : a.row_end;
     const int64_t r0 = cs + (int64_t)tile * bm;
@@ -52,8 +57,8 @@ __device__ __forceinline__ TileDecode decode(const AttnArgs& a, int bm) {
     d.rows = (int)(ce - r0 < bm ? ce - r0 : bm);
     d.q_base = r0;
     d.q_local = r0 - a.row_begin;
-    d.k_base = a.k_offsets[b];
-    d.nk = a.k_offsets[b + 1] - d.k_base;
+    d.k_base = sload(a.k_offsets + b);
+    d.nk = sload(a.k_offsets + b + 1) - d.k_base;
     d.kbeg = 0;
     d.kend = d.nk;
     d.qpos0 = d.nk;

@@ -24,16 +24,20 @@
 // works on block 1 while the vector ALU activates block 0.
 //
 // Bias classes, decided per (wavefront, 32-key block) from exact integer
-// ranges:
+// ranges, one tile ahead of their use and in scalar registers:
 //   * The position bucket min(i-j, P-1) is one constant when every i-j >= P-1.
-//   * The time bucket is one constant when its value agrees at both ends of the
-//     block's elapsed-time range [min t_i - max t_j, max t_i - min t_j]. The
-//     bucket is monotone in the elapsed time, so agreement at both ends means
-//     it holds everywhere.
-//   * A constant bias becomes the accumulator's initial value, at no cost per
-//     element. Otherwise each element gathers from LDS-resident tables. The
-//     time bucket is then the count of leading zeros of the 32-bit elapsed time
-//     + 1 (a 64-bit path covers spans past 2^31 s).
+//   * The time bucket is monotone in the elapsed time, so over the block's
+//     elapsed-time range [min t_i - max t_j, max t_i - min t_j] (the key side
+//     comes precomputed per 32-key block, see KeyRange) its values run from the
+//     bucket of the lower end to the bucket of the upper end:
+//       - one bucket: a constant;
+//       - two adjacent buckets b, b+1: an element is in b+1 exactly when
+//         t_i + 1 - t_j >= 2^(b+1), one 32-bit compare and select per element;
+//       - more: the bucket of each element from the count of leading zeros of
+//         the 32-bit t_i + 1 - t_j (a 64-bit path covers spans past 2^31 s).
+//   * A constant bias enters through one extra MFMA k-step (below), at no cost
+//     per element. A block whose position bucket varies gathers it per element
+//     from an LDS-resident table.
 // Masking is a select after SiLU (SiLU(-inf) would be NaN). It runs only on
 // blocks that cross the causal diagonal (or the history tail for candidates).
 // Blocks entirely above the diagonal are skipped.
@@ -78,15 +82,31 @@ __device__ __forceinline__ int tile_off(int row, int col) {
 }
 template <int D>
 constexpr int tile_elems() {
-  return MBN * (D + 8) + 64 * 8;  // + slack for the last DMA span
+  return MBN * (D + 8);
 }
 
-// exact time bucket of a non-negative elapsed time, clamped to the table
+// exact time bucket of an elapsed time (negative counts as 0), clamped to the table
 __device__ __forceinline__ int bucket_of(int64_t dt, int T) {
   dt = dt < 0 ? 0 : dt;
   const int b = 63 - __builtin_clzll((uint64_t)dt + 1ull);
   return b < T - 1 ? b : T - 1;
 }
+
+// Bias class of one (wavefront, 32-key block) pair. Every field is uniform
+// across the wavefront.
+struct BlockClass {
+  bool act;        // some key of the block is visible to some row of the wavefront
+  bool mask;       // the block needs the per-element visibility mask
+  bool pos_c;      // one position bucket over the block (or no position bias)
+  int tmode;       // time bias: 0 one bucket (or none), 1 two adjacent buckets, 2 general
+  bool tfast;      // every elapsed time fits the 32-bit forms
+  bool tsorted;    // no elapsed time in the block is negative
+  int thr;         // tmode 1: upper bucket when the 32-bit t_i + 1 - t_j >= thr
+  float tlo, thi;  // time-table values of the lowest and highest bucket (0 without time bias)
+};
+struct TileClass {
+  BlockClass b[2];
+};
 }  // namespace
 
 bool attn_mfma_supported(int dtype_bf16, int d_qk, int d_v, int P, int T) {
@@ -95,15 +115,15 @@ bool attn_mfma_supported(int dtype_bf16, int d_qk, int d_v, int P, int T) {
 }
 
 bool attn_mfma_strides_ok(const AttnArgs& a) {
-  // the key-tile DMA shares one per-lane offset between K and V; offsets are 32-bit
-  return a.ld_k == a.ld_v && a.ld_k > 0 && (int64_t)(MBN + 1) * a.ld_k < (int64_t(1) << 31);
+  // the key-tile DMA shares one per-lane byte offset between K and V; offsets are 32-bit
+  return a.ld_k == a.ld_v && a.ld_k > 0 && (int64_t)(MBN + 1) * a.ld_k * 2 < (int64_t(1) << 32);
 }
 
 template <int D, bool CAND>
 __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
-  constexpr int NKK = D / 16;       // k-steps of the S^T contraction
-  constexpr int NC = D / 32;        // 32-wide output column blocks
-  constexpr int CPR = D / 8;        // 16-byte chunks per row
+  constexpr int NKK = D / 16;  // k-steps of the S^T contraction
+  constexpr int NC = D / 32;   // 32-wide output column blocks
+  constexpr int CPR = D / 8;   // 16-byte chunks per row
   constexpr int TE = tile_elems<D>();
   // two LDS buffers per matrix as separate objects, so that alias analysis can tell
   // the in-flight DMA target from the buffer being read (no conservative waits)
@@ -113,7 +133,6 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 Vs1[TE];
   __shared__ __attribute__((aligned(16))) uint32_t tk_lo[2][MBN];
   __shared__ int64_t tk64[2][MBN];
-  __shared__ int64_t kstat[2][2][2];  // [buffer][32-key block][min, max]
   __shared__ float rp[kMaxP];
   __shared__ float rt[kTimeTab];
   __shared__ float rtc[32];
@@ -123,13 +142,13 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
   if (!t.valid) return;  // uniform across the workgroup
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
+  const int wu = uniform(w);
   const int l32 = lane & 31, hl = lane >> 5;
   const int h = t.h;
   const bf16* q = (const bf16*)a.q;
-  const bf16* k = (const bf16*)a.k;
-  const bf16* v = (const bf16*)a.v;
   const bool has_pos = a.rab_pos != nullptr;
-  const bool has_time = a.rab_time != nullptr && a.ts_q != nullptr && a.ts_k != nullptr;
+  const bool has_time = a.rab_time != nullptr && a.ts_q != nullptr && a.ts_k != nullptr &&
+                        a.key_ranges != nullptr;
   const int P = a.P, T = a.T;
 
   if (has_pos)
@@ -141,11 +160,13 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
       rtc[tid] = a.rab_time[(int64_t)h * T + (bt < T - 1 ? bt : T - 1)];
     }
   }
+  const float pb = has_pos ? sload(a.rab_pos + (int64_t)h * P + P - 1) : 0.f;  // bucket P-1
+  const float* rtg = a.rab_time + (int64_t)h * T;
 
   // this lane's query row (the S^T column it holds) and its Q fragment
   const int wrow = 32 * w + l32;
   const bool row_ok = wrow < t.rows;
-  const bool wave_live = 32 * w < t.rows;
+  const bool wave_live = 32 * wu < t.rows;
   bf16x8 qf[NKK];
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) {
@@ -160,14 +181,19 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
   const uint32_t tq1 = (uint32_t)tq + 1u;
   const int64_t qmin = uniform64(wave_min64(row_ok ? tq : INT64_MAX));
   const int64_t qmax = uniform64(wave_max64(row_ok ? tq : INT64_MIN));
-  const int64_t qpos = CAND ? t.qpos0 : t.qpos0 + wrow;
-  const int64_t wrow0 = t.qpos0 + 32 * w;  // causal position of the wavefront's first row
-  const int64_t wlast = t.qpos0 + (int64_t)min(32 * w + 31, t.rows - 1);  // its last live row
+  // positions inside one sequence fit in 32 bits (lengths are bounded by an int N)
+  const int nk = (int)t.nk, kend = (int)t.kend, kbeg = (int)t.kbeg, qpos0 = (int)t.qpos0;
+  const int qpos = CAND ? qpos0 : qpos0 + wrow;
+  const int wrow0 = qpos0 + 32 * wu;                        // the wavefront's first row
+  const int wlast = qpos0 + min(32 * wu + 31, t.rows - 1);  // its last live row
 
-  // constant A fragment for the bias k-step: A[key][0] = A[key][1] = 1
-  bf16x8 ones;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) ones[i] = (bf16)((hl == 0 && i < 2) ? 1.f : 0.f);
+  // constant A fragment for the bias k-step, A[key][0] = A[key][1] = 1, rebuilt at
+  // each use (one select and three zero moves) rather than held in registers
+  const uint32_t ones_w = hl == 0 ? 0x3f803f80u : 0u;  // two bf16 ones in one word
+  auto ones = [&]() {
+    u32x4 f = {ones_w, 0u, 0u, 0u};
+    return __builtin_bit_cast(bf16x8, f);
+  };
 
   f32x16 o[NC];
 #pragma unroll
@@ -179,325 +205,364 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
   // instruction fills 16-byte slot L of a contiguous 1 KiB span, so the padded
   // layout comes from which source chunk each lane fetches. Rows past the data
   // repeat the last valid row: their scores are masked and multiply finite values.
-  constexpr int SPR = CPR + 1;                         // 16-byte slots per LDS row
-  constexpr int NSLOT = MBN * SPR;                     // slots per matrix tile
-  constexpr int NINSTR = (NSLOT + 63) / 64;            // wave-instructions per matrix tile
-  int64_t ptk = 0;
-  // Per-lane source offsets (elements from the tile's first row) of this wavefront's
-  // DMA instructions, computed once. K and V share the row stride. A full tile
-  // then needs only the uniform base pointer advanced; the tail tile clamps rows
-  // past the data to the last valid row.
+  constexpr int SPR = CPR + 1;        // 16-byte slots per LDS row
+  constexpr int NSLOT = MBN * SPR;    // slots per matrix tile
+  constexpr int NINSTR = NSLOT / 64;  // wave-instructions per matrix tile
   constexpr int NIW = (NINSTR + 3) / 4;
-  uint32_t soff[NIW];
+  static_assert(NSLOT % 64 == 0, "every DMA instruction fills 64 slots");
+  // Wavefront w issues instructions w, w+4, w+8, ... of each matrix tile. The
+  // (key row, byte column) source of each of its slots is packed into one word,
+  // computed once; K and V share the row stride. The address is a uniform base
+  // plus a 32-bit offset (the scalar-base form of the instruction).
+  const uint32_t ldb = (uint32_t)(a.ld_k * 2);
+  uint32_t spk[NIW];
 #pragma unroll
   for (int j = 0; j < NIW; ++j) {
     const int slot = 64 * (w + 4 * j) + lane;
     const int row = slot / SPR, pc = slot % SPR;
-    soff[j] = (uint32_t)(row * a.ld_k + 8 * (pc < CPR ? pc : 0));
+    spk[j] = (uint32_t)row | ((uint32_t)(pc < CPR ? pc : 0) << 10);
   }
-  auto issue_tile = [&](auto bufc, int64_t k0) {
+  const char* kg = (const char*)a.k + (int64_t)h * D * 2;
+  const char* vg = (const char*)a.v + (int64_t)h * D * 2;
+  struct DmaSrc {
+    const char* kb;
+    const char* vb;
+    uint32_t lim;  // last key row of the data in the tile
+  };
+  auto dma_src = [&](int k0) {
+    return DmaSrc{kg + (t.k_base + k0) * a.ld_k * 2, vg + (t.k_base + k0) * a.ld_v * 2,
+                  (uint32_t)(nk - 1 - k0)};
+  };
+  // this wavefront's instruction pairs (K and V) for one tile
+  auto dma_tile = [&](auto bufc, const DmaSrc& src) {
     constexpr int buf = decltype(bufc)::value;
     bf16* Kd = buf ? Ks1 : Ks0;
     bf16* Vd = buf ? Vs1 : Vs0;
-    const int64_t last = t.nk - 1;
-    const bf16* kb = k + (t.k_base + k0) * a.ld_k + (int64_t)h * D;
-    const bf16* vb = v + (t.k_base + k0) * a.ld_v + (int64_t)h * D;
-    const bool full = k0 + MBN - 1 <= last;
 #pragma unroll
     for (int j = 0; j < NIW; ++j) {
-      const int i = w + 4 * j;
+      const int i = wu + 4 * j;
       if (i >= NINSTR) break;
-      const int slot = 64 * i + lane;
-      if (slot < NSLOT) {
-        uint32_t off = soff[j];
-        if (!full) {
-          const int row = slot / SPR, pc = slot % SPR;
-          const int64_t r = min(k0 + row, last) - k0;
-          off = (uint32_t)(r * a.ld_k + 8 * (pc < CPR ? pc : 0));
-        }
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kb + off),
-                                         (__attribute__((address_space(3))) void*)(&Kd[512 * i]),
-                                         16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vb + off),
-                                         (__attribute__((address_space(3))) void*)(&Vd[512 * i]),
-                                         16, 0, 0);
-      }
+      const uint32_t row = min(spk[j] & 1023u, src.lim);
+      const uint32_t off = row * ldb + 16u * (spk[j] >> 10);
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(src.kb + off),
+          (__attribute__((address_space(3))) void*)(&Kd[512 * i]), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(src.vb + off),
+          (__attribute__((address_space(3))) void*)(&Vd[512 * i]), 16, 0, 0);
     }
-    if (has_time && tid < MBN) ptk = (k0 + tid < t.nk) ? a.ts_k[t.k_base + k0 + tid] : 0;
   };
-  auto finish_tile = [&](auto bufc, int64_t k0) {
+  int64_t ptk = 0;
+  // each wavefront fetches the timestamps of 16 of the tile's keys
+  auto ts_fetch = [&](int k0) {
+    if (has_time && lane < 16) {
+      const int key = k0 + 16 * w + lane;
+      ptk = key < nk ? a.ts_k[t.k_base + key] : 0;
+    }
+  };
+  auto finish_tile = [&](auto bufc, bool store_ts) {
     constexpr int buf = decltype(bufc)::value;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    if (has_time && tid < MBN) {
-      const bool ok = k0 + tid < t.nk;
-      tk_lo[buf][tid] = (uint32_t)ptk;
-      tk64[buf][tid] = ptk;
-      // min and max over each half-wavefront (one 32-key block each)
-      int64_t mn = ok ? ptk : INT64_MAX, mx = ok ? ptk : INT64_MIN;
-#pragma unroll
-      for (int o2 = 16; o2 >= 1; o2 >>= 1) {
-        const int64_t a1 = __shfl_xor(mn, o2, 64), a2 = __shfl_xor(mx, o2, 64);
-        mn = a1 < mn ? a1 : mn;
-        mx = a2 > mx ? a2 : mx;
-      }
-      if ((tid & 31) == 0) {
-        kstat[buf][tid >> 5][0] = mn;
-        kstat[buf][tid >> 5][1] = mx;
-      }
+    if (store_ts && has_time && lane < 16) {
+      tk_lo[buf][16 * w + lane] = (uint32_t)ptk;
+      tk64[buf][16 * w + lane] = ptk;
     }
   };
 
-  const int64_t nkt = (t.kend - t.kbeg + MBN - 1) / MBN;
+  // ---- bias classes (scalar), from the key blocks' precomputed timestamp ranges
+  const KeyRange* krs = has_time ? a.key_ranges + key_range_slot(t.k_base, t.seq) : nullptr;
+  auto load_ranges = [&](int k0, KeyRange* r) {
+    if (has_time && wave_live) {
+      const KeyRange* p = krs + (k0 >> 5);  // p + 1 is a valid slot even past the last block
+      r[0].lo = sload(&p[0].lo);
+      r[0].hi = sload(&p[0].hi);
+      r[1].lo = sload(&p[1].lo);
+      r[1].hi = sload(&p[1].hi);
+    }
+  };
+  auto classify = [&](int k0, const KeyRange* r) {
+    TileClass c;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      BlockClass& bc = c.b[kb];
+      const int kb0 = k0 + 32 * kb;
+      bc.act = wave_live && kb0 < kend && (CAND || kb0 <= wlast);
+      bc.mask = CAND ? (kb0 + 32 > kend) : (kb0 + 31 > wrow0);
+      const int min_dpos = (CAND ? qpos0 : wrow0) - (kb0 + 31);
+      bc.pos_c = !has_pos || min_dpos >= P - 1;
+      bc.tmode = 0;
+      bc.tfast = true;
+      bc.tsorted = true;
+      bc.thr = 0;
+      bc.tlo = 0.f;
+      bc.thi = 0.f;
+      if (has_time && bc.act) {
+        const int64_t lo = qmin - r[kb].hi, hi = qmax - r[kb].lo;  // elapsed-time range
+        const int blo = bucket_of(lo, T), bhi = bucket_of(hi, T);
+        bc.tfast = time_fast_ok(qmin, qmax, r[kb].lo, r[kb].hi);
+        bc.tsorted = lo >= 0;
+        bc.tmode = blo == bhi ? 0 : ((bhi == blo + 1 && bc.tfast) ? 1 : 2);
+        bc.thr = bhi < 31 ? (1 << bhi) : 0x7fffffff;
+        bc.tlo = sload(rtg + blo);
+        bc.thi = sload(rtg + bhi);
+      }
+    }
+    return c;
+  };
+
+  const int nkt = (kend - kbeg + MBN - 1) / MBN;
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
+  // Pipeline: tile t computes while tile t+1's keys and values stream into the
+  // idle buffer. At the end of tile t the bias classes of tile t+1 are decided
+  // from timestamp ranges requested one tile earlier, and those of tile t+2
+  // are requested, so the range loads never wait.
+  TileClass cls{};
+  KeyRange rnx[2];  // timestamp ranges of the next tile's key blocks
   if (nkt > 0) {
-    issue_tile(B0{}, t.kbeg);
-    finish_tile(B0{}, t.kbeg);
+    dma_tile(B0{}, dma_src(kbeg));
+    ts_fetch(kbeg);
+    KeyRange r[2];
+    load_ranges(kbeg, r);
+    cls = classify(kbeg, r);
+    if (nkt > 1) load_ranges(kbeg + MBN, rnx);
+    finish_tile(B0{}, true);
   }
   __syncthreads();
 
-  // per-lane key offset inside a 32-key block for accumulator slot r
-  // keyoff(r) = 8*(r/4) + 4*hl + (r%4)
-  auto tile_step = [&](auto bufc, int64_t kt) {
+  auto kfrag = [&](const bf16* Kt, int kb, int kk) {
+    return load_bf16x8(&Kt[tile_off<D>(32 * kb + l32, 16 * kk + 8 * hl)]);
+  };
+  // B fragment of the bias k-step: rows 0 and 1 hold bias_hi and bias_lo (a bf16
+  // split, exact to ~2^-16 relative) for every query column
+  auto bias_frag = [&](float bias) {
+    bf16x8 bfrag;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) bfrag[i] = (bf16)0.f;
+    const bf16 bhi = (bf16)bias;
+    if (hl == 0) {
+      bfrag[0] = bhi;
+      bfrag[1] = (bf16)(bias - (float)bhi);
+    }
+    return bfrag;
+  };
+  const int g16 = lane >> 4, rho = lane & 15;
+  // V fragment m = s2 * NC + c of 32-key block kb: the k-slot (hl, i) of step s2
+  // is key 16*s2 + 8*(i/4) + 4*hl + i%4, the accumulator's key order
+  auto vfrag = [&](const bf16* Vt, int kb, int m) {
+    const int s2 = m / NC, c = m % NC;
+    const int krow = 32 * kb + 16 * s2 + 4 * hl + (rho >> 2);
+    const int col = c * 32 + 16 * (g16 & 1) + 4 * (rho & 3);
+    const bf16x4 v1 = tr_read(&Vt[tile_off<D>(krow, col)]);
+    const bf16x4 v2 = tr_read(&Vt[tile_off<D>(krow + 8, col)]);
+    bf16x8 bv;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      bv[i] = v1[i];
+      bv[4 + i] = v2[i];
+    }
+    return bv;
+  };
+
+  auto tile_step = [&](auto bufc, int kt) {
     constexpr int buf = decltype(bufc)::value;
     using BN_ = std::integral_constant<int, 1 - buf>;
-    const int64_t k0 = t.kbeg + kt * MBN;
-    if (kt + 1 < nkt) issue_tile(BN_{}, k0 + MBN);
-
-    if (wave_live) {
-      const bf16* Kt = buf ? Ks1 : Ks0;
-      const bf16* Vt = buf ? Vs1 : Vs0;
-      // ---- classify both 32-key blocks (wave-uniform scalars)
-      bool act[2], need_mask[2], uni[2], pos_c[2], time_c[2], time_fast[2], time_sorted[2];
-      float ubias[2];
+    const int k0 = kbeg + kt * MBN;
+    const bool more = kt + 1 < nkt;
+    const int kn = k0 + MBN;  // the next tile's first key
+    if (more) {
+      dma_tile(BN_{}, dma_src(kn));
+      ts_fetch(kn);
+    }
+    TileClass cn = cls;
+    KeyRange rn2[2] = {};
+    const BlockClass c0 = cls.b[0];
+    const BlockClass c1 = cls.b[1];
+    const bf16* Kt = buf ? Ks1 : Ks0;
+    const bf16* Vt = buf ? Vs1 : Vs0;
+    const bool fast = c0.act && c1.act && !c0.mask && !c1.mask && c0.pos_c && c1.pos_c &&
+                      c0.tmode == 0 && c1.tmode == 0;
+    constexpr int E = 16 / NKK;  // scores activated per interleaved step
+    // SiLU of accumulator slots st*E .. st*E+E-1 into bf16 A fragments
+    auto act_step = [&](const f32x16& x, bf16x8* pa, int st) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int64_t kb0 = k0 + 32 * kb;
-        act[kb] = kb0 < t.kend && (CAND || kb0 <= wlast);
-        need_mask[kb] = CAND ? (kb0 + 32 > t.kend) : (kb0 + 31 > wrow0);
-        const int64_t min_dpos = (CAND ? t.qpos0 : wrow0) - (kb0 + 31);
-        pos_c[kb] = !has_pos || min_dpos >= P - 1;
-        float b = has_pos && pos_c[kb] ? rp[P - 1] : 0.f;
-        time_c[kb] = true;
-        time_fast[kb] = true;
-        time_sorted[kb] = true;
-        if (has_time && act[kb]) {
-          const int64_t kmin = uniform64(kstat[buf][kb][0]);
-          const int64_t kmax = uniform64(kstat[buf][kb][1]);
-          const int64_t lo = qmin - kmax, hi = qmax - kmin;  // elapsed-time range
-          const int blo = bucket_of(lo, T), bhi = bucket_of(hi, T);
-          time_c[kb] = blo == bhi;
-          if (time_c[kb]) b += rt[blo < 63 ? blo : 63];
-          time_fast[kb] = time_fast_ok(qmin, qmax, kmin, kmax);
-          time_sorted[kb] = lo >= 0;
-        }
-        uni[kb] = pos_c[kb] && time_c[kb];
-        ubias[kb] = b;
+      for (int e = 0; e < E; ++e) {
+        const int r = st * E + e;
+        pa[r >> 3][r & 7] = (bf16)silu_fast(x[r]);
       }
-
-      // ---- S^T. A uniform bias enters as one extra MFMA k-step: a constant all-ones
-      // A fragment (keys x {0,1}) times a B fragment holding bias_hi, bias_lo
-      // (bf16 split, exact to ~2^-16 relative) for every row. The accumulator then
-      // starts from the inline zero, and no vector instruction touches the bias.
-      auto qk = [&](int kb, bool with_bias, float bias) {
-        f32x16 acc;
-        const bf16x8 kf0 = load_bf16x8(&Kt[tile_off<D>(32 * kb + l32, 8 * hl)]);
-        if (with_bias) {
-          bf16x8 bfrag;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) bfrag[i] = (bf16)0.f;
-          const bf16 bhi = (bf16)bias;
-          if (hl == 0) {
-            bfrag[0] = bhi;
-            bfrag[1] = (bf16)(bias - (float)bhi);
-          }
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, bfrag, f32x16{}, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf0, qf[0], acc, 0, 0, 0);
-        } else {
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf0, qf[0], f32x16{}, 0, 0, 0);
-        }
-#pragma unroll
-        for (int kk = 1; kk < NKK; ++kk) {
-          const bf16x8 kf = load_bf16x8(&Kt[tile_off<D>(32 * kb + l32, 16 * kk + 8 * hl)]);
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], acc, 0, 0, 0);
-        }
-        return acc;
-      };
-      // SiLU to bf16 A fragments, with the mask applied when asked
-      auto activate = [&](const f32x16& x, int kb, bool mask, bf16x8* pa) {
-        const int64_t kb0 = k0 + 32 * kb;
-        const int dbase = (int)(qpos - kb0) - 4 * hl;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float p = silu_fast(x[r]);
-          if (mask) {
-            const int keyoff = 8 * (r >> 2) + 4 * hl + (r & 3);
-            const bool vis = CAND ? (kb0 + keyoff < t.kend) : (dbase - (8 * (r >> 2) + (r & 3)) >= 0);
-            p = vis ? p : 0.f;
-          }
-          pa[r >> 3][r & 7] = (bf16)p;
-        }
-      };
-      // O += P V; the k-slot (hl, i) of step s2 is key 16*s2 + 8*(i/4) + 4*hl + i%4
-      auto pv = [&](int kb, const bf16x8* pa) {
-        const int g = lane >> 4, rho = lane & 15;
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          const int krow = 32 * kb + 16 * s2 + 4 * hl + (rho >> 2);
-#pragma unroll
-          for (int c = 0; c < NC; ++c) {
-            const int col = c * 32 + 16 * (g & 1) + 4 * (rho & 3);
-            const bf16x4 v1 = tr_read(&Vt[tile_off<D>(krow, col)]);
-            const bf16x4 v2 = tr_read(&Vt[tile_off<D>(krow + 8, col)]);
-            bf16x8 bv;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) { bv[i] = v1[i]; bv[4 + i] = v2[i]; }
-            o[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[s2], bv, o[c], 0, 0, 0);
-          }
-        }
-      };
-
-      const bool fast = act[0] && act[1] && uni[0] && uni[1] && !need_mask[0] && !need_mask[1];
-      if (fast) {
-        // Common case: both blocks live, uniform bias, no mask. The instruction order
-        // is written out and fenced (sched_barrier) so that the in-order wavefront
-        // issues one MFMA (~40 cycles in the matrix core), then the independent
-        // vector work that fits under it:
-        //   block 0: S^T chain;
-        //   block 1: S^T chain, each step carrying the SiLU of ~2 of block 0's scores;
-        //   block 0: P V, each step carrying the SiLU of 2 of block 1's scores;
-        //   block 1: P V.
-        constexpr int NS = NKK + 1;  // S steps per block (bias step + NKK)
-        auto bias_frag = [&](float bias) {
-          bf16x8 bfrag;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) bfrag[i] = (bf16)0.f;
-          const bf16 bhi = (bf16)bias;
-          if (hl == 0) {
-            bfrag[0] = bhi;
-            bfrag[1] = (bf16)(bias - (float)bhi);
-          }
-          return bfrag;
-        };
-        auto kfrag = [&](int kb, int kk) {
-          return load_bf16x8(&Kt[tile_off<D>(32 * kb + l32, 16 * kk + 8 * hl)]);
-        };
-        const int g = lane >> 4, rho = lane & 15;
-        auto vfrag = [&](int kb, int m) {  // m = s2 * NC + c
-          const int s2 = m / NC, c = m % NC;
-          const int krow = 32 * kb + 16 * s2 + 4 * hl + (rho >> 2);
-          const int col = c * 32 + 16 * (g & 1) + 4 * (rho & 3);
-          const bf16x4 v1 = tr_read(&Vt[tile_off<D>(krow, col)]);
-          const bf16x4 v2 = tr_read(&Vt[tile_off<D>(krow + 8, col)]);
-          bf16x8 bv;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) { bv[i] = v1[i]; bv[4 + i] = v2[i]; }
-          return bv;
-        };
-        auto act_range = [&](const f32x16& x, bf16x8* pa, int r0, int r1) {
-#pragma unroll
-          for (int r = r0; r < r1; ++r) pa[r >> 3][r & 7] = (bf16)silu_fast(x[r]);
-        };
-        const bf16x8 bf0 = bias_frag(ubias[0]), bf1 = bias_frag(ubias[1]);
-        // block 0: S^T
+    };
+    // Common case: both blocks live, no mask, one position bucket and one time
+    // bucket per block, so the bias is a constant that the bias k-step adds. The
+    // path is one basic block (no branch, so no instruction can be moved across
+    // the fences); its instruction order is written out and fenced
+    // (sched_barrier) so that the in-order wavefront issues one MFMA, then the
+    // independent vector work that fits under it:
+    //   block 0: S^T chain;
+    //   block 1: S^T chain, each step carrying the SiLU of 16/NKK of block 0's scores;
+    //   block 0: P V, each step carrying the SiLU of 16/NKK of block 1's scores;
+    //   block 1: P V.
+    auto fast_path = [&]() {
+      f32x16 s0;
+      {
         bf16x8 kq[NKK];
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) kq[kk] = kfrag(0, kk);
-        f32x16 s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, bf0, f32x16{}, 0, 0, 0);
+        for (int kk = 0; kk < NKK; ++kk) kq[kk] = kfrag(Kt, 0, kk);
+        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones(), bias_frag(pb + c0.tlo), f32x16{}, 0,
+                                                     0, 0);
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk)
           s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kq[kk], qf[kk], s0, 0, 0, 0);
+      }
+      bf16x8 k1[NKK];
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) kq[kk] = kfrag(1, kk);
+      for (int kk = 0; kk < NKK; ++kk) k1[kk] = kfrag(Kt, 1, kk);
+      f32x16 s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones(), bias_frag(pb + c1.tlo), f32x16{},
+                                                          0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      bf16x8 pa0[2], pa1[2];
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1[kk], qf[kk], s1, 0, 0, 0);
+        act_step(s0, pa0, kk);
         __builtin_amdgcn_sched_barrier(0);
-        // block 1: S^T, carrying block 0's SiLU
-        bf16x8 pa0[2], pa1[2];
-        f32x16 s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, bf1, f32x16{}, 0, 0, 0);
-        act_range(s0, pa0, 0, 16 / NS);
+      }
+      constexpr int NPV = 2 * NC;  // P V steps per block, one per activation step
+      static_assert(NPV == NKK, "one P V step per activation step");
+      bf16x8 vb = vfrag(Vt, 0, 0);
+#pragma unroll
+      for (int m = 0; m < NPV; ++m) {
+        const bf16x8 vnext = vfrag(Vt, m + 1 < NPV ? 0 : 1, (m + 1) % NPV);
+        o[m % NC] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa0[m / NC], vb, o[m % NC], 0, 0, 0);
+        act_step(s1, pa1, m);
+        vb = vnext;
         __builtin_amdgcn_sched_barrier(0);
+      }
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-          s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kq[kk], qf[kk], s1, 0, 0, 0);
-          act_range(s0, pa0, (kk + 1) * 16 / NS, (kk + 2) * 16 / NS);
-          __builtin_amdgcn_sched_barrier(0);
+      for (int m = 0; m < NPV; ++m) {
+        const bf16x8 vnext = vfrag(Vt, 1, (m + 1) % NPV);
+        o[m % NC] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa1[m / NC], vb, o[m % NC], 0, 0, 0);
+        vb = vnext;
+      }
+    };
+
+    // General path: any mix of masks, per-element position buckets and
+    // per-element time buckets. Both blocks' S^T first, then each block's
+    // per-element bias and SiLU, then both P V products.
+    auto general_path = [&]() {
+      f32x16 x[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const BlockClass& bc = kb ? c1 : c0;
+        if (!bc.act) continue;
+        bf16x8 kq[NKK];
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) kq[kk] = kfrag(Kt, kb, kk);
+        // the constant part of the bias (the lower time bucket when two)
+        const float ub = (bc.pos_c ? pb : 0.f) + (bc.tmode < 2 ? bc.tlo : 0.f);
+        x[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones(), bias_frag(ub), f32x16{}, 0, 0, 0);
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk)
+          x[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kq[kk], qf[kk], x[kb], 0, 0, 0);
+      }
+      bf16x8 pa[2][2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const BlockClass& bc = kb ? c1 : c0;
+        if (!bc.act) continue;
+        const int kb0 = k0 + 32 * kb;
+        // i - j = dbase - (8*(r/4) + r%4) for accumulator slot r
+        const int dbase = qpos - kb0 - 4 * hl;
+        if (!bc.pos_c) {
+          float g[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            int d = dbase - (8 * (r >> 2) + (r & 3));
+            d = d < 0 ? 0 : (d < P - 1 ? d : P - 1);
+            g[r] = rp[d];
+          }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) x[kb][r] += g[r];
         }
-        // block 0: P V, carrying block 1's SiLU
-        constexpr int NPV = 2 * NC;
-        bf16x8 vb = vfrag(0, 0);
+        const uint32_t* tkl = tk_lo[buf] + 32 * kb + 4 * hl;
+        if (bc.tmode == 1) {
+          // two adjacent buckets: the upper one's excess over the constant
+          const float dl = bc.thi - bc.tlo;
 #pragma unroll
-        for (int m = 0; m < NPV; ++m) {
-          const bf16x8 vnext = vfrag(m + 1 < NPV ? 0 : 1, (m + 1) % NPV);
-          o[m % NC] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa0[m / NC], vb, o[m % NC], 0, 0, 0);
-          act_range(s1, pa1, m * 16 / NPV, (m + 1) * 16 / NPV);
-          vb = vnext;
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        // block 1: P V
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const u32x4 tk4 = *reinterpret_cast<const u32x4*>(tkl + 8 * g4);
 #pragma unroll
-        for (int m = 0; m < NPV; ++m) {
-          const bf16x8 vnext = vfrag(1, (m + 1) % NPV);
-          o[m % NC] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa1[m / NC], vb, o[m % NC], 0, 0, 0);
-          vb = vnext;
-        }
-      } else {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          if (!act[kb]) continue;
-          const int64_t kb0 = k0 + 32 * kb;
-          f32x16 x = qk(kb, uni[kb] && ubias[kb] != 0.f, ubias[kb]);
-          if (!uni[kb]) {
-            // per-element bias for this block
-            const int dbase = (int)(qpos - kb0) - 4 * hl;  // i - j = dbase - (8*(r/4) + r%4)
-            if (!pos_c[kb]) {
-#pragma unroll
-              for (int r = 0; r < 16; ++r) {
-                int d = dbase - (8 * (r >> 2) + (r & 3));
-                d = d < 0 ? 0 : (d < P - 1 ? d : P - 1);
-                x[r] += rp[d];
-              }
-            }
-            // the constant part of the bias (position or time, whichever is constant)
-            if (pos_c[kb] != time_c[kb] && ubias[kb] != 0.f) {
-#pragma unroll
-              for (int r = 0; r < 16; ++r) x[r] += ubias[kb];
-            }
-            if (has_time && !time_c[kb]) {
-              const uint32_t* tkl = tk_lo[buf] + 32 * kb + 4 * hl;
-              if (time_fast[kb] && time_sorted[kb]) {
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                  const u32x4 tk4 = *reinterpret_cast<const u32x4*>(tkl + 8 * g);
-#pragma unroll
-                  for (int e = 0; e < 4; ++e)
-                    x[4 * g + e] += rtc[__builtin_clz((tq1 - tk4[e]) | 1u)];
-                }
-              } else if (time_fast[kb]) {
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                  const u32x4 tk4 = *reinterpret_cast<const u32x4*>(tkl + 8 * g);
-#pragma unroll
-                  for (int e = 0; e < 4; ++e) x[4 * g + e] += rtc[time_clz_fast(tq1, tk4[e])];
-                }
-              } else {
-                const int64_t* tk = tk64[buf] + 32 * kb + 4 * hl;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                  const int bt = time_bucket64(tq, tk[8 * (r >> 2) + (r & 3)]);
-                  x[r] += rt[bt < 63 ? bt : 63];
-                }
-              }
+            for (int e = 0; e < 4; ++e) {
+              const int d = (int)(tq1 - tk4[e]);
+              x[kb][4 * g4 + e] += d >= bc.thr ? dl : 0.f;
             }
           }
-          bf16x8 pa[2];
-          activate(x, kb, need_mask[kb], pa);
-          pv(kb, pa);
+        } else if (bc.tmode == 2) {
+          float g[16];
+          if (bc.tfast) {
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) {
+              const u32x4 tk4 = *reinterpret_cast<const u32x4*>(tkl + 8 * g4);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const uint32_t dd = tq1 - tk4[e];
+                // no negative elapsed time: the low bit keeps the count defined
+                g[4 * g4 + e] =
+                    rtc[bc.tsorted ? __builtin_clz(dd | 1u) : time_clz_fast(tq1, tk4[e])];
+              }
+            }
+          } else {
+            const int64_t* tk = tk64[buf] + 32 * kb + 4 * hl;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int bt = time_bucket64(tq, tk[8 * (r >> 2) + (r & 3)]);
+              g[r] = rt[bt < 63 ? bt : 63];
+            }
+          }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) x[kb][r] += g[r];
+        }
+        // SiLU to bf16 A fragments, with the mask applied when asked
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float p = silu_fast(x[kb][r]);
+          if (bc.mask) {
+            const int keyoff = 8 * (r >> 2) + 4 * hl + (r & 3);
+            const bool vis =
+                CAND ? (kb0 + keyoff < kend) : (dbase - (8 * (r >> 2) + (r & 3)) >= 0);
+            p = vis ? p : 0.f;
+          }
+          pa[kb][r >> 3][r & 7] = (bf16)p;
         }
       }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const BlockClass& bc = kb ? c1 : c0;
+        if (!bc.act) continue;
+#pragma unroll
+        for (int m = 0; m < 2 * NC; ++m)
+          o[m % NC] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[kb][m / NC], vfrag(Vt, kb, m),
+                                                              o[m % NC], 0, 0, 0);
+      }
+    };
+
+    if (wave_live) {
+      if (fast)
+        fast_path();
+      else
+        general_path();
     }
-    if (kt + 1 < nkt) finish_tile(BN_{}, k0 + MBN);
+    // the next tile's classes: its timestamp ranges were loaded a tile ago
+    if (more) {
+      cn = classify(kn, rnx);
+      if (kt + 2 < nkt) load_ranges(kn + MBN, rn2);
+    }
+    finish_tile(BN_{}, more);
     __syncthreads();
+    cls = cn;
+    rnx[0] = rn2[0];
+    rnx[1] = rn2[1];
   };
-  for (int64_t kt = 0; kt < nkt; kt += 2) {
+  for (int kt = 0; kt < nkt; kt += 2) {
     tile_step(B0{}, kt);
     if (kt + 1 < nkt) tile_step(B1{}, kt + 1);
   }

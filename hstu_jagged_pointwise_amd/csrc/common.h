@@ -15,6 +15,14 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Load of data that no kernel in flight writes, through the scalar data cache
+// when the address is wavefront-uniform (the constant address space lets the
+// compiler select s_load).
+template <typename T>
+__device__ __forceinline__ T sload(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)p;
+}
+
 // ---------------------------------------------------------------------------
 // Bias buckets. These compute the relative attention bias rab^{p,t} of
 // eq. 2 ("What an HSTU layer changes", HSTU chapter). The bias encodes

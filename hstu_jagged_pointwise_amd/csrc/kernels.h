@@ -5,6 +5,18 @@
 
 namespace hstu {
 
+// Smallest and largest timestamp of one 32-key block of a sequence. Block j of
+// sequence b (keys 32j .. 32j+31, clipped to the sequence) sits at slot
+// key_range_slot(offsets[b], b) + j; distinct sequences never share a slot.
+struct KeyRange {
+  int64_t lo, hi;
+};
+__host__ __device__ inline int64_t key_range_slot(int64_t seq_start, int seq) {
+  return seq_start / 32 + seq;
+}
+// Slots needed for `total` keys in `batch` sequences.
+inline int64_t key_range_slots(int64_t total, int batch) { return total / 32 + batch + 1; }
+
 // One attention launch. Row strides (ld_*) are in elements. Tensor bases point
 // at head 0 of row 0; head h sits at column h * d within each row.
 struct AttnArgs {
@@ -19,6 +31,7 @@ struct AttnArgs {
   const int64_t* ts_k;        // per key row, or NULL
   const float* rab_pos;       // [H][P] or NULL
   const float* rab_time;      // [H][T] or NULL
+  const KeyRange* key_ranges; // per 32-key block timestamp ranges of the keys (with ts_k), else NULL
   int batch;                  // number of sequences (causal) or users (candidate mode)
   int H, d_qk, d_v, P, T;
   float inv_n;
@@ -54,6 +67,9 @@ bool attn_mfma_strides_ok(const AttnArgs& a);
 
 hipError_t launch_plan_causal(const int64_t* offsets, int B, int tile_rows, int max_tiles,
                               int2* items, int n_items, hipStream_t s);
+// Fills the per-block timestamp ranges of B jagged sequences (see KeyRange).
+hipError_t launch_key_ranges(const int64_t* offsets, const int64_t* ts, int B, int64_t max_len,
+                             KeyRange* out, hipStream_t s);
 hipError_t launch_attn_simple(const AttnArgs& a, int use_bf16, bool cand, hipStream_t s);
 hipError_t launch_attn_mfma(const AttnArgs& a, bool cand, hipStream_t s);
 

@@ -10,6 +10,8 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <algorithm>
+
 namespace hstu {
 
 constexpr int kPlanThreads = 1024;
@@ -65,6 +67,42 @@ __global__ __launch_bounds__(kPlanThreads) void plan_causal_kernel(const int64_t
       if (pos < n_items) items[pos] = make_int2(b, t);
     }
   }
+}
+
+// Timestamp range of every 32-key block (the keys one attention wavefront
+// classifies at a time). Each half-wavefront reduces one block; the attention
+// kernel then decides a block's bias class from two scalar loads instead of
+// reducing timestamps itself on every key tile.
+__global__ __launch_bounds__(256) void key_range_kernel(const int64_t* __restrict__ off,
+                                                        const int64_t* __restrict__ ts,
+                                                        KeyRange* __restrict__ out) {
+  const int b = blockIdx.x;
+  const int64_t s0 = off[b], n = off[b + 1] - s0;
+  const int64_t nblk = (n + 31) / 32;
+  const int64_t base = key_range_slot(s0, b);
+  const int l32 = threadIdx.x & 31, half = threadIdx.x >> 5;
+  for (int64_t j = (int64_t)blockIdx.y * 8 + half; j < nblk; j += (int64_t)gridDim.y * 8) {
+    const int64_t key = 32 * j + l32;
+    const bool ok = key < n;
+    int64_t mn = ok ? ts[s0 + key] : INT64_MAX;
+    int64_t mx = ok ? ts[s0 + key] : INT64_MIN;
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) {  // stays inside the half-wavefront
+      const int64_t a1 = __shfl_xor(mn, o, 64), a2 = __shfl_xor(mx, o, 64);
+      mn = a1 < mn ? a1 : mn;
+      mx = a2 > mx ? a2 : mx;
+    }
+    if (l32 == 0) out[base + j] = KeyRange{mn, mx};
+  }
+}
+
+hipError_t launch_key_ranges(const int64_t* offsets, const int64_t* ts, int B, int64_t max_len,
+                             KeyRange* out, hipStream_t s) {
+  if (B <= 0 || max_len <= 0) return hipSuccess;
+  const int64_t blocks = (max_len + 31) / 32;
+  const unsigned gy = (unsigned)std::min<int64_t>((blocks + 7) / 8, 64);
+  hipLaunchKernelGGL(key_range_kernel, dim3((unsigned)B, gy), dim3(256), 0, s, offsets, ts, out);
+  return hipGetLastError();
 }
 
 hipError_t launch_plan_causal(const int64_t* offsets, int B, int tile_rows, int max_tiles,

@@ -102,7 +102,8 @@ def test_workspace_sizes(ops):
     n = ops.hstu_attn_workspace_size(d, off)
     items = 3 + 1 + 0 + 2
     al = lambda x: (x + 255) // 256 * 256
-    assert n == al(items * 8) + al(500 * 2 * 64 * 4)
+    key_ranges = 500 // 32 + 4 + 1  # one (min, max) timestamp pair per 32-key block slot
+    assert n == al(items * 8) + al(key_ranges * 16) + al(500 * 2 * 64 * 4)
     d32 = _desc(ops, dtype_code=ops.HSTU_F32, batch=4, max_seq_len=300)  # fp32: 64-row tiles
     assert ops.hstu_attn_workspace_size(d32, off) == al((5 + 1 + 0 + 4) * 8) + al(500 * 2 * 64 * 4)
     with pytest.raises(ops.HstuError) as e:
