@@ -391,49 +391,137 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
         pa[r >> 3][r & 7] = (bf16)silu_fast(x[r]);
       }
     };
+    // S^T of one block, with the constant part of its bias through the bias k-step
+    auto s_chain = [&](int kb, float bias) {
+      bf16x8 kq[NKK];
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) kq[kk] = kfrag(Kt, kb, kk);
+      f32x16 x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones(), bias_frag(bias), f32x16{}, 0, 0, 0);
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk)
+        x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kq[kk], qf[kk], x, 0, 0, 0);
+      return x;
+    };
+    // Each tile ends in one shared tail, the only code that touches the output
+    // accumulators: block 0's P V, carrying the SiLU of block 1's scores x1,
+    // then block 1's P V. The paths before it hand over block 0's P fragments
+    // pa0 and x1. A masked or inactive score is handed over as 0, whose SiLU is
+    // exactly 0.
+    bf16x8 pa0[2];
+    f32x16 x1;
     // Common case: both blocks live, no mask, one position bucket and one time
     // bucket per block, so the bias is a constant that the bias k-step adds. The
-    // path is one basic block (no branch, so no instruction can be moved across
-    // the fences); its instruction order is written out and fenced
-    // (sched_barrier) so that the in-order wavefront issues one MFMA, then the
-    // independent vector work that fits under it:
-    //   block 0: S^T chain;
-    //   block 1: S^T chain, each step carrying the SiLU of 16/NKK of block 0's scores;
-    //   block 0: P V, each step carrying the SiLU of 16/NKK of block 1's scores;
-    //   block 1: P V.
+    // path is one basic block (no branch, so nothing moves across the fences);
+    // its instruction order is written out and fenced (sched_barrier) so that
+    // the in-order wavefront issues one MFMA, then the independent vector work
+    // that fits under it: block 0's S^T chain; block 1's S^T chain, each step
+    // carrying the SiLU of 16/NKK of block 0's scores.
     auto fast_path = [&]() {
-      f32x16 s0;
-      {
-        bf16x8 kq[NKK];
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) kq[kk] = kfrag(Kt, 0, kk);
-        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones(), bias_frag(pb + c0.tlo), f32x16{}, 0,
-                                                     0, 0);
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk)
-          s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kq[kk], qf[kk], s0, 0, 0, 0);
-      }
+      const f32x16 s0 = s_chain(0, pb + c0.tlo);
       bf16x8 k1[NKK];
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) k1[kk] = kfrag(Kt, 1, kk);
       f32x16 s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones(), bias_frag(pb + c1.tlo), f32x16{},
                                                           0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
-      bf16x8 pa0[2], pa1[2];
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
         s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1[kk], qf[kk], s1, 0, 0, 0);
         act_step(s0, pa0, kk);
         __builtin_amdgcn_sched_barrier(0);
       }
+      x1 = s1;
+    };
+
+    // General path, one 32-key block at a time: any mix of masks, per-element
+    // position buckets and per-element time buckets; the constant part of the
+    // bias (the lower time bucket when two) goes through the bias k-step.
+    auto general_block = [&](int kb, const BlockClass& bc) {
+      if (!bc.act) return f32x16{};
+      const int kb0 = k0 + 32 * kb;
+      f32x16 x = s_chain(kb, (bc.pos_c ? pb : 0.f) + (bc.tmode < 2 ? bc.tlo : 0.f));
+      // i - j = dbase - (8*(r/4) + r%4) for accumulator slot r
+      const int dbase = qpos - kb0 - 4 * hl;
+      if (!bc.pos_c) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          int d = dbase - (8 * (r >> 2) + (r & 3));
+          d = d < 0 ? 0 : (d < P - 1 ? d : P - 1);
+          x[r] += rp[d];
+        }
+      }
+      const uint32_t* tkl = tk_lo[buf] + 32 * kb + 4 * hl;
+      if (bc.tmode == 1) {
+        // two adjacent buckets: the upper one's excess over the constant
+        const float dl = bc.thi - bc.tlo;
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const u32x4 tk4 = *reinterpret_cast<const u32x4*>(tkl + 8 * g4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int d = (int)(tq1 - tk4[e]);
+            x[4 * g4 + e] += d >= bc.thr ? dl : 0.f;
+          }
+        }
+      } else if (bc.tmode == 2) {
+        if (bc.tfast) {
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const u32x4 tk4 = *reinterpret_cast<const u32x4*>(tkl + 8 * g4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              x[4 * g4 + e] += rtc[bc.tsorted ? __builtin_clz((tq1 - tk4[e]) | 1u)
+                                              : time_clz_fast(tq1, tk4[e])];
+          }
+        } else {
+          const int64_t* tk = tk64[buf] + 32 * kb + 4 * hl;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int bt = time_bucket64(tq, tk[8 * (r >> 2) + (r & 3)]);
+            x[r] += rt[bt < 63 ? bt : 63];
+          }
+        }
+      }
+      if (bc.mask) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int keyoff = 8 * (r >> 2) + 4 * hl + (r & 3);
+          const bool vis = CAND ? (kb0 + keyoff < kend) : (dbase - (8 * (r >> 2) + (r & 3)) >= 0);
+          x[r] = vis ? x[r] : 0.f;
+        }
+      }
+      return x;
+    };
+    auto general_path = [&]() {
+      const f32x16 x0 = general_block(0, c0);
+#pragma unroll
+      for (int st = 0; st < NKK; ++st) act_step(x0, pa0, st);
+      x1 = general_block(1, c1);
+    };
+
+    if (wave_live) {
+      if (fast)
+        fast_path();
+      else
+        general_path();
+    } else {
+      // no live rows: P = 0 for both blocks (V holds finite data)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pa0[0][i] = pa0[1][i] = (bf16)0.f;
+      x1 = f32x16{};
+    }
+    // shared tail: block 0's P V carrying block 1's SiLU, then block 1's P V
+    {
+      bf16x8 pa1[2];
       constexpr int NPV = 2 * NC;  // P V steps per block, one per activation step
       static_assert(NPV == NKK, "one P V step per activation step");
       bf16x8 vb = vfrag(Vt, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int m = 0; m < NPV; ++m) {
         const bf16x8 vnext = vfrag(Vt, m + 1 < NPV ? 0 : 1, (m + 1) % NPV);
         o[m % NC] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa0[m / NC], vb, o[m % NC], 0, 0, 0);
-        act_step(s1, pa1, m);
+        act_step(x1, pa1, m);
         vb = vnext;
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -443,113 +531,6 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
         o[m % NC] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa1[m / NC], vb, o[m % NC], 0, 0, 0);
         vb = vnext;
       }
-    };
-
-    // General path: any mix of masks, per-element position buckets and
-    // per-element time buckets. Both blocks' S^T first, then each block's
-    // per-element bias and SiLU, then both P V products.
-    auto general_path = [&]() {
-      f32x16 x[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const BlockClass& bc = kb ? c1 : c0;
-        if (!bc.act) continue;
-        bf16x8 kq[NKK];
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) kq[kk] = kfrag(Kt, kb, kk);
-        // the constant part of the bias (the lower time bucket when two)
-        const float ub = (bc.pos_c ? pb : 0.f) + (bc.tmode < 2 ? bc.tlo : 0.f);
-        x[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones(), bias_frag(ub), f32x16{}, 0, 0, 0);
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk)
-          x[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kq[kk], qf[kk], x[kb], 0, 0, 0);
-      }
-      bf16x8 pa[2][2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const BlockClass& bc = kb ? c1 : c0;
-        if (!bc.act) continue;
-        const int kb0 = k0 + 32 * kb;
-        // i - j = dbase - (8*(r/4) + r%4) for accumulator slot r
-        const int dbase = qpos - kb0 - 4 * hl;
-        if (!bc.pos_c) {
-          float g[16];
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            int d = dbase - (8 * (r >> 2) + (r & 3));
-            d = d < 0 ? 0 : (d < P - 1 ? d : P - 1);
-            g[r] = rp[d];
-          }
-#pragma unroll
-          for (int r = 0; r < 16; ++r) x[kb][r] += g[r];
-        }
-        const uint32_t* tkl = tk_lo[buf] + 32 * kb + 4 * hl;
-        if (bc.tmode == 1) {
-          // two adjacent buckets: the upper one's excess over the constant
-          const float dl = bc.thi - bc.tlo;
-#pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {
-            const u32x4 tk4 = *reinterpret_cast<const u32x4*>(tkl + 8 * g4);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int d = (int)(tq1 - tk4[e]);
-              x[kb][4 * g4 + e] += d >= bc.thr ? dl : 0.f;
-            }
-          }
-        } else if (bc.tmode == 2) {
-          float g[16];
-          if (bc.tfast) {
-#pragma unroll
-            for (int g4 = 0; g4 < 4; ++g4) {
-              const u32x4 tk4 = *reinterpret_cast<const u32x4*>(tkl + 8 * g4);
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const uint32_t dd = tq1 - tk4[e];
-                // no negative elapsed time: the low bit keeps the count defined
-                g[4 * g4 + e] =
-                    rtc[bc.tsorted ? __builtin_clz(dd | 1u) : time_clz_fast(tq1, tk4[e])];
-              }
-            }
-          } else {
-            const int64_t* tk = tk64[buf] + 32 * kb + 4 * hl;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int bt = time_bucket64(tq, tk[8 * (r >> 2) + (r & 3)]);
-              g[r] = rt[bt < 63 ? bt : 63];
-            }
-          }
-#pragma unroll
-          for (int r = 0; r < 16; ++r) x[kb][r] += g[r];
-        }
-        // SiLU to bf16 A fragments, with the mask applied when asked
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float p = silu_fast(x[kb][r]);
-          if (bc.mask) {
-            const int keyoff = 8 * (r >> 2) + 4 * hl + (r & 3);
-            const bool vis =
-                CAND ? (kb0 + keyoff < kend) : (dbase - (8 * (r >> 2) + (r & 3)) >= 0);
-            p = vis ? p : 0.f;
-          }
-          pa[kb][r >> 3][r & 7] = (bf16)p;
-        }
-      }
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const BlockClass& bc = kb ? c1 : c0;
-        if (!bc.act) continue;
-#pragma unroll
-        for (int m = 0; m < 2 * NC; ++m)
-          o[m % NC] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[kb][m / NC], vfrag(Vt, kb, m),
-                                                              o[m % NC], 0, 0, 0);
-      }
-    };
-
-    if (wave_live) {
-      if (fast)
-        fast_path();
-      else
-        general_path();
     }
     // the next tile's classes: its timestamp ranges were loaded a tile ago
     if (more) {
