@@ -92,21 +92,35 @@ __device__ __forceinline__ int bucket_of(int64_t dt, int T) {
   return b < T - 1 ? b : T - 1;
 }
 
-// Bias class of one (wavefront, 32-key block) pair. Every field is uniform
-// across the wavefront.
-struct BlockClass {
-  bool act;        // some key of the block is visible to some row of the wavefront
-  bool mask;       // the block needs the per-element visibility mask
-  bool pos_c;      // one position bucket over the block (or no position bias)
-  int tmode;       // time bias: 0 one bucket (or none), 1 two adjacent buckets, 2 general
-  bool tfast;      // every elapsed time fits the 32-bit forms
-  bool tsorted;    // no elapsed time in the block is negative
-  int thr;         // tmode 1: upper bucket when the 32-bit t_i + 1 - t_j >= thr
-  float tlo, thi;  // time-table values of the lowest and highest bucket (0 without time bias)
-};
+// Bias classes of one tile's two 32-key blocks for one wavefront (uniform
+// values), packed so that two tiles' worth stays in few scalar registers.
+// Byte kb of f describes block kb:
+//   bit 0 act      some key of the block is visible to some row of the wavefront
+//   bit 1 mask     the block needs the per-element visibility mask
+//   bit 2 pos_c    one position bucket over the block (or no position bias)
+//   bits 3-4 tmode time bias: 0 one bucket (or none), 1 two adjacent buckets, 2 general
+//   bit 5 tfast    every elapsed time fits the 32-bit forms
+//   bit 6 tsorted  no elapsed time in the block is negative
+// and bits 16 + 8*kb .. 21 + 8*kb hold the block's highest time bucket bhi
+// (tmode 1: an element is in it when the 32-bit t_i + 1 - t_j >= 2^bhi).
 struct TileClass {
-  BlockClass b[2];
+  uint32_t f;
+  float tlo[2], thi[2];  // time-table values of each block's lowest and highest bucket
 };
+struct BlockClass {  // one block's view of a TileClass
+  uint32_t bits, bhi;
+  float tlo, thi;
+  __device__ bool act() const { return bits & 1u; }
+  __device__ bool mask() const { return bits & 2u; }
+  __device__ bool pos_c() const { return bits & 4u; }
+  __device__ uint32_t tmode() const { return (bits >> 3) & 3u; }
+  __device__ bool tfast() const { return bits & 32u; }
+  __device__ bool tsorted() const { return bits & 64u; }
+  __device__ int thr() const { return (int)(1u << bhi); }
+};
+__device__ __forceinline__ BlockClass block_class(const TileClass& c, int kb) {
+  return BlockClass{(c.f >> (8 * kb)) & 0xffu, (c.f >> (16 + 8 * kb)) & 63u, c.tlo[kb], c.thi[kb]};
+}
 }  // namespace
 
 bool attn_mfma_supported(int dtype_bf16, int d_qk, int d_v, int P, int T) {
@@ -282,30 +296,28 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
   };
   auto classify = [&](int k0, const KeyRange* r) {
     TileClass c;
+    c.f = 0;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      BlockClass& bc = c.b[kb];
       const int kb0 = k0 + 32 * kb;
-      bc.act = wave_live && kb0 < kend && (CAND || kb0 <= wlast);
-      bc.mask = CAND ? (kb0 + 32 > kend) : (kb0 + 31 > wrow0);
+      const bool act = wave_live && kb0 < kend && (CAND || kb0 <= wlast);
+      const bool mask = CAND ? (kb0 + 32 > kend) : (kb0 + 31 > wrow0);
       const int min_dpos = (CAND ? qpos0 : wrow0) - (kb0 + 31);
-      bc.pos_c = !has_pos || min_dpos >= P - 1;
-      bc.tmode = 0;
-      bc.tfast = true;
-      bc.tsorted = true;
-      bc.thr = 0;
-      bc.tlo = 0.f;
-      bc.thi = 0.f;
-      if (has_time && bc.act) {
+      const bool pos_c = !has_pos || min_dpos >= P - 1;
+      uint32_t bits = (act ? 1u : 0u) | (mask ? 2u : 0u) | (pos_c ? 4u : 0u) | 32u | 64u;
+      c.tlo[kb] = 0.f;
+      c.thi[kb] = 0.f;
+      if (has_time && act) {
         const int64_t lo = qmin - r[kb].hi, hi = qmax - r[kb].lo;  // elapsed-time range
         const int blo = bucket_of(lo, T), bhi = bucket_of(hi, T);
-        bc.tfast = time_fast_ok(qmin, qmax, r[kb].lo, r[kb].hi);
-        bc.tsorted = lo >= 0;
-        bc.tmode = blo == bhi ? 0 : ((bhi == blo + 1 && bc.tfast) ? 1 : 2);
-        bc.thr = bhi < 31 ? (1 << bhi) : 0x7fffffff;
-        bc.tlo = sload(rtg + blo);
-        bc.thi = sload(rtg + bhi);
+        const bool tfast = time_fast_ok(qmin, qmax, r[kb].lo, r[kb].hi);
+        const uint32_t tmode = blo == bhi ? 0u : ((bhi == blo + 1 && tfast) ? 1u : 2u);
+        bits = (bits & 7u) | (tmode << 3) | (tfast ? 32u : 0u) | (lo >= 0 ? 64u : 0u);
+        c.f |= (uint32_t)bhi << (16 + 8 * kb);
+        c.tlo[kb] = sload(rtg + blo);
+        c.thi[kb] = sload(rtg + bhi);
       }
+      c.f |= bits << (8 * kb);
     }
     return c;
   };
@@ -314,9 +326,9 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
   // Pipeline: tile t computes while tile t+1's keys and values stream into the
-  // idle buffer. At the end of tile t the bias classes of tile t+1 are decided
-  // from timestamp ranges requested one tile earlier, and those of tile t+2
-  // are requested, so the range loads never wait.
+  // idle buffer. At the start of tile t the bias classes of tile t+1 are
+  // decided from timestamp ranges requested one tile earlier, and those of tile
+  // t+2 are requested, so no scalar load is waited for on the way.
   TileClass cls{};
   KeyRange rnx[2];  // timestamp ranges of the next tile's key blocks
   if (nkt > 0) {
@@ -374,14 +386,20 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
       dma_tile(BN_{}, dma_src(kn));
       ts_fetch(kn);
     }
+    // the next tile's classes, from timestamp ranges requested a tile ago; the
+    // scalar loads of their table values then have this whole tile to land
     TileClass cn = cls;
     KeyRange rn2[2] = {};
-    const BlockClass c0 = cls.b[0];
-    const BlockClass c1 = cls.b[1];
+    if (more) {
+      cn = classify(kn, rnx);
+      if (kt + 2 < nkt) load_ranges(kn + MBN, rn2);
+    }
+    const BlockClass c0 = block_class(cls, 0);
+    const BlockClass c1 = block_class(cls, 1);
     const bf16* Kt = buf ? Ks1 : Ks0;
     const bf16* Vt = buf ? Vs1 : Vs0;
-    const bool fast = c0.act && c1.act && !c0.mask && !c1.mask && c0.pos_c && c1.pos_c &&
-                      c0.tmode == 0 && c1.tmode == 0;
+    // both blocks active, unmasked, one position bucket, one time bucket
+    const bool fast = (cls.f & 0x1f1fu) == 0x0505u;
     constexpr int E = 16 / NKK;  // scores activated per interleaved step
     // SiLU of accumulator slots st*E .. st*E+E-1 into bf16 A fragments
     auto act_step = [&](const f32x16& x, bf16x8* pa, int st) {
@@ -437,12 +455,12 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
     // position buckets and per-element time buckets; the constant part of the
     // bias (the lower time bucket when two) goes through the bias k-step.
     auto general_block = [&](int kb, const BlockClass& bc) {
-      if (!bc.act) return f32x16{};
+      if (!bc.act()) return f32x16{};
       const int kb0 = k0 + 32 * kb;
-      f32x16 x = s_chain(kb, (bc.pos_c ? pb : 0.f) + (bc.tmode < 2 ? bc.tlo : 0.f));
+      f32x16 x = s_chain(kb, (bc.pos_c() ? pb : 0.f) + (bc.tmode() < 2 ? bc.tlo : 0.f));
       // i - j = dbase - (8*(r/4) + r%4) for accumulator slot r
       const int dbase = qpos - kb0 - 4 * hl;
-      if (!bc.pos_c) {
+      if (!bc.pos_c()) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           int d = dbase - (8 * (r >> 2) + (r & 3));
@@ -451,7 +469,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
         }
       }
       const uint32_t* tkl = tk_lo[buf] + 32 * kb + 4 * hl;
-      if (bc.tmode == 1) {
+      if (bc.tmode() == 1) {
         // two adjacent buckets: the upper one's excess over the constant
         const float dl = bc.thi - bc.tlo;
 #pragma unroll
@@ -460,17 +478,17 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int d = (int)(tq1 - tk4[e]);
-            x[4 * g4 + e] += d >= bc.thr ? dl : 0.f;
+            x[4 * g4 + e] += d >= bc.thr() ? dl : 0.f;
           }
         }
-      } else if (bc.tmode == 2) {
-        if (bc.tfast) {
+      } else if (bc.tmode() == 2) {
+        if (bc.tfast()) {
 #pragma unroll
           for (int g4 = 0; g4 < 4; ++g4) {
             const u32x4 tk4 = *reinterpret_cast<const u32x4*>(tkl + 8 * g4);
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              x[4 * g4 + e] += rtc[bc.tsorted ? __builtin_clz((tq1 - tk4[e]) | 1u)
+              x[4 * g4 + e] += rtc[bc.tsorted() ? __builtin_clz((tq1 - tk4[e]) | 1u)
                                               : time_clz_fast(tq1, tk4[e])];
           }
         } else {
@@ -482,7 +500,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
           }
         }
       }
-      if (bc.mask) {
+      if (bc.mask()) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int keyoff = 8 * (r >> 2) + 4 * hl + (r & 3);
@@ -531,11 +549,6 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
         o[m % NC] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa1[m / NC], vb, o[m % NC], 0, 0, 0);
         vb = vnext;
       }
-    }
-    // the next tile's classes: its timestamp ranges were loaded a tile ago
-    if (more) {
-      cn = classify(kn, rnx);
-      if (kt + 2 < nkt) load_ranges(kn + MBN, rn2);
     }
     finish_tile(BN_{}, more);
     __syncthreads();
