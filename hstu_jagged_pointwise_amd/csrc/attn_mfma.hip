@@ -248,14 +248,12 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
                   (uint32_t)(nk - 1 - k0)};
   };
   // this wavefront's instruction pairs (K and V) for one tile
-  auto dma_tile = [&](auto bufc, const DmaSrc& src) {
+  auto dma_pair = [&](auto bufc, const DmaSrc& src, int j) {
     constexpr int buf = decltype(bufc)::value;
     bf16* Kd = buf ? Ks1 : Ks0;
     bf16* Vd = buf ? Vs1 : Vs0;
-#pragma unroll
-    for (int j = 0; j < NIW; ++j) {
+    {
       const int i = wu + 4 * j;
-      if (i >= NINSTR) break;
       const uint32_t row = min(spk[j] & 1023u, src.lim);
       const uint32_t off = row * ldb + 16u * (spk[j] >> 10);
       __builtin_amdgcn_global_load_lds(
@@ -265,6 +263,12 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
           (const __attribute__((address_space(1))) void*)(src.vb + off),
           (__attribute__((address_space(3))) void*)(&Vd[512 * i]), 16, 0, 0);
     }
+  };
+  static_assert(NINSTR == 4 * (NIW - 1) + 1, "only wavefront 0 issues a last pair");
+  auto dma_tile = [&](auto bufc, const DmaSrc& src) {
+#pragma unroll
+    for (int j = 0; j < NIW - 1; ++j) dma_pair(bufc, src, j);
+    if (wu == 0) dma_pair(bufc, src, NIW - 1);
   };
   int64_t ptk = 0;
   // each wavefront fetches the timestamps of 16 of the tile's keys
@@ -382,10 +386,12 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
     const int k0 = kbeg + kt * MBN;
     const bool more = kt + 1 < nkt;
     const int kn = k0 + MBN;  // the next tile's first key
-    if (more) {
-      dma_tile(BN_{}, dma_src(kn));
-      ts_fetch(kn);
-    }
+    // the last tile refills the idle buffer with its own keys (harmless), so
+    // that the DMA inside the fenced fast path needs no branch
+    const DmaSrc nsrc = dma_src(more ? kn : k0);
+    auto dma = [&](int j) { dma_pair(BN_{}, nsrc, j); };
+    if (wu == 0) dma(NIW - 1);
+    if (more) ts_fetch(kn);
     // the next tile's classes, from timestamp ranges requested a tile ago; the
     // scalar loads of their table values then have this whole tile to land
     TileClass cn = cls;
@@ -410,14 +416,20 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
       }
     };
     // S^T of one block, with the constant part of its bias through the bias k-step
-    auto s_chain = [&](int kb, float bias) {
+    auto s_chain = [&](int kb, float bias, bool with_dma) {
       bf16x8 kq[NKK];
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) kq[kk] = kfrag(Kt, kb, kk);
       f32x16 x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones(), bias_frag(bias), f32x16{}, 0, 0, 0);
+      if (with_dma) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk)
+      for (int kk = 0; kk < NKK; ++kk) {
         x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kq[kk], qf[kk], x, 0, 0, 0);
+        if (with_dma) {  // the dependent chain has room for the next tile's DMA
+          if (kk < NIW - 1) dma(kk);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
       return x;
     };
     // Each tile ends in one shared tail, the only code that touches the output
@@ -435,7 +447,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
     // that fits under it: block 0's S^T chain; block 1's S^T chain, each step
     // carrying the SiLU of 16/NKK of block 0's scores.
     auto fast_path = [&]() {
-      const f32x16 s0 = s_chain(0, pb + c0.tlo);
+      const f32x16 s0 = s_chain(0, pb + c0.tlo, true);
       bf16x8 k1[NKK];
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) k1[kk] = kfrag(Kt, 1, kk);
@@ -457,7 +469,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
     auto general_block = [&](int kb, const BlockClass& bc) {
       if (!bc.act()) return f32x16{};
       const int kb0 = k0 + 32 * kb;
-      f32x16 x = s_chain(kb, (bc.pos_c() ? pb : 0.f) + (bc.tmode() < 2 ? bc.tlo : 0.f));
+      f32x16 x = s_chain(kb, (bc.pos_c() ? pb : 0.f) + (bc.tmode() < 2 ? bc.tlo : 0.f), false);
       // i - j = dbase - (8*(r/4) + r%4) for accumulator slot r
       const int dbase = qpos - kb0 - 4 * hl;
       if (!bc.pos_c()) {
@@ -511,6 +523,8 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
       return x;
     };
     auto general_path = [&]() {
+#pragma unroll
+      for (int j = 0; j < NIW - 1; ++j) dma(j);
       const f32x16 x0 = general_block(0, c0);
 #pragma unroll
       for (int st = 0; st < NKK; ++st) act_step(x0, pa0, st);
@@ -523,6 +537,8 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
       else
         general_path();
     } else {
+#pragma unroll
+      for (int j = 0; j < NIW - 1; ++j) dma(j);
       // no live rows: P = 0 for both blocks (V holds finite data)
 #pragma unroll
       for (int i = 0; i < 8; ++i) pa0[0][i] = pa0[1][i] = (bf16)0.f;
