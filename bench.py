@@ -220,8 +220,9 @@ def cpu_baseline(x, budget_s=12.0):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    # the clocks take a few dozen calls to settle; the timed calls start after them
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--only", default="attn,mfalcon,layers,cpu")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     args = ap.parse_args()
