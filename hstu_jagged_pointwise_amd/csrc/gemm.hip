@@ -9,8 +9,11 @@
 // W is stored [out, in], so both operands are contiguous along the reduction
 // dimension and feed v_mfma_f32_32x32x16_bf16 directly from LDS rows. Workgroup
 // tiles are 128x128, or 64x64 when the grid would otherwise leave compute units
-// idle; K is staged through double-buffered LDS 64 at a time. fp32 inputs take a
-// plain vector-ALU tiled kernel.
+// idle. K streams through a 4-stage LDS ring 32 at a time, with three stages in
+// flight, filled by global_load_lds. Tiles are ordered so that the tiles of one
+// row block of A run on one XCD (sharing its L2). The epilogue stages each
+// wavefront's tile in LDS and writes whole 16-byte row segments. fp32 inputs
+// take a plain vector-ALU tiled kernel.
 #include "common.h"
 #include "kernels.h"
 
@@ -19,41 +22,110 @@
 namespace hstu {
 
 namespace {
-constexpr int GBK = 64;          // K per pipeline stage
-constexpr int GLD = GBK + 8;     // padded LDS row (elements): conflict-free ds_read_b128
-constexpr int GSPR = GLD / 8;    // 16-byte slots per LDS row (8 data + 1 pad)
+constexpr int GBK = 32;  // K per pipeline stage
+constexpr int NST = 4;   // LDS ring stages: NST-1 stages load while one is multiplied
 
-__device__ __forceinline__ void dma16(const bf16* g, bf16* lds_base) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
-                                   (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// Workgroup barrier that leaves in-flight global->LDS loads alone (__syncthreads
+// also waits for every outstanding vector memory operation, which would drain the
+// ring). This wavefront's LDS operations complete first.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 }  // namespace
 
-// BM x BN workgroup tile, 4 wavefronts as 2 x 2, each wavefront (BM/2) x (BN/2) of
-// 32x32 MFMA blocks. K streams through two LDS stages filled by global_load_lds
-// (the next stage loads while the current one is multiplied; one barrier per stage).
-// Rows past M or N repeat the last valid row; K must be a multiple of 8, and the
-// K tail of the last stage is zero-filled by a plain store.
+// LDS ring geometry of a BM x BN tile: each stage holds BM rows of A then BN rows
+// of W, GBK elements each, padded by 8 (the 16 rows of one ds_read_b128 phase fall
+// in distinct banks). A stage is filled by whole 64-lane DMA instructions, dealt
+// to the 4 wavefronts round robin and padded to an equal count per wavefront (the
+// per-wavefront waits count instructions).
+template <int BM, int BN>
+struct GemmShape {
+  static constexpr int GLD = GBK + 8, GSPR = GLD / 8, CPR = GBK / 8;
+  static constexpr int WM = BM / 2, WN = BN / 2;
+  static constexpr int FM = WM / 32, FN = WN / 32;
+  static constexpr int SLOTS = (BM + BN) * GSPR;
+  static constexpr int INSTR = (SLOTS + 63) / 64;
+  static constexpr int PERW = (INSTR + 3) / 4;           // instructions per wavefront (padded)
+  static constexpr int A_INSTR = BM * GSPR / 64;          // instructions that read A
+  static constexpr int STAGE = (4 * PERW) * 512;          // bf16 elements per stage (incl. junk)
+  static_assert(BM * GSPR % 64 == 0, "A rows fill whole instructions");
+};
+
+// C[M,N] = epi(A[M,K] W[N,K]^T + bias): 4 wavefronts as 2 x 2, each (BM/2) x (BN/2)
+// of 32x32 MFMA blocks. Rows past M or N repeat the last valid row; K must be a
+// multiple of 8, and the K tail of the last stage is zeroed in LDS.
 template <int BM, int BN, typename OutT>
 __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const bf16* __restrict__ A, int64_t lda,
-                                                           const bf16* __restrict__ W, int64_t ldw,
-                                                           const float* __restrict__ bias,
-                                                           const bf16* __restrict__ R, int64_t ldr,
-                                                           OutT* __restrict__ C, int64_t ldc,
-                                                           int64_t M, int N, int K, int silu) {
-  constexpr int WM = BM / 2, WN = BN / 2;      // per-wavefront tile
-  constexpr int FM = WM / 32, FN = WN / 32;    // 32x32 blocks per wavefront
-  constexpr int A_SLOTS = BM * GSPR, W_SLOTS = BN * GSPR;
-  constexpr int A_INSTR = (A_SLOTS + 63) / 64, W_INSTR = (W_SLOTS + 63) / 64;
-  __shared__ __attribute__((aligned(16))) bf16 As0[A_INSTR * 512];
-  __shared__ __attribute__((aligned(16))) bf16 As1[A_INSTR * 512];
-  __shared__ __attribute__((aligned(16))) bf16 Ws0[W_INSTR * 512];
-  __shared__ __attribute__((aligned(16))) bf16 Ws1[W_INSTR * 512];
+                                                         const bf16* __restrict__ W, int64_t ldw,
+                                                         const float* __restrict__ bias,
+                                                         const bf16* __restrict__ R, int64_t ldr,
+                                                         OutT* __restrict__ C, int64_t ldc, int64_t M,
+                                                         int N, int K, int silu, int tiles_n,
+                                                         int tiles_total) {
+  using G = GemmShape<BM, BN>;
+  constexpr int FM = G::FM, FN = G::FN, PERW = G::PERW, STAGE = G::STAGE;
+  constexpr int GLD = G::GLD, GSPR = G::GSPR, CPR = G::CPR;
+  __shared__ __attribute__((aligned(16))) bf16 S0[STAGE];
+  __shared__ __attribute__((aligned(16))) bf16 S1[STAGE];
+  __shared__ __attribute__((aligned(16))) bf16 S2[STAGE];
+  __shared__ __attribute__((aligned(16))) bf16 S3[STAGE];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
   const int l32 = lane & 31, hl = lane >> 5;
   const int wm = w >> 1, wn = w & 1;
-  const int64_t m0 = (int64_t)blockIdx.y * BM;
-  const int n0 = blockIdx.x * BN;
+  // XCD-aware order: workgroups are dealt to the 8 XCDs round robin; consecutive
+  // logical tiles (same row block of A) go to one XCD and share its L2
+  int tile;
+  {
+    const int b = blockIdx.x, x = b & 7, j = b >> 3;
+    const int per = tiles_total >> 3, rem = tiles_total & 7;
+    tile = (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + j;
+  }
+  const int64_t m0 = (int64_t)(tile / tiles_n) * BM;
+  const int n0 = (tile % tiles_n) * BN;
+
+  // per-lane DMA sources of this wavefront's PERW instructions (byte offsets from the
+  // row-block base of A or W; rows past M or N repeat the last row; pad slots fetch chunk 0)
+  uint32_t soff[PERW];
+  bool isA[PERW];
+#pragma unroll
+  for (int j = 0; j < PERW; ++j) {
+    const int i = wu + 4 * j;
+    const int slot = 64 * i + lane;
+    const int row = slot / GSPR, pc = slot % GSPR;
+    const int c = pc < CPR ? pc : 0;
+    isA[j] = i < G::A_INSTR;
+    if (i >= G::INSTR) {  // junk instruction: any valid A chunk
+      soff[j] = 0;
+      isA[j] = true;
+    } else if (isA[j]) {
+      const int64_t r = min(m0 + row, M - 1) - m0;
+      soff[j] = (uint32_t)(r * lda * 2 + 16 * c);
+    } else {
+      const int r = min(n0 + (row - BM), N - 1) - n0;
+      soff[j] = (uint32_t)((int64_t)r * ldw * 2 + 16 * c);
+    }
+  }
+  const char* abase = (const char*)(A + m0 * lda);
+  const char* wbase = (const char*)(W + (int64_t)n0 * ldw);
+  const int nks = (K + GBK - 1) / GBK;
+  auto issue = [&](auto bufc, int ks) {
+    constexpr int buf = decltype(bufc)::value;
+    bf16* D = buf == 0 ? S0 : buf == 1 ? S1 : buf == 2 ? S2 : S3;
+    const uint32_t kb = (uint32_t)ks * GBK * 2;
+#pragma unroll
+    for (int j = 0; j < PERW; ++j) {
+      const int i = wu + 4 * j;
+      const char* src = (isA[j] ? abase : wbase) + soff[j] + kb;
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                       (__attribute__((address_space(3))) void*)(&D[512 * i]), 16,
+                                       0, 0);
+    }
+  };
   f32x16 acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -61,74 +133,30 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const bf16* __restric
     for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  const int nks = (K + GBK - 1) / GBK;
-  auto issue = [&](auto bufc, int k0) {
+  auto compute = [&](auto bufc, int ks) {
     constexpr int buf = decltype(bufc)::value;
-    bf16* Ad = buf ? As1 : As0;
-    bf16* Wd = buf ? Ws1 : Ws0;
-    const bool ktail = k0 + GBK > K;
-#pragma unroll
-    for (int i = w; i < A_INSTR; i += 4) {
-      const int slot = 64 * i + lane;
-      if (slot < A_SLOTS) {
-        const int row = slot / GSPR, pc = slot % GSPR;
-        int c = pc < 8 ? pc : 0;
-        if (ktail && k0 + 8 * c >= K) c = 0;  // out-of-range K chunk: fetch any valid chunk
-        const int64_t gr = min(m0 + row, M - 1);
-        dma16(A + gr * lda + k0 + 8 * c, &Ad[512 * i]);
-      }
-    }
-#pragma unroll
-    for (int i = w; i < W_INSTR; i += 4) {
-      const int slot = 64 * i + lane;
-      if (slot < W_SLOTS) {
-        const int row = slot / GSPR, pc = slot % GSPR;
-        int c = pc < 8 ? pc : 0;
-        if (ktail && k0 + 8 * c >= K) c = 0;
-        const int64_t gr = min(n0 + row, N - 1);
-        dma16(W + gr * ldw + k0 + 8 * c, &Wd[512 * i]);
-      }
-    }
-  };
-  auto finish = [&](auto bufc, int k0) {
-    constexpr int buf = decltype(bufc)::value;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    if (k0 + GBK > K) {
-      // zero the K tail so that it adds nothing (the DMA filled it with valid data)
-      __syncthreads();
-      bf16* Ad = buf ? As1 : As0;
-      bf16* Wd = buf ? Ws1 : Ws0;
-      const int kv = K - k0;  // valid K in this stage, a multiple of 8
-      for (int e = tid; e < BM * 8; e += 256) {
-        const int row = e >> 3, c = e & 7;
+    bf16* D = buf == 0 ? S0 : buf == 1 ? S1 : buf == 2 ? S2 : S3;
+    if ((ks + 1) * GBK > K) {  // K tail: zero the chunks past K (uniform branch, last stage only)
+      lds_barrier();
+      const int kv = K - ks * GBK;  // a multiple of 8
+      for (int e = tid; e < (BM + BN) * CPR; e += 256) {
+        const int row = e / CPR, c = e % CPR;
         if (8 * c >= kv) {
-#pragma unroll
-          for (int q = 0; q < 8; ++q) Ad[row * GLD + 8 * c + q] = (bf16)0.f;
+          u32x4 z = {0u, 0u, 0u, 0u};
+          *reinterpret_cast<u32x4*>(&D[row * GLD + 8 * c]) = z;
         }
       }
-      for (int e = tid; e < BN * 8; e += 256) {
-        const int row = e >> 3, c = e & 7;
-        if (8 * c >= kv) {
-#pragma unroll
-          for (int q = 0; q < 8; ++q) Wd[row * GLD + 8 * c + q] = (bf16)0.f;
-        }
-      }
+      lds_barrier();
     }
-  };
-  auto compute = [&](auto bufc) {
-    constexpr int buf = decltype(bufc)::value;
-    const bf16* Ad = buf ? As1 : As0;
-    const bf16* Wd = buf ? Ws1 : Ws0;
 #pragma unroll
     for (int kk = 0; kk < GBK / 16; ++kk) {
       bf16x8 af[FM], bfr[FN];
 #pragma unroll
       for (int i = 0; i < FM; ++i)
-        af[i] = *reinterpret_cast<const bf16x8*>(&Ad[(wm * WM + 32 * i + l32) * GLD + 16 * kk + 8 * hl]);
+        af[i] = *reinterpret_cast<const bf16x8*>(&D[(wm * G::WM + 32 * i + l32) * GLD + 16 * kk + 8 * hl]);
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8*>(&Wd[(wn * WN + 32 * j + l32) * GLD + 16 * kk + 8 * hl]);
+        bfr[j] = *reinterpret_cast<const bf16x8*>(&D[(BM + wn * G::WN + 32 * j + l32) * GLD + 16 * kk + 8 * hl]);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -136,39 +164,74 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const bf16* __restric
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
   };
+  // prologue: NST-1 stages in flight
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
-  issue(B0{}, 0);
-  finish(B0{}, 0);
-  __syncthreads();
-  for (int ks = 0; ks < nks; ks += 2) {
-    if (ks + 1 < nks) issue(B1{}, (ks + 1) * GBK);
-    compute(B0{});
-    if (ks + 1 < nks) finish(B1{}, (ks + 1) * GBK);
-    __syncthreads();
-    if (ks + 1 >= nks) break;
-    if (ks + 2 < nks) issue(B0{}, (ks + 2) * GBK);
-    compute(B1{});
-    if (ks + 2 < nks) finish(B0{}, (ks + 2) * GBK);
-    __syncthreads();
+  using B2 = std::integral_constant<int, 2>;
+  using B3 = std::integral_constant<int, 3>;
+  if (0 < nks) issue(B0{}, 0);
+  if (1 < nks) issue(B1{}, 1);
+  if (2 < nks) issue(B2{}, 2);
+  auto step = [&](auto bufc, int ks) {
+    constexpr int buf = decltype(bufc)::value;
+    using BI = std::integral_constant<int, (buf + NST - 1) % NST>;
+    // stage ks landed once at most the later stages' instructions are outstanding
+    if (ks + 2 < nks) wait_vmcnt<2 * PERW>();
+    else if (ks + 1 < nks) wait_vmcnt<PERW>();
+    else wait_vmcnt<0>();
+    lds_barrier();
+    // the buffer of stage ks-1 is free (every wavefront passed this barrier after using it)
+    if (ks + NST - 1 < nks) issue(BI{}, ks + NST - 1);
+    compute(bufc, ks);
+  };
+  for (int ks = 0; ks < nks; ks += NST) {
+    step(B0{}, ks);
+    if (ks + 1 < nks) step(B1{}, ks + 1);
+    if (ks + 2 < nks) step(B2{}, ks + 2);
+    if (ks + 3 < nks) step(B3{}, ks + 3);
   }
-  // acc[i][j][r] = C[m0 + wm*WM + 32i + 8(r/4) + 4hl + r%4][n0 + wn*WN + 32j + l32]
+  __syncthreads();  // every wavefront is done with the ring; reuse it for the epilogue
+
+  // epilogue: each wavefront stages its WM x WN fp32 tile (bias and SiLU applied) in its
+  // own ring buffer, then writes 16-byte row segments (residual added there)
+  constexpr int EP = G::WN + 4;  // padded fp32 row
+  static_assert(G::WM * EP * 4 <= STAGE * 2, "epilogue tile fits one ring buffer");
+  float* E = (float*)(w == 0 ? S0 : w == 1 ? S1 : w == 2 ? S2 : S3);
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
-    const int n = n0 + wn * WN + 32 * j + l32;
-    if (n >= N) continue;
-    const float bn = bias ? bias[n] : 0.f;
+    const int nl = 32 * j + l32;
+    const int n = n0 + wn * G::WN + nl;
+    const float bn = (bias && n < N) ? bias[n] : 0.f;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t m = m0 + wm * WM + 32 * i + 8 * (r >> 2) + 4 * hl + (r & 3);
-        if (m >= M) continue;
+        const int ml = 32 * i + 8 * (r >> 2) + 4 * hl + (r & 3);
         float y = acc[i][j][r] + bn;
         if (silu) y = silu_fast(y);
-        if (R) y += (float)R[m * ldr + n];
-        C[m * ldc + n] = from_f32<OutT>(y);
+        E[ml * EP + nl] = y;
       }
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): own LDS writes done (same wavefront reads)
+  constexpr int SEGS = G::WM * (G::WN / 8);  // 8-column segments
+#pragma unroll
+  for (int s = lane; s < SEGS; s += 64) {
+    const int ml = s / (G::WN / 8), cs = s % (G::WN / 8);
+    const int64_t m = m0 + wm * G::WM + ml;
+    const int n = n0 + wn * G::WN + 8 * cs;
+    if (m >= M || n >= N) continue;
+    const f32x4 lo = *reinterpret_cast<const f32x4*>(&E[ml * EP + 8 * cs]);
+    const f32x4 hi = *reinterpret_cast<const f32x4*>(&E[ml * EP + 8 * cs + 4]);
+    float y[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    if (R) {
+      const bf16x8 rv = *reinterpret_cast<const bf16x8*>(&R[m * ldr + n]);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) y[q] += (float)rv[q];
+    }
+    bf16x8 o;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) o[q] = (bf16)y[q];
+    *reinterpret_cast<bf16x8*>(&C[m * ldc + n]) = o;
   }
 }
 
@@ -226,18 +289,22 @@ hipError_t launch_gemm(const void* A, int64_t lda, const void* W, int64_t ldw, c
                        int silu, int bf16flag, hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
   if (bf16flag) {
+    // the DMA and the epilogue move 16-byte rows segments
+    if (N % 8 != 0 || K % 8 != 0 || lda % 8 != 0 || ldw % 8 != 0 || ldc % 8 != 0 ||
+        (R && ldr % 8 != 0))
+      return hipErrorInvalidValue;
     // 128x128 tiles when they give at least ~one workgroup per compute unit, else 64x64
     const int64_t big = ((N + 127) / 128) * ((M + 127) / 128);
     if (big >= 256) {
-      const dim3 grid((unsigned)((N + 127) / 128), (unsigned)((M + 127) / 128));
-      hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, bf16>), grid, dim3(256), 0, s, (const bf16*)A,
-                         lda, (const bf16*)W, ldw, bias, (const bf16*)R, ldr, (bf16*)C, ldc, M, N,
-                         K, silu);
+      const int tn = (N + 127) / 128, tm = (int)((M + 127) / 128);
+      hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, bf16>), dim3(tn * tm), dim3(256), 0, s,
+                         (const bf16*)A, lda, (const bf16*)W, ldw, bias, (const bf16*)R, ldr,
+                         (bf16*)C, ldc, M, N, K, silu, tn, tn * tm);
     } else {
-      const dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 63) / 64));
-      hipLaunchKernelGGL((gemm_bf16_kernel<64, 64, bf16>), grid, dim3(256), 0, s, (const bf16*)A,
-                         lda, (const bf16*)W, ldw, bias, (const bf16*)R, ldr, (bf16*)C, ldc, M, N,
-                         K, silu);
+      const int tn = (N + 63) / 64, tm = (int)((M + 63) / 64);
+      hipLaunchKernelGGL((gemm_bf16_kernel<64, 64, bf16>), dim3(tn * tm), dim3(256), 0, s,
+                         (const bf16*)A, lda, (const bf16*)W, ldw, bias, (const bf16*)R, ldr,
+                         (bf16*)C, ldc, M, N, K, silu, tn, tn * tm);
     }
   } else {
     const dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 63) / 64));
