@@ -307,43 +307,72 @@ hstu_status layer_once(const hstu_layer_desc* d, const int64_t* off_dev, const i
 }
 
 // ---------------------------------------------------------------- M-FALCON
+// The history pass of M-FALCON produces a cache that the candidate pass reads:
+// per layer, the f1 output over the history (its K and V columns are the keys
+// and values the candidates attend to), and the per-32-key timestamp ranges.
+// mfalcon_score runs both passes with the cache inside its workspace;
+// mfalcon_history and mfalcon_score_cached let a caller keep the cache across
+// requests for the same users.
 struct MfPlan {
   Jagged hist;
   int64_t cand_total = 0;
   int kv_splits = 1;          // key-range splits of the candidate attention (MFMA kernel only)
   int64_t keys_per_split = 0;
-  size_t ws = 0;
+  size_t cache = 0;           // bytes of the history cache
+  size_t hist_ws = 0;         // history-pass workspace
+  size_t cand_ws = 0;         // candidate-pass workspace
 };
 
 constexpr int64_t kKeysPerSplit = 512;  // history keys per candidate-attention workgroup
 constexpr int kMaxSplits = 16;
 
-struct MfBufs {
-  LayerBufs hist;             // history scratch (items, uvqk of the current layer unused)
-  std::vector<void*> hist_uvqk;  // per layer f1 output over the history (cached K and V)
+struct MfCache {
+  std::vector<void*> uvqk;  // per layer f1 output over the history [n_h, f1] (K/V cache)
+  KeyRange* kr;             // timestamp ranges of the history keys (MFMA kernel), else NULL
+};
+struct MfHistBufs {
+  int2* items;
+  float* o;
+  void* g;
   void* hx[2];
+};
+struct MfCandBufs {
   void* c_uvqk;
   float* c_o;
   void* c_g;
   void* cx[2];
 };
 
-void carve_mfalcon(Carver& c, const mfalcon_desc* d, const MfPlan& p, MfBufs* b) {
+void carve_cache(Carver& c, const mfalcon_desc* d, const MfPlan& p, MfCache* b) {
+  const hstu_layer_desc& ld = d->layer;
+  const hstu_attn_desc& a = ld.attn;
+  const int64_t f1 = 2LL * a.num_heads * (a.d_v + a.d_qk);
+  const int64_t nh = p.hist.total;
+  b->uvqk.assign(ld.num_layers, nullptr);
+  for (int l = 0; l < ld.num_layers; ++l) b->uvqk[l] = c.take((size_t)nh * f1 * elt_size(a.dtype));
+  b->kr = (KeyRange*)c.take(key_range_bytes(&a, nh));
+}
+
+void carve_hist_ws(Carver& c, const mfalcon_desc* d, const MfPlan& p, MfHistBufs* b) {
+  const hstu_layer_desc& ld = d->layer;
+  const hstu_attn_desc& a = ld.attn;
+  const size_t es = elt_size(a.dtype);
+  const int64_t hv = (int64_t)a.num_heads * a.d_v;
+  const int64_t nh = p.hist.total;
+  b->items = (int2*)c.take((size_t)p.hist.items * sizeof(int2));
+  b->o = (float*)c.take((size_t)nh * hv * sizeof(float));
+  b->g = c.take((size_t)nh * hv * es);
+  b->hx[0] = ld.num_layers > 1 ? c.take((size_t)nh * ld.d_model * es) : nullptr;
+  b->hx[1] = ld.num_layers > 2 ? c.take((size_t)nh * ld.d_model * es) : nullptr;
+}
+
+void carve_cand_ws(Carver& c, const mfalcon_desc* d, const MfPlan& p, MfCandBufs* b) {
   const hstu_layer_desc& ld = d->layer;
   const hstu_attn_desc& a = ld.attn;
   const size_t es = elt_size(a.dtype);
   const int64_t f1 = 2LL * a.num_heads * (a.d_v + a.d_qk);
   const int64_t hv = (int64_t)a.num_heads * a.d_v;
-  const int64_t nh = p.hist.total;
   const int64_t m = std::min<int64_t>(d->microbatch, std::max<int64_t>(p.cand_total, 1));
-  b->hist.items = (int2*)c.take((size_t)p.hist.items * sizeof(int2));
-  b->hist.kr = (KeyRange*)c.take(key_range_bytes(&a, nh));
-  b->hist.o = (float*)c.take((size_t)nh * hv * sizeof(float));
-  b->hist.g = c.take((size_t)nh * hv * es);
-  b->hist_uvqk.assign(ld.num_layers, nullptr);
-  for (int l = 0; l < ld.num_layers; ++l) b->hist_uvqk[l] = c.take((size_t)nh * f1 * es);
-  b->hx[0] = ld.num_layers > 1 ? c.take((size_t)nh * ld.d_model * es) : nullptr;
-  b->hx[1] = ld.num_layers > 2 ? c.take((size_t)nh * ld.d_model * es) : nullptr;
   b->c_uvqk = c.take((size_t)m * f1 * es);
   b->c_o = (float*)c.take((size_t)p.kv_splits * m * hv * sizeof(float));
   b->c_g = c.take((size_t)m * hv * es);
@@ -351,6 +380,7 @@ void carve_mfalcon(Carver& c, const mfalcon_desc* d, const MfPlan& p, MfBufs* b)
   b->cx[1] = ld.num_layers > 2 ? c.take((size_t)m * ld.d_model * es) : nullptr;
 }
 
+// The history half of the plan (cand offsets may be NULL: then no candidate sizes).
 hstu_status plan_mfalcon(const mfalcon_desc* d, const int64_t* hoff, const int64_t* coff,
                          MfPlan* p) {
   if (!d) return fail(HSTU_INVALID_ARGUMENT, "descriptor is NULL");
@@ -360,22 +390,23 @@ hstu_status plan_mfalcon(const mfalcon_desc* d, const int64_t* hoff, const int64
   const hstu_attn_desc& a = d->layer.attn;
   st = check_offsets(hoff, a.batch, a.max_seq_len, attn_tile_rows(&a), "hist_offsets", &p->hist);
   if (st) return st;
-  Jagged cj;
-  st = check_offsets(coff, a.batch, -1, 1, "cand_offsets", &cj);
-  if (st) return st;
-  for (int b = 0; b < a.batch; ++b) {
-    const int64_t nh = hoff[b + 1] - hoff[b], nc = coff[b + 1] - coff[b];
-    if (nc > 0 && nh + 1 > a.max_seq_len)
-      return fail(HSTU_INVALID_ARGUMENT,
-                  "user %d: history %lld plus the candidate exceeds max_seq_len %d", b,
-                  (long long)nh, a.max_seq_len);
+  if (coff) {
+    Jagged cj;
+    st = check_offsets(coff, a.batch, -1, 1, "cand_offsets", &cj);
+    if (st) return st;
+    for (int b = 0; b < a.batch; ++b) {
+      const int64_t nh = hoff[b + 1] - hoff[b], nc = coff[b + 1] - coff[b];
+      if (nc > 0 && nh + 1 > a.max_seq_len)
+        return fail(HSTU_INVALID_ARGUMENT,
+                    "user %d: history %lld plus the candidate exceeds max_seq_len %d", b,
+                    (long long)nh, a.max_seq_len);
+    }
+    p->cand_total = cj.total;
   }
-  p->cand_total = cj.total;
   // The MFMA kernel splits the history into key ranges of kKeysPerSplit (more when
   // the history is long), so that a microbatch of ~1k candidates still fills the
   // device. The geometry depends on the history lengths only.
-  if (attn_mfma_supported(a.dtype == HSTU_BF16, a.d_qk, a.d_v, a.num_pos_buckets,
-                          a.num_time_buckets) && p->hist.max_len > kKeysPerSplit) {
+  if (uses_mfma(&a) && p->hist.max_len > kKeysPerSplit) {
     p->kv_splits = (int)std::min<int64_t>(kMaxSplits,
                                           (p->hist.max_len + kKeysPerSplit - 1) / kKeysPerSplit);
     p->keys_per_split = ((p->hist.max_len + p->kv_splits - 1) / p->kv_splits + 63) / 64 * 64;
@@ -383,9 +414,169 @@ hstu_status plan_mfalcon(const mfalcon_desc* d, const int64_t* hoff, const int64
   if ((int64_t)p->hist.items * a.num_heads >= (int64_t(1) << 31))
     return fail(HSTU_UNSUPPORTED, "too many history tiles for one launch");
   Carver c{nullptr};
-  MfBufs b;
-  carve_mfalcon(c, d, *p, &b);
-  p->ws = c.off;
+  MfCache cb;
+  carve_cache(c, d, *p, &cb);
+  p->cache = c.off;
+  Carver h{nullptr};
+  MfHistBufs hb;
+  carve_hist_ws(h, d, *p, &hb);
+  p->hist_ws = h.off;
+  Carver k{nullptr};
+  MfCandBufs kb;
+  carve_cand_ws(k, d, *p, &kb);
+  p->cand_ws = k.off;
+  return HSTU_OK;
+}
+
+hstu_status check_ws(const void* ws, size_t have, size_t need, const char* what) {
+  if (have < need || (!ws && need))
+    return fail(HSTU_WORKSPACE_TOO_SMALL, "%s needs %zu bytes (got %zu)", what, need, have);
+  if (((uintptr_t)ws & (kAlign - 1)) != 0)
+    return fail(HSTU_INVALID_ARGUMENT, "%s must be 256-byte aligned", what);
+  return HSTU_OK;
+}
+
+// History pass: layers 0..L-2 in full; layer L-1 only needs its K and V. Every
+// layer's f1 output stays in the cache.
+hstu_status run_history(const mfalcon_desc* d, const MfPlan& p, const int64_t* hist_offsets,
+                        const int64_t* hist_ts, const void* hist_x,
+                        const hstu_layer_weights* weights, const MfCache& cache,
+                        const MfHistBufs& hb, hipStream_t s) {
+  if (p.hist.total == 0) return HSTU_OK;
+  const hstu_layer_desc& ld = d->layer;
+  const int L = ld.num_layers;
+  LayerBufs lb{};
+  lb.items = hb.items;
+  lb.kr = cache.kr;
+  lb.o = hb.o;
+  lb.g = hb.g;
+  // the history's work items (layers 0..L-2) and key ranges (every layer, candidates included)
+  hstu_status st = plan_causal(ld.attn, hist_offsets, hist_ts, p.hist, lb, s);
+  if (st) return st;
+  const void* in = hist_x;
+  for (int l = 0; l < L; ++l) {
+    lb.uvqk = cache.uvqk[l];
+    void* out = (l < L - 1) ? hb.hx[l % 2] : nullptr;
+    st = layer_once(&ld, hist_offsets, hist_ts, p.hist, in, weights[l], out, lb, s, l == L - 1);
+    if (st) return st;
+    in = out;
+  }
+  return HSTU_OK;
+}
+
+// Candidate microbatches, in global candidate order, against a history cache.
+hstu_status run_candidates(const mfalcon_desc* d, const MfPlan& p, const int64_t* hist_offsets,
+                           const int64_t* hist_ts, const MfCache& cache,
+                           const int64_t* cand_offsets_host, const int64_t* cand_offsets,
+                           const int64_t* cand_ts, const void* cand_x,
+                           const hstu_layer_weights* weights, const float* w_head, void* cand_out,
+                           float* cand_logit, const MfCandBufs& b, hipStream_t s) {
+  const hstu_layer_desc& ld = d->layer;
+  const hstu_attn_desc& a = ld.attn;
+  const int L = ld.num_layers;
+  const int bf = a.dtype == HSTU_BF16;
+  const size_t es = elt_size(a.dtype);
+  const int hv = a.num_heads * a.d_v;
+  const int dm = ld.d_model;
+  const int B = a.batch;
+  const int64_t m = d->microbatch;
+  for (int64_t m0 = 0; m0 < p.cand_total; m0 += m) {
+    const int64_t m1 = std::min(m0 + m, p.cand_total);
+    const int64_t rows = m1 - m0;
+    // users whose candidate range overlaps [m0, m1)
+    int ub = (int)(std::upper_bound(cand_offsets_host, cand_offsets_host + B + 1, m0) -
+                   cand_offsets_host) - 1;
+    int ue = (int)(std::lower_bound(cand_offsets_host, cand_offsets_host + B + 1, m1) -
+                   cand_offsets_host);  // one past the last overlapping user
+    ub = std::max(ub, 0);
+    ue = std::min(ue, B);
+    int64_t max_rows = 0;
+    for (int u = ub; u < ue; ++u) {
+      const int64_t cs = std::max(cand_offsets_host[u], m0), ce = std::min(cand_offsets_host[u + 1], m1);
+      max_rows = std::max(max_rows, ce - cs);
+    }
+    const void* in = (const char*)cand_x + (size_t)m0 * dm * es;
+    for (int l = 0; l < L; ++l) {
+      const hstu_layer_weights& w = weights[l];
+      void* out = (l == L - 1) ? (void*)((char*)cand_out + (size_t)m0 * dm * es) : b.cx[l % 2];
+      const int64_t f1 = 2LL * a.num_heads * (a.d_v + a.d_qk);
+      HSTU_TRY(launch_gemm(in, dm, w.w1, dm, w.b1, nullptr, 0, b.c_uvqk, f1, rows, (int)f1, dm, 1,
+                           bf, s),
+               "candidate f1 projection");
+      const UVQK cv = split_view(b.c_uvqk, a);
+      const UVQK hvw = split_view(cache.uvqk[l], a);
+      AttnArgs aa = base_args(&a);
+      aa.q = cv.q;
+      aa.ld_q = cv.ld;
+      aa.kc = cv.k;
+      aa.vc = cv.v;
+      aa.ld_kc = aa.ld_vc = cv.ld;
+      aa.k = hvw.k;
+      aa.v = hvw.v;
+      aa.ld_k = aa.ld_v = hvw.ld;
+      aa.out = b.c_o;
+      aa.ld_o = hv;
+      aa.out_f32 = 1;
+      aa.q_offsets = cand_offsets;
+      aa.k_offsets = hist_offsets;
+      aa.ts_q = cand_ts;
+      aa.ts_k = hist_ts;
+      aa.rab_pos = w.rab_pos;
+      aa.rab_time = w.rab_time;
+      aa.key_ranges = (hist_ts && w.rab_time) ? cache.kr : nullptr;  // unread when no history
+      aa.row_begin = m0;
+      aa.row_end = m1;
+      aa.max_user_rows = max_rows;
+      // key-range splits of the history: fixed by the history lengths alone, so a
+      // candidate's reduction order never depends on the microbatch around it
+      aa.kv_splits = p.kv_splits;
+      aa.keys_per_split = p.keys_per_split;
+      aa.part_stride = rows * hv;
+      for (int u0 = ub; u0 < ue; u0 += 65535) {
+        aa.user_begin = u0;
+        aa.n_users = std::min(ue - u0, 65535);
+        HSTU_TRY(run_attention(&a, aa, true, s), "candidate attention");
+      }
+      HSTU_TRY(launch_ln_gate(b.c_o, hv, aa.kv_splits, aa.part_stride, cv.u, cv.ld, w.ln_gamma,
+                              w.ln_beta, a.ln_eps, b.c_g, hv, rows, hv, bf, s),
+               "candidate layer norm gate");
+      HSTU_TRY(launch_gemm(b.c_g, hv, w.w2, hv, w.b2, ld.residual ? in : nullptr, dm, out, dm, rows,
+                           dm, hv, 0, bf, s),
+               "candidate f2 projection");
+      in = out;
+    }
+    if (cand_logit)
+      HSTU_TRY(launch_rowdot((const char*)cand_out + (size_t)m0 * dm * es, dm, w_head,
+                             cand_logit + m0, rows, dm, bf, s),
+               "candidate logit");
+  }
+  return HSTU_OK;
+}
+
+hstu_status check_history_args(const hstu_layer_weights* weights, int L, const MfPlan& p,
+                               const void* hist_offsets, const void* hist_x) {
+  hstu_status st = check_weights(weights, L);
+  if (st) return st;
+  if (p.hist.total > 0 && (!hist_offsets || !hist_x))
+    return fail(HSTU_INVALID_ARGUMENT, "hist_offsets and hist_x are required");
+  if (hist_x && !aligned16(hist_x))
+    return fail(HSTU_INVALID_ARGUMENT, "activation pointers must be 16-byte aligned");
+  return HSTU_OK;
+}
+
+hstu_status check_candidate_args(const MfPlan& p, const int64_t* hist_offsets,
+                                 const int64_t* hist_ts, const int64_t* cand_offsets,
+                                 const int64_t* cand_ts, const void* cand_x, const void* cand_out,
+                                 const float* cand_logit, const float* w_head) {
+  if ((hist_ts == nullptr) != (cand_ts == nullptr))
+    return fail(HSTU_INVALID_ARGUMENT, "hist_ts and cand_ts must both be set or both be NULL");
+  if (!hist_offsets || !cand_offsets)
+    return fail(HSTU_INVALID_ARGUMENT, "device offsets are required");
+  if (!cand_x || !cand_out) return fail(HSTU_INVALID_ARGUMENT, "cand_x and cand_out are required");
+  if (!aligned16(cand_x) || !aligned16(cand_out))
+    return fail(HSTU_INVALID_ARGUMENT, "activation pointers must be 16-byte aligned");
+  if (cand_logit && !w_head) return fail(HSTU_INVALID_ARGUMENT, "cand_logit needs w_head");
+  (void)p;
   return HSTU_OK;
 }
 
@@ -525,10 +716,11 @@ hstu_status hstu_layer_fwd(const hstu_layer_desc* desc, const int64_t* seq_offse
 hstu_status mfalcon_workspace_size(const mfalcon_desc* desc, const int64_t* hist_offsets_host,
                                    const int64_t* cand_offsets_host, size_t* bytes) {
   if (!bytes) return fail(HSTU_INVALID_ARGUMENT, "bytes is NULL");
+  if (!cand_offsets_host) return fail(HSTU_INVALID_ARGUMENT, "cand_offsets_host is NULL");
   MfPlan p;
   hstu_status st = plan_mfalcon(desc, hist_offsets_host, cand_offsets_host, &p);
   if (st) return st;
-  *bytes = p.ws;
+  *bytes = align_up(p.cache) + align_up(p.hist_ws) + align_up(p.cand_ws);
   return HSTU_OK;
 }
 
@@ -539,128 +731,119 @@ hstu_status mfalcon_score(const mfalcon_desc* desc, const int64_t* hist_offsets_
                           const hstu_layer_weights* weights, const float* w_head,
                           void* cand_out, float* cand_logit, void* workspace,
                           size_t workspace_bytes, void* stream) {
+  if (!cand_offsets_host) return fail(HSTU_INVALID_ARGUMENT, "cand_offsets_host is NULL");
   MfPlan p;
   hstu_status st = plan_mfalcon(desc, hist_offsets_host, cand_offsets_host, &p);
   if (st) return st;
-  const hstu_layer_desc& ld = desc->layer;
-  const hstu_attn_desc& a = ld.attn;
-  if ((st = check_weights(weights, ld.num_layers))) return st;
+  if ((st = check_weights(weights, desc->layer.num_layers))) return st;
+  if (p.cand_total == 0) {
+    if ((hist_ts == nullptr) != (cand_ts == nullptr))
+      return fail(HSTU_INVALID_ARGUMENT, "hist_ts and cand_ts must both be set or both be NULL");
+    return HSTU_OK;
+  }
+  if ((st = check_candidate_args(p, hist_offsets, hist_ts, cand_offsets, cand_ts, cand_x, cand_out,
+                                 cand_logit, w_head)))
+    return st;
+  if ((st = check_history_args(weights, desc->layer.num_layers, p, hist_offsets, hist_x))) return st;
+  const size_t need = align_up(p.cache) + align_up(p.hist_ws) + align_up(p.cand_ws);
+  if ((st = check_ws(workspace, workspace_bytes, need, "workspace"))) return st;
+  hipStream_t s = (hipStream_t)stream;
+  Carver c{(char*)workspace};
+  MfCache cache;
+  carve_cache(c, desc, p, &cache);
+  c.off = align_up(p.cache);
+  MfHistBufs hb;
+  carve_hist_ws(c, desc, p, &hb);
+  c.off = align_up(p.cache) + align_up(p.hist_ws);
+  MfCandBufs cb;
+  carve_cand_ws(c, desc, p, &cb);
+  if ((st = run_history(desc, p, hist_offsets, hist_ts, hist_x, weights, cache, hb, s))) return st;
+  return run_candidates(desc, p, hist_offsets, hist_ts, cache, cand_offsets_host, cand_offsets,
+                        cand_ts, cand_x, weights, w_head, cand_out, cand_logit, cb, s);
+}
+
+hstu_status mfalcon_cache_size(const mfalcon_desc* desc, const int64_t* hist_offsets_host,
+                               size_t* bytes) {
+  if (!bytes) return fail(HSTU_INVALID_ARGUMENT, "bytes is NULL");
+  MfPlan p;
+  hstu_status st = plan_mfalcon(desc, hist_offsets_host, nullptr, &p);
+  if (st) return st;
+  *bytes = p.cache;
+  return HSTU_OK;
+}
+
+hstu_status mfalcon_history_workspace_size(const mfalcon_desc* desc,
+                                           const int64_t* hist_offsets_host, size_t* bytes) {
+  if (!bytes) return fail(HSTU_INVALID_ARGUMENT, "bytes is NULL");
+  MfPlan p;
+  hstu_status st = plan_mfalcon(desc, hist_offsets_host, nullptr, &p);
+  if (st) return st;
+  *bytes = p.hist_ws;
+  return HSTU_OK;
+}
+
+hstu_status mfalcon_history(const mfalcon_desc* desc, const int64_t* hist_offsets_host,
+                            const int64_t* hist_offsets, const int64_t* hist_ts,
+                            const void* hist_x, const hstu_layer_weights* weights, void* cache,
+                            size_t cache_bytes, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  MfPlan p;
+  hstu_status st = plan_mfalcon(desc, hist_offsets_host, nullptr, &p);
+  if (st) return st;
+  if ((st = check_history_args(weights, desc->layer.num_layers, p, hist_offsets, hist_x))) return st;
+  if ((st = check_ws(cache, cache_bytes, p.cache, "cache"))) return st;
+  if ((st = check_ws(workspace, workspace_bytes, p.hist_ws, "workspace"))) return st;
+  Carver c{(char*)cache};
+  MfCache cb;
+  carve_cache(c, desc, p, &cb);
+  Carver w{(char*)workspace};
+  MfHistBufs hb;
+  carve_hist_ws(w, desc, p, &hb);
+  return run_history(desc, p, hist_offsets, hist_ts, hist_x, weights, cb, hb, (hipStream_t)stream);
+}
+
+hstu_status mfalcon_cached_workspace_size(const mfalcon_desc* desc,
+                                          const int64_t* hist_offsets_host,
+                                          const int64_t* cand_offsets_host, size_t* bytes) {
+  if (!bytes) return fail(HSTU_INVALID_ARGUMENT, "bytes is NULL");
+  if (!cand_offsets_host) return fail(HSTU_INVALID_ARGUMENT, "cand_offsets_host is NULL");
+  MfPlan p;
+  hstu_status st = plan_mfalcon(desc, hist_offsets_host, cand_offsets_host, &p);
+  if (st) return st;
+  *bytes = p.cand_ws;
+  return HSTU_OK;
+}
+
+hstu_status mfalcon_score_cached(const mfalcon_desc* desc, const int64_t* hist_offsets_host,
+                                 const int64_t* hist_offsets, const int64_t* hist_ts,
+                                 const void* cache, size_t cache_bytes,
+                                 const int64_t* cand_offsets_host, const int64_t* cand_offsets,
+                                 const int64_t* cand_ts, const void* cand_x,
+                                 const hstu_layer_weights* weights, const float* w_head,
+                                 void* cand_out, float* cand_logit, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  if (!cand_offsets_host) return fail(HSTU_INVALID_ARGUMENT, "cand_offsets_host is NULL");
+  MfPlan p;
+  hstu_status st = plan_mfalcon(desc, hist_offsets_host, cand_offsets_host, &p);
+  if (st) return st;
+  if ((st = check_weights(weights, desc->layer.num_layers))) return st;
   if ((hist_ts == nullptr) != (cand_ts == nullptr))
     return fail(HSTU_INVALID_ARGUMENT, "hist_ts and cand_ts must both be set or both be NULL");
   if (p.cand_total == 0) return HSTU_OK;
-  if (!hist_offsets || !cand_offsets)
-    return fail(HSTU_INVALID_ARGUMENT, "device offsets are required");
-  if (!cand_x || !cand_out || (p.hist.total > 0 && !hist_x))
-    return fail(HSTU_INVALID_ARGUMENT, "hist_x, cand_x and cand_out are required");
-  if (!aligned16(cand_x) || !aligned16(cand_out) || (hist_x && !aligned16(hist_x)))
-    return fail(HSTU_INVALID_ARGUMENT, "activation pointers must be 16-byte aligned");
-  if (cand_logit && !w_head) return fail(HSTU_INVALID_ARGUMENT, "cand_logit needs w_head");
-  if (workspace_bytes < p.ws || (!workspace && p.ws))
-    return fail(HSTU_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes (got %zu)", p.ws,
-                workspace_bytes);
-  if (((uintptr_t)workspace & (kAlign - 1)) != 0)
-    return fail(HSTU_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
-  hipStream_t s = (hipStream_t)stream;
-  Carver c{(char*)workspace};
-  MfBufs b;
-  carve_mfalcon(c, desc, p, &b);
-  const int L = ld.num_layers;
-  const int bf = a.dtype == HSTU_BF16;
-  const size_t es = elt_size(a.dtype);
-  const int hv = a.num_heads * a.d_v;
-  const int dm = ld.d_model;
-
-  // history pass, once: layers 0..L-2 in full; layer L-1 only needs its K and V
-  if (p.hist.total > 0) {
-    LayerBufs hb = b.hist;
-    // the history's work items (layers 0..L-2) and key ranges (every layer,
-    // candidates included)
-    if ((st = plan_causal(a, hist_offsets, hist_ts, p.hist, hb, s))) return st;
-    const void* in = hist_x;
-    for (int l = 0; l < L; ++l) {
-      hb.uvqk = b.hist_uvqk[l];
-      void* out = (l < L - 1) ? b.hx[l % 2] : nullptr;
-      st = layer_once(&ld, hist_offsets, hist_ts, p.hist, in, weights[l], out, hb, s,
-                      l == L - 1);
-      if (st) return st;
-      in = out;
-    }
-  }
-
-  // candidate microbatches, in global candidate order
-  const int B = a.batch;
-  const int64_t m = desc->microbatch;
-  for (int64_t m0 = 0; m0 < p.cand_total; m0 += m) {
-    const int64_t m1 = std::min(m0 + m, p.cand_total);
-    const int64_t rows = m1 - m0;
-    // users whose candidate range overlaps [m0, m1)
-    int ub = (int)(std::upper_bound(cand_offsets_host, cand_offsets_host + B + 1, m0) -
-                   cand_offsets_host) - 1;
-    int ue = (int)(std::lower_bound(cand_offsets_host, cand_offsets_host + B + 1, m1) -
-                   cand_offsets_host);  // one past the last overlapping user
-    ub = std::max(ub, 0);
-    ue = std::min(ue, B);
-    int64_t max_rows = 0;
-    for (int u = ub; u < ue; ++u) {
-      const int64_t cs = std::max(cand_offsets_host[u], m0), ce = std::min(cand_offsets_host[u + 1], m1);
-      max_rows = std::max(max_rows, ce - cs);
-    }
-    const void* in = (const char*)cand_x + (size_t)m0 * dm * es;
-    for (int l = 0; l < L; ++l) {
-      const hstu_layer_weights& w = weights[l];
-      void* out = (l == L - 1) ? (void*)((char*)cand_out + (size_t)m0 * dm * es) : b.cx[l % 2];
-      const int64_t f1 = 2LL * a.num_heads * (a.d_v + a.d_qk);
-      HSTU_TRY(launch_gemm(in, dm, w.w1, dm, w.b1, nullptr, 0, b.c_uvqk, f1, rows, (int)f1, dm, 1,
-                           bf, s),
-               "candidate f1 projection");
-      const UVQK cv = split_view(b.c_uvqk, a);
-      const UVQK hvw = split_view(b.hist_uvqk[l], a);
-      AttnArgs aa = base_args(&a);
-      aa.q = cv.q;
-      aa.ld_q = cv.ld;
-      aa.kc = cv.k;
-      aa.vc = cv.v;
-      aa.ld_kc = aa.ld_vc = cv.ld;
-      aa.k = hvw.k;
-      aa.v = hvw.v;
-      aa.ld_k = aa.ld_v = hvw.ld;
-      aa.out = b.c_o;
-      aa.ld_o = hv;
-      aa.out_f32 = 1;
-      aa.q_offsets = cand_offsets;
-      aa.k_offsets = hist_offsets;
-      aa.ts_q = cand_ts;
-      aa.ts_k = hist_ts;
-      aa.rab_pos = w.rab_pos;
-      aa.rab_time = w.rab_time;
-      aa.key_ranges = (hist_ts && w.rab_time) ? b.hist.kr : nullptr;  // unread when no history
-      aa.row_begin = m0;
-      aa.row_end = m1;
-      aa.max_user_rows = max_rows;
-      // key-range splits of the history: fixed by the history lengths alone, so a
-      // candidate's reduction order never depends on the microbatch around it
-      aa.kv_splits = p.kv_splits;
-      aa.keys_per_split = p.keys_per_split;
-      aa.part_stride = rows * hv;
-      for (int u0 = ub; u0 < ue; u0 += 65535) {
-        aa.user_begin = u0;
-        aa.n_users = std::min(ue - u0, 65535);
-        HSTU_TRY(run_attention(&a, aa, true, s), "candidate attention");
-      }
-      HSTU_TRY(launch_ln_gate(b.c_o, hv, aa.kv_splits, aa.part_stride, cv.u, cv.ld, w.ln_gamma,
-                              w.ln_beta, a.ln_eps, b.c_g, hv, rows, hv, bf, s),
-               "candidate layer norm gate");
-      HSTU_TRY(launch_gemm(b.c_g, hv, w.w2, hv, w.b2, ld.residual ? in : nullptr, dm, out, dm, rows,
-                           dm, hv, 0, bf, s),
-               "candidate f2 projection");
-      in = out;
-    }
-    if (cand_logit)
-      HSTU_TRY(launch_rowdot((const char*)cand_out + (size_t)m0 * dm * es, dm, w_head,
-                             cand_logit + m0, rows, dm, bf, s),
-               "candidate logit");
-  }
-  return HSTU_OK;
+  if ((st = check_candidate_args(p, hist_offsets, hist_ts, cand_offsets, cand_ts, cand_x, cand_out,
+                                 cand_logit, w_head)))
+    return st;
+  if ((st = check_ws(cache, cache_bytes, p.cache, "cache"))) return st;
+  if ((st = check_ws(workspace, workspace_bytes, p.cand_ws, "workspace"))) return st;
+  Carver c{(char*)const_cast<void*>(cache)};
+  MfCache cb;
+  carve_cache(c, desc, p, &cb);
+  Carver w{(char*)workspace};
+  MfCandBufs kb;
+  carve_cand_ws(w, desc, p, &kb);
+  return run_candidates(desc, p, hist_offsets, hist_ts, cb, cand_offsets_host, cand_offsets,
+                        cand_ts, cand_x, weights, w_head, cand_out, cand_logit, kb,
+                        (hipStream_t)stream);
 }
 
 hstu_status hstu_debug_buckets(const hstu_attn_desc* desc, const int64_t* seq_offsets_host,

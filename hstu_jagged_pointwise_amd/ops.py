@@ -69,6 +69,16 @@ _sig = {
     "mfalcon_score": ([ctypes.POINTER(mfalcon_desc), _I64P, _P, _P, _P, _I64P, _P, _P, _P,
                        ctypes.POINTER(hstu_layer_weights), _P, _P, _P, _P, ctypes.c_size_t, _P],
                       ctypes.c_int),
+    "mfalcon_cache_size": ([ctypes.POINTER(mfalcon_desc), _I64P, _SZP], ctypes.c_int),
+    "mfalcon_history_workspace_size": ([ctypes.POINTER(mfalcon_desc), _I64P, _SZP], ctypes.c_int),
+    "mfalcon_history": ([ctypes.POINTER(mfalcon_desc), _I64P, _P, _P, _P,
+                         ctypes.POINTER(hstu_layer_weights), _P, ctypes.c_size_t, _P,
+                         ctypes.c_size_t, _P], ctypes.c_int),
+    "mfalcon_cached_workspace_size": ([ctypes.POINTER(mfalcon_desc), _I64P, _I64P, _SZP],
+                                      ctypes.c_int),
+    "mfalcon_score_cached": ([ctypes.POINTER(mfalcon_desc), _I64P, _P, _P, _P, ctypes.c_size_t,
+                              _I64P, _P, _P, _P, ctypes.POINTER(hstu_layer_weights), _P, _P, _P,
+                              _P, ctypes.c_size_t, _P], ctypes.c_int),
     "hstu_debug_buckets": ([ctypes.POINTER(hstu_attn_desc), _I64P, _P, _P, ctypes.c_int32, _P, _P,
                             _P], ctypes.c_int),
 }
@@ -262,6 +272,68 @@ def mfalcon_score(hist_offsets, hist_ts, hist_x, cand_offsets, cand_ts, cand_x,
                              _ptr(hist_x), _i64p(ch), _ptr(cand_offsets), _ptr(cand_ts),
                              _ptr(cand_x), arr, _ptr(w_head), _ptr(out), _ptr(logit), _ptr(ws),
                              nbytes, _stream(stream)))
+    return out, logit
+
+
+def _mf_desc(layers, n_users, cand_or_hist_x, *, num_heads, d_qk, d_v, max_seq_len, microbatch,
+             ln_eps, residual):
+    ld = layer_desc(layers, n_users, num_heads, d_qk, d_v, cand_or_hist_x.shape[1], max_seq_len,
+                    _dtype_code(cand_or_hist_x), ln_eps, residual)
+    return mfalcon_desc(ld, int(microbatch))
+
+
+def mfalcon_cache_size(desc, hist_offsets_host) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib.mfalcon_cache_size(ctypes.byref(desc), _i64p(hist_offsets_host), ctypes.byref(n)))
+    return n.value
+
+
+def mfalcon_history(hist_offsets, hist_ts, hist_x, layers: Sequence[LayerWeights], *, num_heads,
+                    d_qk, d_v, max_seq_len, microbatch=1, ln_eps=1e-5, residual=0, cache=None,
+                    workspace=None, hist_offsets_host=None, stream=None):
+    """History pass of M-FALCON into a reusable cache (a uint8 device tensor, returned)."""
+    hh = _host_offsets(hist_offsets, hist_offsets_host)
+    desc = _mf_desc(layers, len(hh) - 1, hist_x, num_heads=num_heads, d_qk=d_qk, d_v=d_v,
+                    max_seq_len=max_seq_len, microbatch=microbatch, ln_eps=ln_eps,
+                    residual=residual)
+    need = mfalcon_cache_size(desc, hh)
+    if cache is None:
+        cache = torch.empty(max(need, 1), dtype=torch.uint8, device=hist_x.device)
+    n = ctypes.c_size_t(0)
+    _check(lib.mfalcon_history_workspace_size(ctypes.byref(desc), _i64p(hh), ctypes.byref(n)))
+    ws, nbytes = _workspace(n.value, hist_x.device, workspace)
+    arr = _weights_array(layers)
+    _check(lib.mfalcon_history(ctypes.byref(desc), _i64p(hh), _ptr(hist_offsets), _ptr(hist_ts),
+                               _ptr(hist_x), arr, _ptr(cache), cache.numel(), _ptr(ws), nbytes,
+                               _stream(stream)))
+    return cache
+
+
+def mfalcon_score_cached(cache, hist_offsets, hist_ts, cand_offsets, cand_ts, cand_x,
+                         layers: Sequence[LayerWeights], *, num_heads, d_qk, d_v, max_seq_len,
+                         microbatch, w_head=None, ln_eps=1e-5, residual=0, out=None, logit=None,
+                         workspace=None, hist_offsets_host=None, cand_offsets_host=None,
+                         stream=None):
+    """Candidate pass of M-FALCON against a cache from mfalcon_history. Returns (out, logit)."""
+    hh = _host_offsets(hist_offsets, hist_offsets_host)
+    ch = _host_offsets(cand_offsets, cand_offsets_host)
+    desc = _mf_desc(layers, len(hh) - 1, cand_x, num_heads=num_heads, d_qk=d_qk, d_v=d_v,
+                    max_seq_len=max_seq_len, microbatch=microbatch, ln_eps=ln_eps,
+                    residual=residual)
+    if out is None:
+        out = torch.empty_like(cand_x)
+    if logit is None and w_head is not None:
+        logit = torch.empty(cand_x.shape[0], dtype=torch.float32, device=cand_x.device)
+    n = ctypes.c_size_t(0)
+    _check(lib.mfalcon_cached_workspace_size(ctypes.byref(desc), _i64p(hh), _i64p(ch),
+                                             ctypes.byref(n)))
+    ws, nbytes = _workspace(n.value, cand_x.device, workspace)
+    arr = _weights_array(layers)
+    _check(lib.mfalcon_score_cached(ctypes.byref(desc), _i64p(hh), _ptr(hist_offsets),
+                                    _ptr(hist_ts), _ptr(cache), cache.numel(), _i64p(ch),
+                                    _ptr(cand_offsets), _ptr(cand_ts), _ptr(cand_x), arr,
+                                    _ptr(w_head), _ptr(out), _ptr(logit), _ptr(ws), nbytes,
+                                    _stream(stream)))
     return out, logit
 
 

@@ -188,6 +188,47 @@ hstu_status mfalcon_score(const mfalcon_desc* desc, const int64_t* hist_offsets_
                           size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * A persistent M-FALCON history cache, for serving several requests (candidate
+ * sets) against the same users' histories (HSTU chapter, "M-FALCON": the
+ * history's keys and values are computed once and reused, as a KV cache).
+ *
+ * mfalcon_history runs the history pass of mfalcon_score and stores what the
+ * candidate pass needs in `cache` (caller-owned device memory, 256-byte
+ * aligned, at least mfalcon_cache_size bytes): per layer the f1 output over
+ * the history, and the per-32-key timestamp ranges of the history keys.
+ * `workspace` (mfalcon_history_workspace_size bytes) is scratch for the call
+ * only.
+ *
+ * mfalcon_score_cached runs the candidate pass against such a cache. Its
+ * results equal mfalcon_score's bit for bit when the descriptor, the history
+ * offsets and timestamps, and the weights are the ones the cache was built
+ * with; the library cannot check that the cache matches (it keeps no state),
+ * so that is the caller's contract. The cache is only read, so calls with
+ * different candidate sets may share it. `workspace` is
+ * mfalcon_cached_workspace_size bytes.
+ * ---------------------------------------------------------------------- */
+hstu_status mfalcon_cache_size(const mfalcon_desc* desc, const int64_t* hist_offsets_host,
+                               size_t* bytes);
+hstu_status mfalcon_history_workspace_size(const mfalcon_desc* desc,
+                                           const int64_t* hist_offsets_host, size_t* bytes);
+hstu_status mfalcon_history(const mfalcon_desc* desc, const int64_t* hist_offsets_host,
+                            const int64_t* hist_offsets, const int64_t* hist_ts,
+                            const void* hist_x, const hstu_layer_weights* weights, void* cache,
+                            size_t cache_bytes, void* workspace, size_t workspace_bytes,
+                            void* stream);
+hstu_status mfalcon_cached_workspace_size(const mfalcon_desc* desc,
+                                          const int64_t* hist_offsets_host,
+                                          const int64_t* cand_offsets_host, size_t* bytes);
+hstu_status mfalcon_score_cached(const mfalcon_desc* desc, const int64_t* hist_offsets_host,
+                                 const int64_t* hist_offsets, const int64_t* hist_ts,
+                                 const void* cache, size_t cache_bytes,
+                                 const int64_t* cand_offsets_host, const int64_t* cand_offsets,
+                                 const int64_t* cand_ts, const void* cand_x,
+                                 const hstu_layer_weights* weights, const float* w_head,
+                                 void* cand_out, float* cand_logit, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * hstu_debug_buckets (test support): writes the position and time bucket
  * indices that the attention kernels use for sequence `seq`, as int32
  * [n][n] matrices (row i = query, column j = key). Entries with j > i are

@@ -165,6 +165,45 @@ def test_mfalcon_rejections(ops):
     assert _mf(ops, ops.mfalcon_desc(ld, 4), hoff, np.zeros(3, np.int64)) == 0
 
 
+def test_mfalcon_cache_rejections(ops):
+    """The cached M-FALCON calls check the cache and workspace before any launch."""
+    ld = _layer_desc(ops)
+    desc = ops.mfalcon_desc(ld, 4)
+    hoff = np.array([0, 5, 12], np.int64)
+    coff = np.array([0, 3, 9], np.int64)
+    hp, cp = hoff.ctypes.data_as(ops._I64P), coff.ctypes.data_as(ops._I64P)
+    n = ctypes.c_size_t(0)
+    assert ops.lib.mfalcon_cache_size(ctypes.byref(desc), hp, ctypes.byref(n)) == 0
+    cache = n.value
+    assert cache > 0
+    assert ops.lib.mfalcon_history_workspace_size(ctypes.byref(desc), hp, ctypes.byref(n)) == 0
+    hws = n.value
+    assert ops.lib.mfalcon_cached_workspace_size(ctypes.byref(desc), hp, cp, ctypes.byref(n)) == 0
+    cws = n.value
+    # the one-shot workspace holds the cache and both passes' scratch
+    full = ctypes.c_size_t(0)
+    assert ops.lib.mfalcon_workspace_size(ctypes.byref(desc), hp, cp, ctypes.byref(full)) == 0
+    al = lambda x: (x + 255) // 256 * 256
+    assert full.value == al(cache) + al(hws) + al(cws)
+    hist = ops.lib.mfalcon_history
+    big = ctypes.c_void_p(0x100000)
+    assert hist(ctypes.byref(desc), hp, FAKE, None, FAKE, _weights(ops), big, cache - 1, big, 1 << 30,
+                None) == 3                                             # cache too small
+    assert hist(ctypes.byref(desc), hp, FAKE, None, FAKE, _weights(ops), ctypes.c_void_p(0x100010),
+                cache, big, 1 << 30, None) == 1                        # cache not 256-aligned
+    assert hist(ctypes.byref(desc), hp, FAKE, None, FAKE, _weights(ops), big, cache, big, 0,
+                None) == 3                                             # workspace too small
+    sc = ops.lib.mfalcon_score_cached
+    args = lambda c, cb, ws, wsb, hts=None, cts=None: (ctypes.byref(desc), hp, FAKE, hts, c, cb, cp,
+                                                        FAKE, cts, FAKE, _weights(ops), None, FAKE,
+                                                        None, ws, wsb, None)
+    assert sc(*args(big, cache - 1, big, 1 << 30)) == 3                 # cache too small
+    assert sc(*args(big, cache, big, cws - 1)) == 3                     # workspace too small
+    assert sc(*args(big, cache, big, 1 << 30, hts=FAKE)) == 1           # ts mismatch
+    assert sc(ctypes.byref(desc), hp, FAKE, None, big, cache, None, FAKE, None, FAKE, _weights(ops),
+              None, FAKE, None, big, 1 << 30, None) == 1                # no host cand offsets
+
+
 def test_debug_buckets_rejections(ops):
     d = _desc(ops)
     f = ops.lib.hstu_debug_buckets

@@ -151,3 +151,49 @@ def test_split_history_multi_user(L):
                            np.random.default_rng(1).permutation(np.arange(62, 126))])
     o, _ = mf_on_gpu(x, cand_x=x.cand_x[perm], cand_ts=x.cand_ts[perm])
     assert np.array_equal(o.float().cpu().numpy(), base[perm])
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_cached_history_equals_one_shot(dt):
+    """mfalcon_history + mfalcon_score_cached equals mfalcon_score bit for bit, and one
+    cache serves several requests (candidate sets) for the same users."""
+    from hstu_jagged_pointwise_amd import ops
+    x = _small(dt, 2, seed=11)
+    announce(f"cached M-FALCON {dt}")
+    dtt = act_dtype(x.dtype)
+    layers = layer_weights_on_gpu(x.layers, x.dtype)
+    kw = dict(num_heads=x.num_heads, d_qk=x.d_qk, d_v=x.d_v, max_seq_len=x.max_seq_len,
+              ln_eps=x.eps, residual=x.residual)
+    cache = ops.mfalcon_history(dev(x.hist_offsets), dev(x.hist_ts), dev(x.hist_x, dtt), layers,
+                                microbatch=x.microbatch, hist_offsets_host=x.hist_offsets, **kw)
+    # request 1: the full candidate set
+    ref, ref_logit = mf_on_gpu(x)
+    got, got_logit = ops.mfalcon_score_cached(cache, dev(x.hist_offsets), dev(x.hist_ts),
+                                              dev(x.cand_offsets), dev(x.cand_ts),
+                                              dev(x.cand_x, dtt), layers, microbatch=x.microbatch,
+                                              w_head=dev(x.w_head), hist_offsets_host=x.hist_offsets,
+                                              cand_offsets_host=x.cand_offsets, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(got, ref) and torch.equal(got_logit, ref_logit)
+    # request 2 against the same cache: a different, smaller candidate set
+    rng = np.random.default_rng(5)
+    coff2 = np.array([0, 2, 2, 7, 7], np.int64)
+    cx2 = rng.standard_normal((7, x.cand_x.shape[1])).astype(np.float32)
+    if dt == "bf16":
+        cx2 = synth.round_bf16(cx2)
+    cts2 = (x.hist_ts[x.hist_offsets[1] - 1] + 100 + np.arange(7)).astype(np.int64)
+    ref2, _ = mf_on_gpu(x, cand_x=cx2, cand_ts=cts2, cand_offsets=coff2)
+    got2, _ = ops.mfalcon_score_cached(cache, dev(x.hist_offsets), dev(x.hist_ts), dev(coff2),
+                                       dev(cts2), dev(cx2, dtt), layers, microbatch=x.microbatch,
+                                       w_head=dev(x.w_head), hist_offsets_host=x.hist_offsets,
+                                       cand_offsets_host=coff2, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(got2, ref2)
+    # and the first request again, after the second: the cache is only read
+    got3, _ = ops.mfalcon_score_cached(cache, dev(x.hist_offsets), dev(x.hist_ts),
+                                       dev(x.cand_offsets), dev(x.cand_ts), dev(x.cand_x, dtt),
+                                       layers, microbatch=x.microbatch, w_head=dev(x.w_head),
+                                       hist_offsets_host=x.hist_offsets,
+                                       cand_offsets_host=x.cand_offsets, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(got3, ref)
