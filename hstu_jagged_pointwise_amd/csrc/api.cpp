@@ -846,6 +846,83 @@ hstu_status mfalcon_score_cached(const mfalcon_desc* desc, const int64_t* hist_o
                         (hipStream_t)stream);
 }
 
+// Stochastic Length (HSTU chapter, "Three more scaling components"): the
+// target length and the keep-whole decision, in double precision on the host.
+hstu_status hstu_sl_lengths(const hstu_sl_desc* desc, const int64_t* offsets_host,
+                            const float* u_keep_host, int64_t* new_offsets_host,
+                            int64_t* target_len) {
+  if (!desc) return fail(HSTU_INVALID_ARGUMENT, "descriptor is NULL");
+  if (desc->max_seq_len < 1) return fail(HSTU_INVALID_ARGUMENT, "max_seq_len (N) must be >= 1");
+  if (!(desc->alpha >= 0.f && desc->alpha <= 2.f))
+    return fail(HSTU_INVALID_ARGUMENT, "alpha must be in [0, 2]");
+  Jagged j;
+  hstu_status st = check_offsets(offsets_host, desc->batch, -1, 1, "offsets", &j);
+  if (st) return st;
+  const int64_t L = (int64_t)std::floor(
+      std::pow((double)desc->max_seq_len, (double)desc->alpha / 2.0) + 1e-9);
+  if (target_len) *target_len = L;
+  if (desc->batch == 0) {
+    if (new_offsets_host) new_offsets_host[0] = 0;
+    return HSTU_OK;
+  }
+  if (!u_keep_host || !new_offsets_host)
+    return fail(HSTU_INVALID_ARGUMENT, "u_keep_host and new_offsets_host are required");
+  int64_t acc = 0;
+  new_offsets_host[0] = 0;
+  for (int b = 0; b < desc->batch; ++b) {
+    const int64_t n = offsets_host[b + 1] - offsets_host[b];
+    const bool whole =
+        n <= L || (double)u_keep_host[b] < ((double)L * (double)L) / ((double)n * (double)n);
+    acc += whole ? n : L;
+    new_offsets_host[b + 1] = acc;
+  }
+  return HSTU_OK;
+}
+
+hstu_status hstu_sl_sample(int32_t batch, const int64_t* offsets_host,
+                           const int64_t* new_offsets_host, const int64_t* offsets,
+                           const int64_t* new_offsets, const uint32_t* keys, int64_t* src_index,
+                           const void* x, int64_t row_bytes, void* out_x, const int64_t* ts,
+                           int64_t* out_ts, void* stream) {
+  Jagged j;
+  hstu_status st = check_offsets(offsets_host, batch, -1, 1, "offsets", &j);
+  if (st) return st;
+  if (batch == 0) return HSTU_OK;
+  if (!new_offsets_host) return fail(HSTU_INVALID_ARGUMENT, "new_offsets_host is NULL");
+  if (new_offsets_host[0] != 0) return fail(HSTU_INVALID_ARGUMENT, "new_offsets[0] must be 0");
+  bool cut = false;
+  for (int b = 0; b < batch; ++b) {
+    const int64_t n = offsets_host[b + 1] - offsets_host[b];
+    const int64_t m = new_offsets_host[b + 1] - new_offsets_host[b];
+    if (m < 0 || m > n)
+      return fail(HSTU_INVALID_ARGUMENT,
+                  "sequence %d: new length %lld must be in [0, %lld]", b, (long long)m,
+                  (long long)n);
+    cut |= m > 0 && m < n;
+  }
+  const int64_t rows = new_offsets_host[batch];
+  if (rows == 0) return HSTU_OK;
+  if (!offsets || !new_offsets || !src_index)
+    return fail(HSTU_INVALID_ARGUMENT, "offsets, new_offsets and src_index are required");
+  if (cut && !keys) return fail(HSTU_INVALID_ARGUMENT, "keys are required to cut a sequence");
+  if ((x == nullptr) != (out_x == nullptr))
+    return fail(HSTU_INVALID_ARGUMENT, "x and out_x must both be set or both be NULL");
+  if ((ts == nullptr) != (out_ts == nullptr))
+    return fail(HSTU_INVALID_ARGUMENT, "ts and out_ts must both be set or both be NULL");
+  if (x) {
+    if (row_bytes <= 0 || row_bytes % 16)
+      return fail(HSTU_INVALID_ARGUMENT, "row_bytes must be a positive multiple of 16");
+    if (row_bytes > (int64_t(1) << 24))
+      return fail(HSTU_UNSUPPORTED, "row_bytes above 16 MiB");
+    if (!aligned16(x) || !aligned16(out_x))
+      return fail(HSTU_INVALID_ARGUMENT, "x and out_x must be 16-byte aligned");
+  }
+  hipStream_t s = (hipStream_t)stream;
+  HSTU_TRY(launch_sl_select(offsets, new_offsets, batch, keys, src_index, s), "sl select");
+  HSTU_TRY(launch_sl_gather(src_index, rows, x, row_bytes, ts, out_x, out_ts, s), "sl gather");
+  return HSTU_OK;
+}
+
 hstu_status hstu_debug_buckets(const hstu_attn_desc* desc, const int64_t* seq_offsets_host,
                                const int64_t* seq_offsets, const int64_t* timestamps, int32_t seq,
                                int32_t* pos_bucket, int32_t* time_bucket, void* stream) {

@@ -89,6 +89,14 @@ hipError_t launch_gemm(const void* A, int64_t lda, const void* W, int64_t ldw,
 hipError_t launch_rowdot(const void* y, int64_t ld_y, const float* w, float* logit, int64_t rows,
                          int d, int use_bf16, hipStream_t s);
 
+// Stochastic Length: src[new_off[b] + i] = input row of the i-th kept action of
+// sequence b (whole when its new length equals its length, else the positions of
+// the smallest (key, position) pairs), then the optional row and timestamp gather.
+hipError_t launch_sl_select(const int64_t* off, const int64_t* new_off, int B,
+                            const uint32_t* keys, int64_t* src, hipStream_t s);
+hipError_t launch_sl_gather(const int64_t* src, int64_t rows, const void* x, int64_t row_bytes,
+                            const int64_t* ts, void* out_x, int64_t* out_ts, hipStream_t s);
+
 hipError_t launch_debug_buckets(const int64_t* offsets, const int64_t* ts, int seq, int n, int P,
                                 int T, int32_t* pos_bucket, int32_t* time_bucket, hipStream_t s);
 

@@ -51,6 +51,11 @@ class mfalcon_desc(ctypes.Structure):
     _fields_ = [("layer", hstu_layer_desc), ("microbatch", ctypes.c_int32)]
 
 
+class hstu_sl_desc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("max_seq_len", ctypes.c_int32),
+                ("alpha", ctypes.c_float)]
+
+
 _P = ctypes.c_void_p
 _I64P = ctypes.POINTER(ctypes.c_int64)
 _SZP = ctypes.POINTER(ctypes.c_size_t)
@@ -79,6 +84,10 @@ _sig = {
     "mfalcon_score_cached": ([ctypes.POINTER(mfalcon_desc), _I64P, _P, _P, _P, ctypes.c_size_t,
                               _I64P, _P, _P, _P, ctypes.POINTER(hstu_layer_weights), _P, _P, _P,
                               _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "hstu_sl_lengths": ([ctypes.POINTER(hstu_sl_desc), _I64P, ctypes.POINTER(ctypes.c_float), _I64P,
+                         _I64P], ctypes.c_int),
+    "hstu_sl_sample": ([ctypes.c_int32, _I64P, _I64P, _P, _P, _P, _P, _P, ctypes.c_int64, _P, _P,
+                        _P, _P], ctypes.c_int),
     "hstu_debug_buckets": ([ctypes.POINTER(hstu_attn_desc), _I64P, _P, _P, ctypes.c_int32, _P, _P,
                             _P], ctypes.c_int),
 }
@@ -335,6 +344,48 @@ def mfalcon_score_cached(cache, hist_offsets, hist_ts, cand_offsets, cand_ts, ca
                                     _ptr(w_head), _ptr(out), _ptr(logit), _ptr(ws), nbytes,
                                     _stream(stream)))
     return out, logit
+
+
+def hstu_sl_lengths(offsets_host, max_seq_len: int, alpha: float, u_keep_host):
+    """New offsets after Stochastic Length, on the host: (new_offsets int64 [B+1], L)."""
+    off = np.ascontiguousarray(offsets_host, dtype=np.int64)
+    u = np.ascontiguousarray(u_keep_host, dtype=np.float32)
+    B = len(off) - 1
+    if len(u) != B:
+        raise ValueError(f"u_keep has {len(u)} entries for {B} sequences")
+    desc = hstu_sl_desc(B, int(max_seq_len), float(alpha))
+    new = np.zeros(B + 1, np.int64)
+    L = ctypes.c_int64(0)
+    _check(lib.hstu_sl_lengths(ctypes.byref(desc), _i64p(off),
+                               u.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), _i64p(new),
+                               ctypes.byref(L)))
+    return new, L.value
+
+
+def hstu_sl_sample(offsets, new_offsets, keys, x=None, timestamps=None, *, offsets_host=None,
+                   new_offsets_host=None, stream=None):
+    """Kept rows of each sequence on the device. keys: int32 or uint32 device tensor, one
+    random 32-bit key per input row (compared as unsigned). Returns (src_index, x[src_index]
+    or None, timestamps[src_index] or None)."""
+    oh = _host_offsets(offsets, offsets_host)
+    nh = _host_offsets(new_offsets, new_offsets_host)
+    B = len(oh) - 1
+    rows = int(nh[-1]) if B > 0 else 0
+    dev = offsets.device
+    src = torch.empty(rows, dtype=torch.int64, device=dev)
+    out_x = out_ts = None
+    row_bytes = 0
+    if x is not None:
+        out_x = torch.empty((rows,) + tuple(x.shape[1:]), dtype=x.dtype, device=dev)
+        row_bytes = x[0].numel() * x.element_size() if x.shape[0] else 0
+    if timestamps is not None:
+        out_ts = torch.empty(rows, dtype=torch.int64, device=dev)
+    if keys is not None and keys.element_size() != 4:
+        raise ValueError("keys must be 32-bit")
+    _check(lib.hstu_sl_sample(int(B), _i64p(oh), _i64p(nh), _ptr(offsets), _ptr(new_offsets),
+                              _ptr(keys), _ptr(src), _ptr(x), int(row_bytes), _ptr(out_x),
+                              _ptr(timestamps), _ptr(out_ts), _stream(stream)))
+    return src, out_x, out_ts
 
 
 def hstu_debug_buckets(seq_offsets, timestamps, seq: int, *, max_seq_len, num_pos_buckets,

@@ -304,3 +304,42 @@ def workload_mfalcon(seed=4, num_layers=1, num_candidates=16384, history=4096, m
     """One user, history 4096, 16,384 candidates in microbatches of 1024, 8 heads, d=64, d_model 512."""
     return make_mfalcon(seed, [history], [num_candidates], 8, 64, 64, 512, 128, 64, "bf16",
                         num_layers=num_layers, microbatch=microbatch)
+
+
+# --------------------------------------------------------------------------
+# Stochastic Length sampling: the random draws it consumes
+# --------------------------------------------------------------------------
+@dataclass
+class SlInputs:
+    offsets: np.ndarray       # int64 [B+1]
+    ts: np.ndarray            # int64 [T_tot]
+    x: np.ndarray             # [T_tot, d_model] (fp32 values; bf16-exact when dtype is bf16)
+    u_keep: np.ndarray        # float32 [B], uniform in [0, 1): the keep-whole draw per sequence
+    keys: np.ndarray          # uint32 [T_tot], uniform: the per-action selection keys
+    max_seq_len: int
+    alpha: float
+    dtype: str
+
+
+def sl_draws(rng, batch, total):
+    """(u_keep float32 [batch] uniform in [0,1), keys uint32 [total] uniform)."""
+    u = rng.random(batch).astype(np.float32)
+    u = np.minimum(u, np.float32(np.nextafter(np.float32(1), np.float32(0))))
+    keys = rng.integers(0, 2**32, size=total, dtype=np.uint64).astype(np.uint32)
+    return u, keys
+
+
+def make_sl(seed, lengths_fn, d_model, N, alpha, dtype="bf16"):
+    rng = np.random.default_rng(seed)
+    lengths = lengths_fn(rng)
+    off = offsets_from_lengths(lengths)
+    ts = timestamps(rng, lengths)
+    x = normal(rng, (int(off[-1]), d_model), 1.0, dtype)
+    u, keys = sl_draws(rng, len(lengths), int(off[-1]))
+    return SlInputs(off, ts, x, u, keys, N, alpha, dtype)
+
+
+def workload_sl_heavy_tail(seed=5, batch=32):
+    """The heavy-tailed training batch (bounded power-law lengths, s=1.2, on [64,4096],
+    d_model 512, bf16) sampled with N = 4096, alpha = 1.6 (target length 776)."""
+    return make_sl(seed, lambda r: lengths_power_law(r, batch, 1.2, 64, 4096), 512, 4096, 1.6)

@@ -229,6 +229,60 @@ hstu_status mfalcon_score_cached(const mfalcon_desc* desc, const int64_t* hist_o
                                  size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Stochastic Length (HSTU chapter, "Three more scaling components",
+ * Stochastic Length): training keeps the full history of short users and of a
+ * few long ones, and cuts the rest to a random subsequence of the target
+ * length L = floor(N^(alpha/2)), so that alpha = 1.6 takes N = 4096 to 776.
+ * The page leaves the rule open. These calls take one reading of it:
+ *   - a sequence of n <= L actions is kept whole;
+ *   - a longer one is kept whole iff u_keep[b] < (L/n)^2, which bounds the
+ *     expected n^2 attention cost of a user by 2 L^2;
+ *   - otherwise it keeps exactly L actions, in their original order. These
+ *     are the L positions whose (keys[row], position) pairs are smallest,
+ *     comparing keys as unsigned 32-bit integers and breaking ties by the
+ *     smaller position.
+ * With uniform random u_keep (in [0, 1)) and keys, the kept subsequence is
+ * uniformly random. The random numbers are inputs, so every call is
+ * deterministic.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int32_t batch;            /* B, number of sequences (>= 0) */
+  int32_t max_seq_len;      /* N (>= 1): the length the target L is derived from */
+  float alpha;              /* in [0, 2]; L = floor(N^(alpha/2)), in double precision */
+} hstu_sl_desc;
+
+/* hstu_sl_lengths (host memory only; no device work): fills new_offsets_host
+ * [B+1] with the offsets after sampling, given the input offsets_host [B+1]
+ * and one float u_keep_host[b] per sequence. Sequence b keeps n_b or L
+ * actions, by the rule above. L itself is written to *target_len when that
+ * pointer is not NULL. */
+hstu_status hstu_sl_lengths(const hstu_sl_desc* desc, const int64_t* offsets_host,
+                            const float* u_keep_host, int64_t* new_offsets_host,
+                            int64_t* target_len);
+
+/* hstu_sl_sample: picks and gathers the kept actions on the device.
+ *   offsets/offsets_host         [B+1] input offsets (device and host copy)
+ *   new_offsets/new_offsets_host [B+1] output offsets, for instance from
+ *       hstu_sl_lengths. Each new length m_b must satisfy 0 <= m_b <= n_b.
+ *       m_b == n_b keeps the sequence whole; a smaller m_b keeps the m_b
+ *       positions with the smallest (key, position) pairs.
+ *   keys       device uint32 [T_in], one random key per input row
+ *              (read only for cut sequences; may be NULL if none is cut)
+ *   src_index  device int64 [T_out] (T_out = new_offsets_host[B]): the global
+ *              input row of output row r, increasing within each sequence
+ *   x, row_bytes, out_x  optional rows to gather: out_x[r] = x[src_index[r]].
+ *              Each row is row_bytes bytes (a multiple of 16). x and out_x
+ *              must be 16-byte aligned. Pass NULL for x and out_x to skip.
+ *   ts, out_ts optional int64 timestamps to gather the same way (NULL: skip)
+ * The device offsets must hold the same values as the host copies. The
+ * scratch needs fit in LDS, so there is no workspace. */
+hstu_status hstu_sl_sample(int32_t batch, const int64_t* offsets_host,
+                           const int64_t* new_offsets_host, const int64_t* offsets,
+                           const int64_t* new_offsets, const uint32_t* keys, int64_t* src_index,
+                           const void* x, int64_t row_bytes, void* out_x, const int64_t* ts,
+                           int64_t* out_ts, void* stream);
+
+/* ------------------------------------------------------------------------
  * hstu_debug_buckets (test support): writes the position and time bucket
  * indices that the attention kernels use for sequence `seq`, as int32
  * [n][n] matrices (row i = query, column j = key). Entries with j > i are
