@@ -1,0 +1,188 @@
+"""CPU oracle for the gradients of the HSTU layer (the backward pass).
+
+TEST INFRASTRUCTURE ONLY. Only the test suite uses this module. The GPU library
+never imports it, calls it or falls back to it.
+
+The HSTU chapter of chenhuiyu.github.io trains the model generatively ("What an
+HSTU layer changes", equations 1-3; "Three more scaling components"), so every
+forward step needs its gradient. These are the gradients of the forward oracle
+(oracle/hstu_oracle.py, same readings: SiLU for phi1 and phi2, the 1/N scale
+after SiLU, clamped position buckets, log2 time buckets, an exact 0 for hidden
+pairs, LayerNorm over the whole H*d_v row), written out by the chain rule in
+fp64, densely per sequence and head:
+
+  attention, per head, visible pairs j <= i:
+    z_ij  = q_i . k_j + bias_ij           a_ij = SiLU(z_ij) / N
+    o_i   = sum_j a_ij v_j
+  with g_i = dL/do_i:
+    dv_j  = sum_i a_ij g_i
+    da_ij = g_i . v_j
+    dz_ij = da_ij SiLU'(z_ij) / N         (0 for hidden pairs)
+    dq_i  = sum_j dz_ij k_j               dk_j = sum_i dz_ij q_i
+    d rab_pos[h][p]  = sum of dz_ij over visible pairs with position bucket p
+    d rab_time[h][t] = sum of dz_ij over visible pairs with time bucket t
+  SiLU'(x) = s (1 + x (1 - s)), s = 1 / (1 + e^{-x}).
+
+  gate (eq. 3), per row with y = LN(o) gamma + beta and out = y (.) u:
+    du = g (.) y,   dy = g (.) u,   dgamma = sum_rows dy (.) xhat,   dbeta = sum_rows dy
+    do = (dxhat - mean(dxhat) - xhat mean(dxhat (.) xhat)) / sqrt(var + eps),
+    dxhat = dy (.) gamma
+
+  layer: z1 = X W1^T + b1, [U|V|Q|K] = SiLU(z1); Y = G W2^T + b2 (+ X):
+    dG = dY W2, dW2 = dY^T G, db2 = sum_rows dY
+    dz1 = d[U|V|Q|K] (.) SiLU'(z1), dW1 = dz1^T X, db1 = sum_rows dz1
+    dX = dz1 W1 (+ dY when residual)
+
+Nothing here reuses the forward's code path for the gradient: the forward
+oracle is called only to supply values (for the finite-difference pins in the
+tests), and the backward formulas above are evaluated directly.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+from . import hstu_oracle as F
+
+__all__ = ["silu_grad", "attention_backward", "gate_backward", "layer_backward",
+           "LayerGrads"]
+
+
+def _f64(a):
+    return None if a is None else np.asarray(a, dtype=np.float64)
+
+
+def silu_grad(x):
+    """d/dx SiLU(x) = s (1 + x (1 - s)) with s = sigmoid(x)."""
+    x = np.asarray(x, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        s = 1.0 / (1.0 + np.exp(-x))
+    return s * (1.0 + x * (1.0 - s))
+
+
+def _buckets(n, t, P, T):
+    """Position and time bucket matrices [n, n] of one sequence (query i, key j)."""
+    pos = np.arange(n, dtype=np.int64)
+    bp = F.pos_bucket(pos[:, None] - pos[None, :], P)
+    bt = None
+    if t is not None:
+        bt = F.time_bucket(t[:, None] - t[None, :], T)
+    return bp, bt
+
+
+def attention_backward(offsets, ts, q, k, v, rab_pos, rab_time, N, d_out, P=None, T=None):
+    """Gradients of causal jagged attention without the gate (eq. 2).
+
+    q, k [T_tot, H, d_qk]; v, d_out [T_tot, H, d_v]. Returns
+    (dq, dk, dv, d_rab_pos [H, P] or None, d_rab_time [H, T] or None), fp64.
+    P and T give the table widths when a table is absent but its gradient is wanted."""
+    offsets = np.asarray(offsets, dtype=np.int64)
+    q, k, v, g = _f64(q), _f64(k), _f64(v), _f64(d_out)
+    Ttot, H, dqk = q.shape
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    P = rab_pos.shape[1] if rab_pos is not None else P
+    T = rab_time.shape[1] if rab_time is not None else T
+    use_time = rab_time is not None and ts is not None
+    drp = np.zeros((H, P)) if rab_pos is not None else None
+    drt = np.zeros((H, T)) if rab_time is not None else None
+    for b in range(len(offsets) - 1):
+        s, e = int(offsets[b]), int(offsets[b + 1])
+        n = e - s
+        if n == 0:
+            continue
+        t = np.asarray(ts, np.int64)[s:e] if use_time else None
+        pos = np.arange(n, dtype=np.int64)
+        vis = pos[None, :] <= pos[:, None]
+        bp, bt = _buckets(n, t, P if P else 1, T if T else 1)
+        for h in range(H):
+            bias = F.bias_matrix(h, pos, pos, t, t, rab_pos, rab_time if use_time else None)
+            z = q[s:e, h] @ k[s:e, h].T + bias
+            a = np.where(vis, F.silu(z) / float(N), 0.0)
+            dv[s:e, h] = a.T @ g[s:e, h]
+            da = g[s:e, h] @ v[s:e, h].T
+            dz = np.where(vis, da * silu_grad(z) / float(N), 0.0)
+            dq[s:e, h] = dz @ k[s:e, h]
+            dk[s:e, h] = dz.T @ q[s:e, h]
+            if drp is not None:
+                drp[h] += np.bincount(bp[vis], weights=dz[vis], minlength=P)
+            if drt is not None and use_time:
+                drt[h] += np.bincount(bt[vis], weights=dz[vis], minlength=T)
+    return dq, dk, dv, drp, drt
+
+
+def gate_backward(o, u, gamma, beta, eps, d_out):
+    """Gradients of out = (LN(o) gamma + beta) (.) u over rows of width W = H*d_v.
+
+    o, u, d_out [R, W]. Returns (do, du, dgamma [W], dbeta [W])."""
+    o, u, g = _f64(o), _f64(u), _f64(d_out)
+    W = o.shape[1]
+    gam = np.ones(W) if gamma is None else _f64(gamma)
+    bet = np.zeros(W) if beta is None else _f64(beta)
+    mu = o.mean(axis=1, keepdims=True)
+    var = ((o - mu) ** 2).mean(axis=1, keepdims=True)
+    rstd = 1.0 / np.sqrt(var + eps)
+    xhat = (o - mu) * rstd
+    y = xhat * gam[None, :] + bet[None, :]
+    du = g * y
+    dy = g * u
+    dgamma = (dy * xhat).sum(axis=0)
+    dbeta = dy.sum(axis=0)
+    dxhat = dy * gam[None, :]
+    do = rstd * (dxhat - dxhat.mean(axis=1, keepdims=True)
+                 - xhat * (dxhat * xhat).mean(axis=1, keepdims=True))
+    return do, du, dgamma, dbeta
+
+
+@dataclass
+class LayerGrads:
+    dx: np.ndarray
+    dw1: np.ndarray
+    db1: np.ndarray
+    dw2: np.ndarray
+    db2: np.ndarray
+    d_rab_pos: Optional[np.ndarray]
+    d_rab_time: Optional[np.ndarray]
+    dgamma: np.ndarray
+    dbeta: np.ndarray
+
+
+def layer_backward(offsets, ts, x, w, H, d_qk, d_v, N, d_y, eps=1e-5, residual=0):
+    """Gradients of one HSTU layer (eqs. 1-3) in fp64, given dL/dY.
+
+    w has the fields of the forward oracle's layer weights (w1, b1, rab_pos, rab_time,
+    gamma, beta, w2, b2)."""
+    x, gy = _f64(x), _f64(d_y)
+    R = x.shape[0]
+    z1 = x @ _f64(w.w1).T
+    if w.b1 is not None:
+        z1 = z1 + _f64(w.b1)[None, :]
+    act = F.silu(z1)
+    cu, cq = H * d_v, H * d_qk
+    U = act[:, 0:cu]
+    V = act[:, cu:2 * cu].reshape(R, H, d_v)
+    Q = act[:, 2 * cu:2 * cu + cq].reshape(R, H, d_qk)
+    K = act[:, 2 * cu + cq:2 * cu + 2 * cq].reshape(R, H, d_qk)
+    o = F.hstu_attention(offsets, ts, Q, K, V, w.rab_pos, w.rab_time, N).reshape(R, cu)
+    y = F.layer_norm_rows(o, w.gamma, w.beta, eps)
+    G = y * U
+    # f2
+    dG = gy @ _f64(w.w2)
+    dw2 = gy.T @ G
+    db2 = gy.sum(axis=0)
+    # gate and norm
+    do, dU, dgamma, dbeta = gate_backward(o, U, w.gamma, w.beta, eps, dG)
+    # attention
+    dQ, dK, dV, drp, drt = attention_backward(offsets, ts, Q, K, V, w.rab_pos, w.rab_time, N,
+                                              do.reshape(R, H, d_v))
+    dact = np.concatenate([dU, dV.reshape(R, cu), dQ.reshape(R, cq), dK.reshape(R, cq)], axis=1)
+    dz1 = dact * silu_grad(z1)
+    dw1 = dz1.T @ x
+    db1 = dz1.sum(axis=0)
+    dx = dz1 @ _f64(w.w1)
+    if residual:
+        dx = dx + gy
+    return LayerGrads(dx, dw1, db1, dw2, db2, drp, drt, dgamma, dbeta)

@@ -1,0 +1,145 @@
+"""Pins of the backward oracle (CPU). Central finite differences of the forward
+oracle check every gradient. A closed form is checked for a one-action sequence, and
+the jagged invariants are checked too: sequences do not interact, hidden pairs
+carry no gradient, and gradients are linear in the upstream gradient."""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import hstu_backward as BW
+from oracle import hstu_oracle as F
+from hstu_jagged_pointwise_amd import synth
+
+EPS = 1e-6
+
+
+def _fd(f, arr, idx):
+    """Central difference of the scalar function f() in arr[idx] (arr changed in place)."""
+    old = arr[idx]
+    arr[idx] = old + EPS
+    up = f()
+    arr[idx] = old - EPS
+    dn = f()
+    arr[idx] = old
+    return (up - dn) / (2 * EPS)
+
+
+def _close(got, want, what):
+    scale = max(1.0, abs(want))
+    assert abs(got - want) <= 1e-6 * scale, f"{what}: analytic {got!r} vs numeric {want!r}"
+
+
+def _attn_case(seed, with_time=True, P=4, T=3):
+    rng = np.random.default_rng(seed)
+    lens = np.array([5, 1, 0, 9], np.int64)
+    off = synth.offsets_from_lengths(lens)
+    n = int(off[-1])
+    H, dqk, dv = 2, 4, 3
+    q = rng.standard_normal((n, H, dqk))
+    k = rng.standard_normal((n, H, dqk))
+    v = rng.standard_normal((n, H, dv))
+    rp = rng.standard_normal((H, P)) * 0.5
+    rt = rng.standard_normal((H, T)) * 0.5
+    # gaps from 0 to ~10 s so that several time buckets, and clamping, occur
+    ts = np.concatenate([np.cumsum(rng.integers(0, 6, size=int(m))) for m in lens if m] or
+                        [np.zeros(0, np.int64)]).astype(np.int64)
+    g = rng.standard_normal((n, H, dv))
+    return off, (ts if with_time else None), q, k, v, rp, rt, g, 9
+
+
+@pytest.mark.parametrize("with_time", [True, False])
+def test_attention_gradients_by_finite_differences(with_time):
+    off, ts, q, k, v, rp, rt, g, N = _attn_case(1, with_time)
+    loss = lambda: float(np.sum(F.hstu_attention(off, ts, q, k, v, rp, rt, N) * g))
+    dq, dk, dv, drp, drt = BW.attention_backward(off, ts, q, k, v, rp, rt, N, g)
+    for name, arr, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv), ("rab_pos", rp, drp),
+                            ("rab_time", rt, drt)):
+        for idx in np.ndindex(arr.shape):
+            _close(grad[idx], _fd(loss, arr, idx), f"d{name}{idx}")
+    if not with_time:
+        assert np.all(drt == 0)  # no timestamps: the time table does not enter the output
+
+
+def test_attention_one_action_closed_form():
+    """n = 1: o = SiLU(q.k + rp[0] + rt[0]) / N v."""
+    rng = np.random.default_rng(2)
+    q, k, v, g = (rng.standard_normal((1, 1, 3)) for _ in range(4))
+    rp, rt = np.array([[0.3, 9.0]]), np.array([[-0.2, 9.0]])
+    ts, N = np.array([100], np.int64), 5
+    z = float(q[0, 0] @ k[0, 0]) + 0.3 - 0.2
+    s = 1 / (1 + math.exp(-z))
+    dsilu = s * (1 + z * (1 - s))
+    gv = float(g[0, 0] @ v[0, 0])
+    dq, dk, dv, drp, drt = BW.attention_backward(np.array([0, 1]), ts, q, k, v, rp, rt, N, g)
+    assert np.allclose(dv[0, 0], z * s / N * g[0, 0], rtol=1e-14)
+    assert np.allclose(dq[0, 0], gv * dsilu / N * k[0, 0], rtol=1e-14)
+    assert np.allclose(dk[0, 0], gv * dsilu / N * q[0, 0], rtol=1e-14)
+    assert np.allclose(drp, [[gv * dsilu / N, 0.0]], rtol=1e-14)
+    assert np.allclose(drt, [[gv * dsilu / N, 0.0]], rtol=1e-14)
+
+
+def test_attention_jagged_and_causal_invariants():
+    off, ts, q, k, v, rp, rt, g, N = _attn_case(3)
+    base = BW.attention_backward(off, ts, q, k, v, rp, rt, N, g)
+    # changing sequence 0's inputs leaves the gradients of sequence 3 (rows 6..14) unchanged
+    q2 = q.copy()
+    q2[:5] += 1.0
+    other = BW.attention_backward(off, ts, q2, k, v, rp, rt, N, g)
+    for a, b in zip(base[:3], other[:3]):
+        assert np.array_equal(a[6:], b[6:])
+    # causality: the upstream gradient of the last row of a sequence reaches
+    # only that row's q and the keys/values, never dq of earlier rows
+    g1 = np.zeros_like(g)
+    g1[14] = g[14]
+    dq1, dk1, dv1, _, _ = BW.attention_backward(off, ts, q, k, v, rp, rt, N, g1)
+    assert np.all(dq1[:14] == 0) and np.any(dq1[14] != 0)
+    assert np.all(dk1[:6] == 0) and np.all(dv1[:6] == 0)
+    # linearity in the upstream gradient
+    two = BW.attention_backward(off, ts, q, k, v, rp, rt, N, 2.0 * g)
+    for a, b in zip(base, two):
+        assert np.allclose(b, 2.0 * a, rtol=1e-13, atol=0)
+
+
+def test_gate_gradients_by_finite_differences():
+    rng = np.random.default_rng(4)
+    R, W = 3, 6
+    o = rng.standard_normal((R, W))
+    u = rng.standard_normal((R, W))
+    gamma = 1 + 0.3 * rng.standard_normal(W)
+    beta = 0.3 * rng.standard_normal(W)
+    g = rng.standard_normal((R, W))
+    eps = 1e-3
+    loss = lambda: float(np.sum(F.layer_norm_rows(o, gamma, beta, eps) * u * g))
+    do, du, dgam, dbet = BW.gate_backward(o, u, gamma, beta, eps, g)
+    for name, arr, grad in (("o", o, do), ("u", u, du), ("gamma", gamma, dgam),
+                            ("beta", beta, dbet)):
+        for idx in np.ndindex(arr.shape):
+            _close(grad[idx], _fd(loss, arr, idx), f"d{name}{idx}")
+    # LayerNorm is invariant to shifting a row, so do sums to zero over each row
+    assert np.allclose(do.sum(axis=1), 0, atol=1e-12)
+
+
+@pytest.mark.parametrize("residual", [0, 1])
+def test_layer_gradients_by_finite_differences(residual):
+    x = synth.make_layer(5, lambda r: np.array([4, 0, 6]), 2, 4, 3, 8, 4, 3, "f32",
+                         random_bias=True, with_ln_affine=True, w_std=0.4, residual=residual)
+    w = x.layers[0]
+    for name in ("w1", "b1", "rab_pos", "rab_time", "gamma", "beta", "w2", "b2"):
+        setattr(w, name, np.asarray(getattr(w, name), np.float64).copy())
+    X = np.asarray(x.x, np.float64).copy()
+    rng = np.random.default_rng(6)
+    gy = rng.standard_normal(X.shape)
+    loss = lambda: float(np.sum(F.hstu_layer(x.offsets, x.ts, X, w, x.num_heads, x.d_qk, x.d_v,
+                                             x.max_seq_len, 1e-5, residual) * gy))
+    gr = BW.layer_backward(x.offsets, x.ts, X, w, x.num_heads, x.d_qk, x.d_v, x.max_seq_len, gy,
+                           1e-5, residual)
+    checks = [("x", X, gr.dx), ("w1", w.w1, gr.dw1), ("b1", w.b1, gr.db1), ("w2", w.w2, gr.dw2),
+              ("b2", w.b2, gr.db2), ("rab_pos", w.rab_pos, gr.d_rab_pos),
+              ("rab_time", w.rab_time, gr.d_rab_time), ("gamma", w.gamma, gr.dgamma),
+              ("beta", w.beta, gr.dbeta)]
+    for name, arr, grad in checks:
+        flat = list(np.ndindex(arr.shape))
+        pick = flat if len(flat) <= 40 else [flat[i] for i in rng.choice(len(flat), 40, False)]
+        for idx in pick:
+            _close(grad[idx], _fd(loss, arr, idx), f"d{name}{idx}")
