@@ -169,6 +169,29 @@ hstu_status plan_attn(const hstu_attn_desc* d, const int64_t* off_host, bool gat
   return HSTU_OK;
 }
 
+// ---------------------------------------------------------------- attention backward
+constexpr int kBwdRows = kSimpleRows;   // query and key tile of the backward kernels
+constexpr int kMaxBiasBins = 2048;      // P + T limit of the bias-table gradient
+
+struct AttnBwdPlan {
+  Jagged j;
+  size_t items = 0, partial = 0, ws = 0;
+};
+
+hstu_status plan_attn_bwd(const hstu_attn_desc* d, const int64_t* off_host, AttnBwdPlan* p) {
+  hstu_status st = check_attn_desc(d);
+  if (st) return st;
+  st = check_offsets(off_host, d->batch, d->max_seq_len, kBwdRows, "seq_offsets", &p->j);
+  if (st) return st;
+  if ((int64_t)p->j.items * d->num_heads >= (int64_t(1) << 31))
+    return fail(HSTU_UNSUPPORTED, "too many tiles for one launch");
+  p->items = (size_t)p->j.items * sizeof(int2);
+  const int64_t bins = (int64_t)d->num_pos_buckets + d->num_time_buckets;
+  p->partial = bins <= kMaxBiasBins ? (size_t)p->j.items * d->num_heads * bins * sizeof(float) : 0;
+  p->ws = align_up(p->items) + align_up(p->partial);
+  return HSTU_OK;
+}
+
 // ---------------------------------------------------------------- layer
 struct LayerPlan {
   Jagged j;
@@ -844,6 +867,79 @@ hstu_status mfalcon_score_cached(const mfalcon_desc* desc, const int64_t* hist_o
   return run_candidates(desc, p, hist_offsets, hist_ts, cb, cand_offsets_host, cand_offsets,
                         cand_ts, cand_x, weights, w_head, cand_out, cand_logit, kb,
                         (hipStream_t)stream);
+}
+
+hstu_status hstu_attn_bwd_workspace_size(const hstu_attn_desc* desc,
+                                         const int64_t* seq_offsets_host, size_t* bytes) {
+  if (!bytes) return fail(HSTU_INVALID_ARGUMENT, "bytes is NULL");
+  AttnBwdPlan p;
+  hstu_status st = plan_attn_bwd(desc, seq_offsets_host, &p);
+  if (st) return st;
+  *bytes = p.ws;
+  return HSTU_OK;
+}
+
+// Gradients of hstu_attn_fwd without the gate (HSTU chapter, eq. 2).
+hstu_status hstu_attn_bwd(const hstu_attn_desc* desc, const int64_t* seq_offsets_host,
+                          const int64_t* seq_offsets, const int64_t* timestamps, const void* q,
+                          const void* k, const void* v, const float* rab_pos,
+                          const float* rab_time, const void* d_out, void* dq, void* dk, void* dv,
+                          float* d_rab_pos, float* d_rab_time, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  AttnBwdPlan p;
+  hstu_status st = plan_attn_bwd(desc, seq_offsets_host, &p);
+  if (st) return st;
+  const bool want_bias = d_rab_pos || d_rab_time;
+  if (want_bias && desc->num_pos_buckets + desc->num_time_buckets > kMaxBiasBins)
+    return fail(HSTU_UNSUPPORTED, "bias-table gradients need P + T <= %d", kMaxBiasBins);
+  hipStream_t s = (hipStream_t)stream;
+  if (p.j.total == 0) {  // no pairs: the table gradients are zero
+    HSTU_TRY(launch_bias_grad_reduce(nullptr, 0, desc->num_heads, desc->num_pos_buckets,
+                                     desc->num_time_buckets, d_rab_pos, d_rab_time, s),
+             "bias gradient");
+    return HSTU_OK;
+  }
+  if (!seq_offsets) return fail(HSTU_INVALID_ARGUMENT, "device seq_offsets is NULL");
+  if (!q || !k || !v || !d_out || !dq || !dk || !dv)
+    return fail(HSTU_INVALID_ARGUMENT, "q, k, v, d_out, dq, dk and dv are required");
+  for (const void* t : {q, k, v, d_out, (const void*)dq, (const void*)dk, (const void*)dv})
+    if (!aligned16(t)) return fail(HSTU_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
+  if ((st = check_ws(workspace, workspace_bytes, p.ws, "workspace"))) return st;
+  Carver c{(char*)workspace};
+  int2* items = (int2*)c.take(p.items);
+  float* partial = (float*)c.take(p.partial);
+  HSTU_TRY(launch_plan_causal(seq_offsets, desc->batch, kBwdRows, p.j.max_tiles, items,
+                              (int)p.j.items, s),
+           "tile planner");
+  AttnBwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.dout = d_out;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.ld_q = a.ld_k = a.ld_dq = a.ld_dk = (int64_t)desc->num_heads * desc->d_qk;
+  a.ld_v = a.ld_do = a.ld_dv = (int64_t)desc->num_heads * desc->d_v;
+  a.offsets = seq_offsets;
+  a.ts = timestamps;
+  a.rab_pos = rab_pos;
+  a.rab_time = rab_time;
+  a.bias_partial = want_bias ? partial : nullptr;
+  a.items = items;
+  a.n_items = (int)p.j.items;
+  a.batch = desc->batch;
+  a.H = desc->num_heads;
+  a.d_qk = desc->d_qk;
+  a.d_v = desc->d_v;
+  a.P = desc->num_pos_buckets;
+  a.T = desc->num_time_buckets;
+  a.inv_n = 1.0f / (float)desc->max_seq_len;
+  HSTU_TRY(launch_attn_bwd_simple(a, desc->dtype == HSTU_BF16, s), "attention backward");
+  if (want_bias)
+    HSTU_TRY(launch_bias_grad_reduce(partial, a.n_items, a.H, a.P, a.T, d_rab_pos, d_rab_time, s),
+             "bias gradient");
+  return HSTU_OK;
 }
 
 // Stochastic Length (HSTU chapter, "Three more scaling components"): the

@@ -73,6 +73,34 @@ hipError_t launch_key_ranges(const int64_t* offsets, const int64_t* ts, int B, i
 hipError_t launch_attn_simple(const AttnArgs& a, int use_bf16, bool cand, hipStream_t s);
 hipError_t launch_attn_mfma(const AttnArgs& a, bool cand, hipStream_t s);
 
+// One attention backward launch (causal mode). Row strides (ld_*) are in elements;
+// head h sits at column h * d within each row.
+struct AttnBwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dout;           // dL/d(attention output) [rows, H, d_v]
+  void* dq;
+  void* dk;
+  void* dv;
+  int64_t ld_q, ld_k, ld_v, ld_do, ld_dq, ld_dk, ld_dv;
+  const int64_t* offsets;
+  const int64_t* ts;          // NULL: no time term (and a zero time-table gradient)
+  const float* rab_pos;       // [H][P] or NULL (= 0)
+  const float* rab_time;      // [H][T] or NULL (= 0)
+  float* bias_partial;        // [n_items][H][P + T] bucket sums of dz per work item, or NULL
+  const int2* items;          // (sequence, tile) list from the planner, 64-row tiles
+  int n_items;
+  int batch, H, d_qk, d_v, P, T;
+  float inv_n;
+};
+
+hipError_t launch_attn_bwd_simple(const AttnBwdArgs& a, int use_bf16, hipStream_t s);
+// d_rab_pos[h][p] / d_rab_time[h][t] = fixed-order sums of the per-item partials
+// (partial may be NULL when n_items is 0; the outputs are then zeros).
+hipError_t launch_bias_grad_reduce(const float* partial, int n_items, int H, int P, int T,
+                                   float* d_rab_pos, float* d_rab_time, hipStream_t s);
+
 // out[r, :] = (LN(o[r, :]) * gamma + beta) (.) u[r, :], width w, over `rows` rows, where
 // o[r, :] is the sum of nsplit partial rows o + s * split_stride (s = 0..nsplit-1, in order).
 hipError_t launch_ln_gate(const float* o, int64_t ld_o, int nsplit, int64_t split_stride,

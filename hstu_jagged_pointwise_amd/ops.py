@@ -84,6 +84,9 @@ _sig = {
     "mfalcon_score_cached": ([ctypes.POINTER(mfalcon_desc), _I64P, _P, _P, _P, ctypes.c_size_t,
                               _I64P, _P, _P, _P, ctypes.POINTER(hstu_layer_weights), _P, _P, _P,
                               _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "hstu_attn_bwd_workspace_size": ([ctypes.POINTER(hstu_attn_desc), _I64P, _SZP], ctypes.c_int),
+    "hstu_attn_bwd": ([ctypes.POINTER(hstu_attn_desc), _I64P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                       _P, _P, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "hstu_sl_lengths": ([ctypes.POINTER(hstu_sl_desc), _I64P, ctypes.POINTER(ctypes.c_float), _I64P,
                          _I64P], ctypes.c_int),
     "hstu_sl_sample": ([ctypes.c_int32, _I64P, _I64P, _P, _P, _P, _P, _P, ctypes.c_int64, _P, _P,
@@ -344,6 +347,32 @@ def mfalcon_score_cached(cache, hist_offsets, hist_ts, cand_offsets, cand_ts, ca
                                     _ptr(w_head), _ptr(out), _ptr(logit), _ptr(ws), nbytes,
                                     _stream(stream)))
     return out, logit
+
+
+def hstu_attn_bwd(seq_offsets, timestamps, q, k, v, d_out, rab_pos=None, rab_time=None, *,
+                  max_seq_len: int, num_pos_buckets=None, num_time_buckets=None,
+                  rab_grads=True, workspace=None, seq_offsets_host=None, stream=None):
+    """Gradients of hstu_attn_fwd (no gate). Returns (dq, dk, dv, d_rab_pos, d_rab_time);
+    the table gradients are fp32 [H, P] / [H, T], or None when rab_grads is False."""
+    host = _host_offsets(seq_offsets, seq_offsets_host)
+    T_tot, H, d_qk = q.shape
+    d_v = v.shape[2]
+    P = rab_pos.shape[1] if rab_pos is not None else (num_pos_buckets or 1)
+    T = rab_time.shape[1] if rab_time is not None else (num_time_buckets or 1)
+    desc = attn_desc(len(host) - 1, H, d_qk, d_v, max_seq_len, P, T, _dtype_code(q))
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    drp = drt = None
+    if rab_grads:
+        drp = torch.empty((H, P), dtype=torch.float32, device=q.device)
+        drt = torch.empty((H, T), dtype=torch.float32, device=q.device)
+    n = ctypes.c_size_t(0)
+    _check(lib.hstu_attn_bwd_workspace_size(ctypes.byref(desc), _i64p(host), ctypes.byref(n)))
+    ws, nbytes = _workspace(n.value, q.device, workspace)
+    _check(lib.hstu_attn_bwd(ctypes.byref(desc), _i64p(host), _ptr(seq_offsets), _ptr(timestamps),
+                             _ptr(q), _ptr(k), _ptr(v), _ptr(rab_pos), _ptr(rab_time),
+                             _ptr(d_out), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(drp), _ptr(drt),
+                             _ptr(ws), nbytes, _stream(stream)))
+    return dq, dk, dv, drp, drt
 
 
 def hstu_sl_lengths(offsets_host, max_seq_len: int, alpha: float, u_keep_host):

@@ -229,6 +229,35 @@ hstu_status mfalcon_score_cached(const mfalcon_desc* desc, const int64_t* hist_o
                                  size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * hstu_attn_bwd: gradients of hstu_attn_fwd without the gate (eq. 2), for
+ * training (the HSTU chapter trains the model generatively). With g = d_out,
+ * the gradient of a loss with respect to the attention output [T_tot, H, d_v]:
+ *   z_ij = q_i.k_j + bias(i, j), a_ij = SiLU(z_ij) / N        (visible j <= i)
+ *   dv_j = sum_i a_ij g_i
+ *   dz_ij = (g_i.v_j) SiLU'(z_ij) / N
+ *   dq_i = sum_j dz_ij k_j,  dk_j = sum_i dz_ij q_i
+ *   d_rab_pos[h][p]  = sum of dz_ij over the pairs of head h in position bucket p
+ *   d_rab_time[h][t] = sum of dz_ij over the pairs of head h in time bucket t
+ * Inputs are those of the forward call (same layouts and dtype). dq, dk, dv
+ * (same shapes and dtype as q, k, v) are overwritten. d_rab_pos [H][P] and
+ * d_rab_time [H][T] are fp32 and overwritten. Pass NULL for either to skip
+ * it. A NULL table still gets its gradient. So does the time table without
+ * timestamps, which is then zero. The table gradients need P + T <= 2048
+ * (HSTU_UNSUPPORTED otherwise). dq, dk and dv are summed in a fixed order, so
+ * they repeat bit for bit. The table gradients are summed per workgroup with
+ * LDS atomics, so they can differ run to run in the last bits.
+ * `workspace` is hstu_attn_bwd_workspace_size bytes.
+ * ---------------------------------------------------------------------- */
+hstu_status hstu_attn_bwd_workspace_size(const hstu_attn_desc* desc,
+                                         const int64_t* seq_offsets_host, size_t* bytes);
+hstu_status hstu_attn_bwd(const hstu_attn_desc* desc, const int64_t* seq_offsets_host,
+                          const int64_t* seq_offsets, const int64_t* timestamps, const void* q,
+                          const void* k, const void* v, const float* rab_pos,
+                          const float* rab_time, const void* d_out, void* dq, void* dk, void* dv,
+                          float* d_rab_pos, float* d_rab_time, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Stochastic Length (HSTU chapter, "Three more scaling components",
  * Stochastic Length): training keeps the full history of short users and of a
  * few long ones, and cuts the rest to a random subsequence of the target

@@ -46,8 +46,8 @@ import numpy as np
 
 from . import hstu_oracle as F
 
-__all__ = ["silu_grad", "attention_backward", "gate_backward", "layer_backward",
-           "LayerGrads"]
+__all__ = ["silu_grad", "attention_backward", "attention_backward_rows", "gate_backward",
+           "layer_backward", "LayerGrads"]
 
 
 def _f64(a):
@@ -77,7 +77,9 @@ def attention_backward(offsets, ts, q, k, v, rab_pos, rab_time, N, d_out, P=None
 
     q, k [T_tot, H, d_qk]; v, d_out [T_tot, H, d_v]. Returns
     (dq, dk, dv, d_rab_pos [H, P] or None, d_rab_time [H, T] or None), fp64.
-    P and T give the table widths when a table is absent but its gradient is wanted."""
+    P and T give the table widths when a table is absent but its gradient is wanted: an
+    absent table counts as zeros, and the time table's gradient needs timestamps (it is
+    zero without them)."""
     offsets = np.asarray(offsets, dtype=np.int64)
     q, k, v, g = _f64(q), _f64(k), _f64(v), _f64(d_out)
     Ttot, H, dqk = q.shape
@@ -86,15 +88,16 @@ def attention_backward(offsets, ts, q, k, v, rab_pos, rab_time, N, d_out, P=None
     dv = np.zeros_like(v)
     P = rab_pos.shape[1] if rab_pos is not None else P
     T = rab_time.shape[1] if rab_time is not None else T
-    use_time = rab_time is not None and ts is not None
-    drp = np.zeros((H, P)) if rab_pos is not None else None
-    drt = np.zeros((H, T)) if rab_time is not None else None
+    have_ts = ts is not None
+    use_time = rab_time is not None and have_ts
+    drp = np.zeros((H, P)) if P else None
+    drt = np.zeros((H, T)) if T else None  # stays zero without timestamps
     for b in range(len(offsets) - 1):
         s, e = int(offsets[b]), int(offsets[b + 1])
         n = e - s
         if n == 0:
             continue
-        t = np.asarray(ts, np.int64)[s:e] if use_time else None
+        t = np.asarray(ts, np.int64)[s:e] if have_ts else None
         pos = np.arange(n, dtype=np.int64)
         vis = pos[None, :] <= pos[:, None]
         bp, bt = _buckets(n, t, P if P else 1, T if T else 1)
@@ -109,9 +112,48 @@ def attention_backward(offsets, ts, q, k, v, rab_pos, rab_time, N, d_out, P=None
             dk[s:e, h] = dz.T @ q[s:e, h]
             if drp is not None:
                 drp[h] += np.bincount(bp[vis], weights=dz[vis], minlength=P)
-            if drt is not None and use_time:
+            if drt is not None and have_ts:
                 drt[h] += np.bincount(bt[vis], weights=dz[vis], minlength=T)
     return dq, dk, dv, drp, drt
+
+
+def attention_backward_rows(offsets, ts, q, k, v, rab_pos, rab_time, N, d_out, rows):
+    """dq, dk and dv of selected global rows, each from its own definition: dq_i needs
+    row i of dz (keys j <= i), dk_j and dv_j need column j of dz and a (queries i >= j).
+    For checking long sequences one row at a time. Returns fp64 arrays [len(rows), H, d]."""
+    offsets = np.asarray(offsets, dtype=np.int64)
+    q, k, v, g = _f64(q), _f64(k), _f64(v), _f64(d_out)
+    H = q.shape[1]
+    use_time = rab_time is not None and ts is not None
+    tsa = np.asarray(ts, np.int64) if use_time else None
+    dq = np.zeros((len(rows), H, q.shape[2]))
+    dk = np.zeros((len(rows), H, k.shape[2]))
+    dv = np.zeros((len(rows), H, v.shape[2]))
+    for idx, r in enumerate(rows):
+        r = int(r)
+        b = int(np.searchsorted(offsets, r, side="right")) - 1
+        s, e = int(offsets[b]), int(offsets[b + 1])
+        p = r - s
+        keys = np.arange(p + 1)           # keys seen by query p
+        qrys = np.arange(p, e - s)        # queries that see key p
+        for h in range(H):
+            # row p of the pair matrices: query p against keys 0..p
+            bias = F.bias_matrix(h, np.array([p]), keys, tsa[r:r + 1] if use_time else None,
+                                 tsa[s:s + p + 1] if use_time else None, rab_pos,
+                                 rab_time if use_time else None)[0]
+            z = k[s:s + p + 1, h] @ q[r, h] + bias
+            dz = (v[s:s + p + 1, h] @ g[r, h]) * silu_grad(z) / float(N)
+            dq[idx, h] = dz @ k[s:s + p + 1, h]
+            # column p: queries p..n-1 against key p
+            bias = F.bias_matrix(h, qrys, np.array([p]), tsa[s + p:e] if use_time else None,
+                                 tsa[r:r + 1] if use_time else None, rab_pos,
+                                 rab_time if use_time else None)[:, 0]
+            z = q[s + p:e, h] @ k[r, h] + bias
+            a = F.silu(z) / float(N)
+            dzc = (g[s + p:e, h] @ v[r, h]) * silu_grad(z) / float(N)
+            dk[idx, h] = dzc @ q[s + p:e, h]
+            dv[idx, h] = a @ g[s + p:e, h]
+    return dq, dk, dv
 
 
 def gate_backward(o, u, gamma, beta, eps, d_out):

@@ -143,3 +143,22 @@ def test_layer_gradients_by_finite_differences(residual):
         pick = flat if len(flat) <= 40 else [flat[i] for i in rng.choice(len(flat), 40, False)]
         for idx in pick:
             _close(grad[idx], _fd(loss, arr, idx), f"d{name}{idx}")
+
+
+def test_sampled_rows_equal_the_full_backward():
+    off, ts, q, k, v, rp, rt, g, N = _attn_case(7)
+    dq, dk, dv, _, _ = BW.attention_backward(off, ts, q, k, v, rp, rt, N, g)
+    rows = np.arange(int(off[-1]))
+    sq, sk, sv = BW.attention_backward_rows(off, ts, q, k, v, rp, rt, N, g, rows)
+    assert np.allclose(sq, dq, rtol=1e-12, atol=1e-14)
+    assert np.allclose(sk, dk, rtol=1e-12, atol=1e-14)
+    assert np.allclose(sv, dv, rtol=1e-12, atol=1e-14)
+
+
+def test_absent_tables_count_as_zeros():
+    off, ts, q, k, v, rp, rt, g, N = _attn_case(8)
+    zp, zt = np.zeros_like(rp), np.zeros_like(rt)
+    want = BW.attention_backward(off, ts, q, k, v, zp, zt, N, g)
+    got = BW.attention_backward(off, ts, q, k, v, None, None, N, g, P=rp.shape[1], T=rt.shape[1])
+    for a, b in zip(want, got):
+        assert np.array_equal(a, b)
