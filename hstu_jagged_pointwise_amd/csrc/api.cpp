@@ -170,25 +170,32 @@ hstu_status plan_attn(const hstu_attn_desc* d, const int64_t* off_host, bool gat
 }
 
 // ---------------------------------------------------------------- attention backward
-constexpr int kBwdRows = kSimpleRows;   // query and key tile of the backward kernels
 constexpr int kMaxBiasBins = 2048;      // P + T limit of the bias-table gradient
+
+bool bwd_uses_mfma(const hstu_attn_desc* d) {
+  return attn_bwd_mfma_supported(d->dtype == HSTU_BF16, d->d_qk, d->d_v, d->num_pos_buckets);
+}
+int bwd_tile_rows(const hstu_attn_desc* d) { return bwd_uses_mfma(d) ? kMfmaRows : kSimpleRows; }
 
 struct AttnBwdPlan {
   Jagged j;
-  size_t items = 0, partial = 0, ws = 0;
+  bool mfma = false;
+  size_t items = 0, ranges = 0, partial = 0, ws = 0;
 };
 
 hstu_status plan_attn_bwd(const hstu_attn_desc* d, const int64_t* off_host, AttnBwdPlan* p) {
   hstu_status st = check_attn_desc(d);
   if (st) return st;
-  st = check_offsets(off_host, d->batch, d->max_seq_len, kBwdRows, "seq_offsets", &p->j);
+  p->mfma = bwd_uses_mfma(d);
+  st = check_offsets(off_host, d->batch, d->max_seq_len, bwd_tile_rows(d), "seq_offsets", &p->j);
   if (st) return st;
   if ((int64_t)p->j.items * d->num_heads >= (int64_t(1) << 31))
     return fail(HSTU_UNSUPPORTED, "too many tiles for one launch");
   p->items = (size_t)p->j.items * sizeof(int2);
+  p->ranges = p->mfma ? (size_t)key_range_slots(p->j.total, d->batch) * sizeof(KeyRange) : 0;
   const int64_t bins = (int64_t)d->num_pos_buckets + d->num_time_buckets;
   p->partial = bins <= kMaxBiasBins ? (size_t)p->j.items * d->num_heads * bins * sizeof(float) : 0;
-  p->ws = align_up(p->items) + align_up(p->partial);
+  p->ws = align_up(p->items) + align_up(p->ranges) + align_up(p->partial);
   return HSTU_OK;
 }
 
@@ -907,10 +914,14 @@ hstu_status hstu_attn_bwd(const hstu_attn_desc* desc, const int64_t* seq_offsets
   if ((st = check_ws(workspace, workspace_bytes, p.ws, "workspace"))) return st;
   Carver c{(char*)workspace};
   int2* items = (int2*)c.take(p.items);
+  KeyRange* kr = (KeyRange*)c.take(p.ranges);
   float* partial = (float*)c.take(p.partial);
-  HSTU_TRY(launch_plan_causal(seq_offsets, desc->batch, kBwdRows, p.j.max_tiles, items,
+  HSTU_TRY(launch_plan_causal(seq_offsets, desc->batch, bwd_tile_rows(desc), p.j.max_tiles, items,
                               (int)p.j.items, s),
            "tile planner");
+  if (p.mfma && timestamps)
+    HSTU_TRY(launch_key_ranges(seq_offsets, timestamps, desc->batch, p.j.max_len, kr, s),
+             "key ranges");
   AttnBwdArgs a{};
   a.q = q;
   a.k = k;
@@ -926,6 +937,7 @@ hstu_status hstu_attn_bwd(const hstu_attn_desc* desc, const int64_t* seq_offsets
   a.rab_pos = rab_pos;
   a.rab_time = rab_time;
   a.bias_partial = want_bias ? partial : nullptr;
+  a.key_ranges = (p.mfma && timestamps) ? kr : nullptr;
   a.items = items;
   a.n_items = (int)p.j.items;
   a.batch = desc->batch;
@@ -935,7 +947,10 @@ hstu_status hstu_attn_bwd(const hstu_attn_desc* desc, const int64_t* seq_offsets
   a.P = desc->num_pos_buckets;
   a.T = desc->num_time_buckets;
   a.inv_n = 1.0f / (float)desc->max_seq_len;
-  HSTU_TRY(launch_attn_bwd_simple(a, desc->dtype == HSTU_BF16, s), "attention backward");
+  if (p.mfma)
+    HSTU_TRY(launch_attn_bwd_mfma(a, s), "attention backward");
+  else
+    HSTU_TRY(launch_attn_bwd_simple(a, desc->dtype == HSTU_BF16, s), "attention backward");
   if (want_bias)
     HSTU_TRY(launch_bias_grad_reduce(partial, a.n_items, a.H, a.P, a.T, d_rab_pos, d_rab_time, s),
              "bias gradient");

@@ -1,5 +1,6 @@
 // Backward pass of the HSTU pointwise attention (eq. 2, "What an HSTU layer
-// changes", HSTU chapter) on the vector ALUs, fp32 math, any supported widths.
+// changes", HSTU chapter) on the vector ALUs, any supported widths: fp32
+// accumulation, with the scores and the activation in fp64.
 //
 // Forward, per head and visible pair j <= i:
 //   z_ij = q_i.k_j + rab(i, j),  a_ij = SiLU(z_ij) / N,  o_i = sum_j a_ij v_j.
@@ -26,11 +27,14 @@ constexpr int BR = kSimpleRows;  // rows (keys or queries) owned by a workgroup
 constexpr int BS = 16;           // rows of the other side per LDS step
 constexpr int kBwdWaves = 4;
 
-// SiLU(z) / N and SiLU'(z) / N from one sigmoid.
-__device__ __forceinline__ void silu_and_grad(float z, float inv_n, float* a, float* da) {
-  const float sg = 1.0f / (1.0f + expf(-z));
-  *a = z * sg * inv_n;
-  *da = sg * (1.0f + z * (1.0f - sg)) * inv_n;
+// SiLU(z) / N and SiLU'(z) / N from one sigmoid, in fp64. Where z is very negative,
+// a = SiLU(z) / N is tiny and its relative error equals the absolute error of z,
+// so z (the q.k and g.v dot products) is accumulated in fp64 too: a key near the
+// end of a sequence has few queries, and its dv and dk rows are made of such terms.
+__device__ __forceinline__ void silu_and_grad(double z, float inv_n, float* a, float* da) {
+  const double sg = 1.0 / (1.0 + exp(-z));
+  *a = (float)(z * sg * (double)inv_n);
+  *da = (float)(sg * (1.0 + z * (1.0 - sg)) * (double)inv_n);
 }
 
 __device__ __forceinline__ int time_bucket_clamped(int64_t tq, int64_t tk, int T) {
@@ -133,19 +137,19 @@ __global__ __launch_bounds__(256) void attn_bwd_kv_simple(AttnBwdArgs a) {
         const int64_t i = q0 + qi;
         float p = 0.f, dz = 0.f;
         if (row_ok && i < t.n && j <= i) {
-          float s = 0.f, dp = 0.f;
+          double s = 0.0, dp = 0.0;
 #pragma unroll 8
-          for (int c = 0; c < DQK; ++c) s = fmaf(Qs[qi][c], Ks[row][c], s);
+          for (int c = 0; c < DQK; ++c) s = fma((double)Qs[qi][c], (double)Ks[row][c], s);
 #pragma unroll 8
-          for (int c = 0; c < DV; ++c) dp = fmaf(Gs[qi][c], Vs[row][c], dp);
+          for (int c = 0; c < DV; ++c) dp = fma((double)Gs[qi][c], (double)Vs[row][c], dp);
           const int bp = pos_bucket((int)(i - j), a.P);
           const int bt = has_time ? time_bucket_clamped(tqs[qi], tk, a.T) : 0;
-          float z = s;
+          double z = s;
           if (rp) z += rp[bp];
           if (rt) z += rt[bt];
           float dsl;
           silu_and_grad(z, a.inv_n, &p, &dsl);
-          dz = dp * dsl;
+          dz = (float)(dp * (double)dsl);
           if (a.bias_partial) {
             atomicAdd(&my_bins[bp], dz);
             if (has_time) atomicAdd(&my_bins[a.P + bt], dz);
@@ -240,17 +244,17 @@ __global__ __launch_bounds__(256) void attn_bwd_q_simple(AttnBwdArgs a) {
       const int64_t j = k0 + key;
       float dz = 0.f;
       if (row_ok && j <= i) {
-        float s = 0.f, dp = 0.f;
+        double s = 0.0, dp = 0.0;
 #pragma unroll 8
-        for (int c = 0; c < DQK; ++c) s = fmaf(Qs[row][c], Ks[key][c], s);
+        for (int c = 0; c < DQK; ++c) s = fma((double)Qs[row][c], (double)Ks[key][c], s);
 #pragma unroll 8
-        for (int c = 0; c < DV; ++c) dp = fmaf(Gs[row][c], Vs[key][c], dp);
-        float z = s;
+        for (int c = 0; c < DV; ++c) dp = fma((double)Gs[row][c], (double)Vs[key][c], dp);
+        double z = s;
         if (rp) z += rp[pos_bucket((int)(i - j), a.P)];
         if (rt) z += rt[time_bucket_clamped(tq, tks[key], a.T)];
         float p, dsl;
         silu_and_grad(z, a.inv_n, &p, &dsl);
-        dz = dp * dsl;
+        dz = (float)(dp * (double)dsl);
       }
       Zs[row][key] = dz;
     }

@@ -89,13 +89,18 @@ struct AttnBwdArgs {
   const float* rab_pos;       // [H][P] or NULL (= 0)
   const float* rab_time;      // [H][T] or NULL (= 0)
   float* bias_partial;        // [n_items][H][P + T] bucket sums of dz per work item, or NULL
-  const int2* items;          // (sequence, tile) list from the planner, 64-row tiles
+  const KeyRange* key_ranges; // per 32-row timestamp ranges (MFMA kernels, with ts), else NULL
+  const int2* items;          // (sequence, tile) list from the planner (64-row tiles for the
+                              // vector-ALU kernels, 128-row tiles for the MFMA kernels)
   int n_items;
   int batch, H, d_qk, d_v, P, T;
   float inv_n;
 };
 
 hipError_t launch_attn_bwd_simple(const AttnBwdArgs& a, int use_bf16, hipStream_t s);
+// True when the MFMA backward handles this shape (bf16, d_qk == d_v in {32,64,128}, P <= 1024).
+bool attn_bwd_mfma_supported(int dtype_bf16, int d_qk, int d_v, int P);
+hipError_t launch_attn_bwd_mfma(const AttnBwdArgs& a, hipStream_t s);
 // d_rab_pos[h][p] / d_rab_time[h][t] = fixed-order sums of the per-item partials
 // (partial may be NULL when n_items is 0; the outputs are then zeros).
 hipError_t launch_bias_grad_reduce(const float* partial, int n_items, int H, int P, int T,

@@ -76,12 +76,14 @@ def test_ragged_tiles(dtype, dqk, dv):
     check_all(x, bwd_gpu(x, g), bwd_oracle(x, g), f"ragged {dtype} {dqk}/{dv}")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("variant", ["no_timestamps", "no_tables", "no_table_grads", "pos_clamp"])
-def test_bias_variants(variant):
+def test_bias_variants(variant, dtype):
+    """P = 8 makes most blocks of the 600-long sequence take one position bucket."""
     P = 8 if variant == "pos_clamp" else 128
-    x = synth.make_attn(13, lambda r: np.array([200, 37, 90]), 2, 64, 64, P, 64, "f32")
+    x = synth.make_attn(13, lambda r: np.array([600, 37, 90]), 2, 64, 64, P, 64, dtype)
     g = _grad_out(x, 14)
-    announce(f"attn bwd bias variant {variant}")
+    announce(f"attn bwd bias variant {variant} {dtype}")
     if variant == "no_timestamps":
         check_all(x, bwd_gpu(x, g, ts=None), bwd_oracle(x, g, ts=None), variant)
     elif variant == "no_tables":
