@@ -22,14 +22,21 @@
 //   dV += P^T G and dK += dZ^T Q, with G and Q read transposed from LDS.
 // The key-side kernel also sums dz per bias bucket into per-wavefront LDS bins,
 // which are written as one partial row per work item and reduced in a fixed order.
+// Most pairs of a block share a time bucket, so a per-element atomic would make the
+// 64 lanes collide on one address: time buckets are summed by wavefront
+// reductions, one per bucket in the block's range, and the clamped position bucket
+// in a register. Only position buckets below the clamp, which differ across the
+// lanes of an instruction, use LDS atomics.
 //
 // Bias per 32x32 block (wavefront-uniform): the position bucket min(i-j, P-1) is
 // the constant P-1 when every i - j >= P - 1. The time bucket is monotone in the
 // elapsed time, so it is one constant when the buckets of the block's smallest and
 // largest elapsed times agree (from the per-32-row timestamp ranges). A block that
 // is fully visible with both constant takes the bias as one scalar and adds the
-// block's dz sum to two bins; any other block computes buckets, mask and bins per
-// element.
+// block's dz sum to two bins. One whose time range covers two adjacent buckets
+// b, b+1 selects between two scalars per element (a pair is in b+1 exactly when
+// dt + 1 >= 2^(b+1), a 32-bit compare when the block's elapsed times fit) and
+// keeps two sums. Any other block computes buckets, mask and bins per element.
 #include "attn_common.h"
 
 namespace hstu {
@@ -167,6 +174,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_q_mfma(AttnBwdArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 Ks[2][TR * (D + 8)];
   __shared__ __attribute__((aligned(16))) bf16 Vs[2][TR * (D + 8)];
   __shared__ int64_t tks[2][TR];
+  __shared__ uint32_t tks32[2][TR];  // low words, for the two-bucket test
   __shared__ float rps[kMaxPosB];
   __shared__ float rts[kTimeB];
 
@@ -214,7 +222,11 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_q_mfma(AttnBwdArgs a) {
   };
   auto load_ts = [&](int kt, int buf) {
     const int64_t k0 = (int64_t)kt * TR;
-    if (tid < TR) tks[buf][tid] = (has_ts && k0 + tid < kend) ? a.ts[t.base + k0 + tid] : 0;
+    if (tid < TR) {
+      const int64_t tv = (has_ts && k0 + tid < kend) ? a.ts[t.base + k0 + tid] : 0;
+      tks[buf][tid] = tv;
+      tks32[buf][tid] = (uint32_t)tv;
+    }
   };
   load_tile(0);
   st.store(Ks[0], Vs[0]);
@@ -241,10 +253,12 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_q_mfma(AttnBwdArgs a) {
       const bool full = q0w >= k0b + 31 && q0w + 31 < t.n;
       const bool posc = q0w - (k0b + 31) >= a.P - 1;
       int blo = 0, bhi = 0;
+      bool fits32 = true;
       if (has_ts) {
         const KeyRange kr = block_range(a, t, k0b);
         blo = tbucket(qr.lo - kr.hi, a.T);
         bhi = tbucket(qr.hi - kr.lo, a.T);
+        fits32 = time_fast_ok(qr.lo, qr.hi, kr.lo, kr.hi);
       }
       bf16x8 pz[2];
       if (full && posc && blo == bhi) {
@@ -253,6 +267,19 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_q_mfma(AttnBwdArgs a) {
         for (int r = 0; r < 16; ++r) {
           float p, dsl;
           silu2(s[r] + bias, a.inv_n, p, dsl);
+          pz[r >> 3][r & 7] = (bf16)(dp[r] * dsl);
+        }
+      } else if (full && posc && bhi == blo + 1 && fits32) {
+        // two adjacent time buckets: a pair is in bhi exactly when dt + 1 >= 2^bhi,
+        // and dt + 1 is the wrapped 32-bit difference of the low words
+        const float b_lo = rps[a.P - 1] + rts[blo], b_hi = rps[a.P - 1] + rts[bhi];
+        const int thr = 1 << bhi;
+        const uint32_t tq1 = (uint32_t)tq + 1u;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int d = (int)(tq1 - tks32[buf][32 * kb + acc_row(r, hl)]);
+          float p, dsl;
+          silu2(s[r] + (d >= thr ? b_hi : b_lo), a.inv_n, p, dsl);
           pz[r >> 3][r & 7] = (bf16)(dp[r] * dsl);
         }
       } else {
@@ -298,6 +325,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kv_mfma(AttnBwdArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 Qs[2][TR * (D + 8)];
   __shared__ __attribute__((aligned(16))) bf16 Gs[2][TR * (D + 8)];
   __shared__ int64_t tqs[2][TR];
+  __shared__ uint32_t tqs32[2][TR];  // low words, for the two-bucket test
   __shared__ float rps[kMaxPosB];
   __shared__ float rts[kTimeB];
   extern __shared__ float bins[];  // [4][P + TT] when bias_partial is set
@@ -350,7 +378,11 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kv_mfma(AttnBwdArgs a) {
     };
     auto load_ts = [&](int qt, int buf) {
       const int64_t q0 = qbeg + (int64_t)qt * TR;
-      if (tid < TR) tqs[buf][tid] = (has_ts && q0 + tid < t.n) ? a.ts[t.base + q0 + tid] : 0;
+      if (tid < TR) {
+        const int64_t tv = (has_ts && q0 + tid < t.n) ? a.ts[t.base + q0 + tid] : 0;
+        tqs[buf][tid] = tv;
+        tqs32[buf][tid] = (uint32_t)tv;
+      }
     };
     load_tile(0);
     st.store(Qs[0], Gs[0]);
@@ -376,10 +408,12 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kv_mfma(AttnBwdArgs a) {
         const bool full = q0b >= k0w + 31 && q0b + 31 < t.n && k0w + 31 < t.n;
         const bool posc = q0b - (k0w + 31) >= a.P - 1;
         int blo = 0, bhi = 0;
+        bool fits32 = true;
         if (has_ts) {
           const KeyRange qr = block_range(a, t, q0b);
           blo = tbucket(qr.lo - kr.hi, a.T);
           bhi = tbucket(qr.hi - kr.lo, a.T);
+          fits32 = time_fast_ok(qr.lo, qr.hi, kr.lo, kr.hi);
         }
         bf16x8 pp[2], pz[2];
         if (full && posc && blo == bhi) {
@@ -401,7 +435,36 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kv_mfma(AttnBwdArgs a) {
               if (lane == 0) my_bins[a.P + blo] += tot;  // lane 0 alone writes its wave's bins here
             }
           }
+        } else if (full && posc && bhi == blo + 1 && fits32) {
+          // two adjacent time buckets (see the query side)
+          const float b_lo = rps[a.P - 1] + rts[blo], b_hi = rps[a.P - 1] + rts[bhi];
+          const int thr = 1 << bhi;
+          const uint32_t tk32 = (uint32_t)tk;
+          float zlo = 0.f, zhi = 0.f;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int d = (int)(tqs32[buf][32 * qb + acc_row(r, hl)] + 1u - tk32);
+            const bool up = d >= thr;
+            float p, dsl;
+            silu2(s[r] + (up ? b_hi : b_lo), a.inv_n, p, dsl);
+            const float dz = dp[r] * dsl;
+            pp[r >> 3][r & 7] = (bf16)p;
+            pz[r >> 3][r & 7] = (bf16)dz;
+            zhi += up ? dz : 0.f;
+            zlo += up ? 0.f : dz;
+          }
+          if (a.bias_partial) {
+            bin_clamp += zlo + zhi;
+            const float tlo = wave_sum64(zlo), thi = wave_sum64(zhi);
+            if (lane == 0) {
+              my_bins[a.P + blo] += tlo;
+              my_bins[a.P + bhi] += thi;
+            }
+          }
         } else {
+          int btv[16];
+          float zv[16];
+          float csum = 0.f;  // this lane's dz in position bucket P-1
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int ir = 32 * qb + acc_row(r, hl);  // query row within the tile
@@ -415,10 +478,28 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kv_mfma(AttnBwdArgs a) {
             const float dz = vis ? dp[r] * dsl : 0.f;
             pp[r >> 3][r & 7] = (bf16)(vis ? p : 0.f);
             pz[r >> 3][r & 7] = (bf16)dz;
-            if (a.bias_partial && vis) {
-              atomicAdd(&my_bins[bp], dz);
-              if (has_ts) atomicAdd(&my_bins[a.P + bt], dz);
+            btv[r] = bt;
+            zv[r] = dz;
+            // below the clamp, the lanes of one slot (one query, 32 keys) hold distinct
+            // buckets, so these atomics do not collide
+            if (a.bias_partial) {
+              if (bp == a.P - 1)
+                csum += dz;
+              else if (vis)
+                atomicAdd(&my_bins[bp], dz);
             }
+          }
+          if (a.bias_partial) {
+            bin_clamp += csum;
+            // every visible pair's time bucket lies in [blo, bhi]: one reduction per bucket
+            if (has_ts)
+              for (int b = blo; b <= bhi; ++b) {
+                float tb = 0.f;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) tb += btv[r] == b ? zv[r] : 0.f;
+                tb = wave_sum64(tb);
+                if (lane == 0) my_bins[a.P + b] += tb;
+              }
           }
         }
 #pragma unroll

@@ -164,3 +164,16 @@ def test_long_sequences_full_size():
         sp, st = drp[h].double().sum().item(), drt[h].double().sum().item()
         mag = drp[h].double().abs().sum().item() + drt[h].double().abs().sum().item()
         assert abs(sp - st) <= 1e-4 * mag, f"table sums, head {h}"
+
+
+@pytest.mark.parametrize("gap", [700, 3])
+def test_even_timestamps_two_bucket_blocks(gap):
+    """Timestamps `gap` seconds apart with 8 position buckets: away from the diagonal most
+    32x32 blocks have one position bucket and an elapsed-time range that covers one or
+    two adjacent time buckets, so the constant and two-bucket block paths carry most of
+    the work; the table gradients check their bucket sums."""
+    x = synth.make_attn(21, lambda r: np.array([1024, 333]), 2, 64, 64, 8, 64, "bf16")
+    x.ts = (np.concatenate([np.arange(1024), np.arange(333)]) * gap + 1_700_000_000).astype(np.int64)
+    g = _grad_out(x, 22)
+    announce(f"attn bwd even timestamps gap={gap}")
+    check_all(x, bwd_gpu(x, g), bwd_oracle(x, g), f"even ts {gap}")
