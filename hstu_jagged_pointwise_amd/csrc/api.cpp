@@ -11,6 +11,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "kernels.h"
@@ -610,6 +611,262 @@ hstu_status check_candidate_args(const MfPlan& p, const int64_t* hist_offsets,
   return HSTU_OK;
 }
 
+// ---------------------------------------------------------------- layer backward
+// Gradients of a stack of HSTU layers (eqs. 1-3). The forward pass is recomputed:
+// the inputs of layers 1..L-1 are kept in the workspace, and each layer's f1
+// pre-activation, attention output and gate are recomputed just before its
+// backward. The weight gradients reduce over tokens; they are GEMMs of transposed
+// row-major activations, split over the token range when the output has few tiles
+// (fp32 partials added in a fixed order).
+struct LayerBwdPlan {
+  Jagged j;
+  int64_t Tp = 0;                // rows padded to a multiple of 32
+  int split1 = 1, split2 = 1;    // split-K of dW1 and dW2
+  int64_t ks1 = 0, ks2 = 0;
+  int ln_blocks = 0;
+  bool bias_ok = false;          // P + T small enough for the bias-table gradient
+  size_t ws = 0;
+};
+
+struct LayerBwdBufs {
+  int2* items;
+  KeyRange* kr;
+  char* xs;       // inputs of layers 1..L-1
+  float* z1;      // f1 pre-activation (fp32)
+  void* uvqk;     // SiLU(z1)
+  float* o;       // attention output (fp32)
+  void* g;        // gated value G
+  void* dg;       // dL/dG
+  void* d_o;      // dL/d(attention output)
+  void* dact;     // dL/d[U|V|Q|K], then dL/dz1 in place
+  void* dyb[2];   // dL/dX of inner layers (ping-pong)
+  void* ta;       // transposed operands of the weight-gradient GEMMs
+  void* tb;
+  void* w1t;
+  void* w2t;
+  float* wpart;   // split-K partials
+  float* bpart;   // bias-table partials
+  float* lnpart;  // dgamma, dbeta partials
+  float* cpart;   // column-sum partials
+};
+
+void split_k(int64_t M, int64_t N, int64_t K, bool bf, int* splits, int64_t* ks) {
+  if (!bf || K <= 0) {
+    *splits = 1;
+    *ks = K;
+    return;
+  }
+  const int64_t tiles = ((M + 63) / 64) * ((N + 63) / 64);
+  int64_t sp = std::max<int64_t>(1, 512 / std::max<int64_t>(tiles, 1));
+  sp = std::min<int64_t>(sp, std::max<int64_t>(1, K / 256));
+  int64_t k = (K + sp - 1) / sp;
+  k = (k + 31) / 32 * 32;
+  *splits = (int)((K + k - 1) / k);
+  *ks = k;
+}
+
+void carve_layer_bwd(Carver& c, const hstu_layer_desc* d, const LayerBwdPlan& p, LayerBwdBufs* b) {
+  const hstu_attn_desc& a = d->attn;
+  const size_t es = elt_size(a.dtype);
+  const int64_t T = p.j.total, F1 = 2LL * a.num_heads * (a.d_v + a.d_qk);
+  const int64_t hv = (int64_t)a.num_heads * a.d_v, dm = d->d_model;
+  const bool bf = a.dtype == HSTU_BF16;
+  b->items = (int2*)c.take((size_t)p.j.items * sizeof(int2));
+  b->kr = (KeyRange*)c.take(key_range_bytes(&a, T));
+  b->xs = (char*)c.take((size_t)(d->num_layers - 1) * T * dm * es);
+  b->z1 = (float*)c.take((size_t)T * F1 * 4);
+  b->uvqk = c.take((size_t)T * F1 * es);
+  b->o = (float*)c.take((size_t)T * hv * 4);
+  b->g = c.take((size_t)T * hv * es);
+  b->dg = c.take((size_t)T * hv * es);
+  b->d_o = c.take((size_t)T * hv * es);
+  b->dact = c.take((size_t)T * F1 * es);
+  for (int i = 0; i < 2; ++i) b->dyb[i] = c.take(d->num_layers > 1 ? (size_t)T * dm * es : 0);
+  b->ta = c.take((size_t)std::max(dm, F1) * p.Tp * es);
+  b->tb = c.take((size_t)std::max(hv, dm) * p.Tp * es);
+  b->w1t = c.take((size_t)dm * F1 * es);
+  b->w2t = c.take((size_t)hv * dm * es);
+  const int64_t wp = std::max<int64_t>(p.split1 > 1 ? p.split1 * F1 * dm : 0,
+                                       p.split2 > 1 ? p.split2 * dm * hv : 0);
+  b->wpart = (float*)c.take(bf ? (size_t)wp * 4 : 0);
+  b->bpart = (float*)c.take(p.bias_ok ? (size_t)p.j.items * a.num_heads *
+                                            (a.num_pos_buckets + a.num_time_buckets) * 4
+                                      : 0);
+  b->lnpart = (float*)c.take((size_t)2 * p.ln_blocks * hv * 4);
+  b->cpart = (float*)c.take((size_t)colsum_chunks(T) * std::max(F1, dm) * 4);
+}
+
+hstu_status plan_layer_bwd(const hstu_layer_desc* d, const int64_t* off_host, LayerBwdPlan* p) {
+  hstu_status st = check_layer_desc(d);
+  if (st) return st;
+  const hstu_attn_desc& a = d->attn;
+  if ((int64_t)a.num_heads * a.d_v > 1024)
+    return fail(HSTU_UNSUPPORTED, "the layer backward needs H*d_v <= 1024");
+  if (attn_tile_rows(&a) != bwd_tile_rows(&a))
+    return fail(HSTU_UNSUPPORTED, "attention forward and backward disagree on the tile");
+  st = check_offsets(off_host, a.batch, a.max_seq_len, attn_tile_rows(&a), "seq_offsets", &p->j);
+  if (st) return st;
+  if ((int64_t)p->j.items * a.num_heads >= (int64_t(1) << 31))
+    return fail(HSTU_UNSUPPORTED, "too many query tiles for one launch");
+  const bool bf = a.dtype == HSTU_BF16;
+  const int64_t T = p->j.total, F1 = 2LL * a.num_heads * (a.d_v + a.d_qk);
+  const int64_t hv = (int64_t)a.num_heads * a.d_v, dm = d->d_model;
+  p->Tp = (T + 31) / 32 * 32;
+  split_k(F1, dm, p->Tp, bf, &p->split1, &p->ks1);
+  split_k(dm, hv, p->Tp, bf, &p->split2, &p->ks2);
+  p->ln_blocks = ln_gate_bwd_blocks(T);
+  p->bias_ok = (int64_t)a.num_pos_buckets + a.num_time_buckets <= kMaxBiasBins;
+  Carver c{nullptr};
+  LayerBwdBufs b;
+  carve_layer_bwd(c, d, *p, &b);
+  p->ws = c.off;
+  return HSTU_OK;
+}
+
+// dW [M, N] (fp32) = A [M, K] W [N, K]^T, both operands transposed activations.
+hstu_status weight_grad(const void* A, const void* W, int64_t M, int N, int64_t K, int splits,
+                        int64_t ks, bool bf, float* wpart, float* out, hipStream_t s) {
+  if (splits <= 1) {
+    HSTU_TRY(launch_gemm_ex(A, K, W, K, nullptr, nullptr, 0, out, N, M, N, (int)K, 0, bf, 1, 1, K, 0,
+                            s),
+             "weight gradient");
+    return HSTU_OK;
+  }
+  HSTU_TRY(launch_gemm_ex(A, K, W, K, nullptr, nullptr, 0, wpart, N, M, N, (int)K, 0, bf, 1, splits,
+                          ks, M * N, s),
+           "weight gradient");
+  HSTU_TRY(launch_sum_rows(wpart, M * N, splits, M * N, out, s), "split-K sum");
+  return HSTU_OK;
+}
+
+// Zero gradients of one layer (no tokens).
+hstu_status zero_layer_grads(const hstu_layer_desc* d, const hstu_layer_grads* g, hipStream_t s) {
+  const hstu_attn_desc& a = d->attn;
+  const int64_t F1 = 2LL * a.num_heads * (a.d_v + a.d_qk);
+  const int64_t hv = (int64_t)a.num_heads * a.d_v, dm = d->d_model;
+  const std::pair<float*, int64_t> all[] = {{g->dw1, F1 * dm}, {g->db1, F1}, {g->dw2, dm * hv},
+                                            {g->db2, dm}, {g->d_ln_gamma, hv}, {g->d_ln_beta, hv}};
+  for (const auto& z : all) HSTU_TRY(launch_sum_rows(nullptr, 0, 0, z.second, z.first, s), "zero");
+  HSTU_TRY(launch_bias_grad_reduce(nullptr, 0, a.num_heads, a.num_pos_buckets, a.num_time_buckets,
+                                   g->d_rab_pos, g->d_rab_time, s),
+           "zero");
+  return HSTU_OK;
+}
+
+// Backward of one layer: reads its input xl and dL/dY, writes dL/dX (if dX) and the
+// parameter gradients in g (each pointer optional).
+hstu_status layer_bwd_once(const hstu_layer_desc* d, const LayerBwdPlan& p, const int64_t* off,
+                           const int64_t* ts, const void* xl, const hstu_layer_weights& w,
+                           const hstu_layer_grads* g, const void* dY, void* dX,
+                           const LayerBwdBufs& b, hipStream_t s) {
+  const hstu_attn_desc& a = d->attn;
+  const int bf = a.dtype == HSTU_BF16;
+  const int64_t T = p.j.total, F1 = 2LL * a.num_heads * (a.d_v + a.d_qk);
+  const int hv = a.num_heads * a.d_v, dm = d->d_model;
+  const hstu_layer_grads none{};
+  if (!g) g = &none;
+  // forward pieces: z1, SiLU(z1), attention output, gate
+  HSTU_TRY(launch_gemm_ex(xl, dm, w.w1, dm, w.b1, nullptr, 0, b.z1, F1, T, (int)F1, dm, 0, bf, 1, 1,
+                          dm, 0, s),
+           "f1 pre-activation");
+  HSTU_TRY(launch_silu_act(b.z1, F1, b.uvqk, F1, T, (int)F1, bf, s), "f1 activation");
+  const UVQK vw = split_view(b.uvqk, a);
+  AttnArgs aa = base_args(&a);
+  aa.q = vw.q;
+  aa.k = vw.k;
+  aa.v = vw.v;
+  aa.ld_q = aa.ld_k = aa.ld_v = vw.ld;
+  aa.out = b.o;
+  aa.ld_o = hv;
+  aa.out_f32 = 1;
+  aa.q_offsets = aa.k_offsets = off;
+  aa.ts_q = aa.ts_k = ts;
+  aa.rab_pos = w.rab_pos;
+  aa.rab_time = w.rab_time;
+  aa.key_ranges = (ts && w.rab_time) ? b.kr : nullptr;
+  aa.items = b.items;
+  aa.n_items = (int)p.j.items;
+  HSTU_TRY(run_attention(&a, aa, false, s), "attention");
+  HSTU_TRY(launch_ln_gate(b.o, hv, 1, 0, vw.u, vw.ld, w.ln_gamma, w.ln_beta, a.ln_eps, b.g, hv, T,
+                          hv, bf, s),
+           "layer norm gate");
+  // f2: dG = dY W2, dW2 = dY^T G, db2 = column sums of dY
+  HSTU_TRY(launch_transpose(w.w2, hv, b.w2t, dm, dm, dm, hv, bf, s), "transpose");
+  HSTU_TRY(launch_gemm_ex(dY, dm, b.w2t, dm, nullptr, nullptr, 0, b.dg, hv, T, hv, dm, 0, bf, 0, 1,
+                          dm, 0, s),
+           "dG");
+  hstu_status st;
+  if (g->dw2) {
+    HSTU_TRY(launch_transpose(dY, dm, b.ta, p.Tp, T, p.Tp, dm, bf, s), "transpose");
+    HSTU_TRY(launch_transpose(b.g, hv, b.tb, p.Tp, T, p.Tp, hv, bf, s), "transpose");
+    if ((st = weight_grad(b.ta, b.tb, dm, hv, p.Tp, p.split2, p.ks2, bf, b.wpart, g->dw2, s)))
+      return st;
+  }
+  HSTU_TRY(launch_colsum(dY, dm, T, dm, bf, b.cpart, g->db2, s), "db2");
+  // gate and norm
+  const UVQK dw = split_view(b.dact, a);
+  float* pg = b.lnpart;
+  float* pb = b.lnpart + (size_t)p.ln_blocks * hv;
+  HSTU_TRY(launch_ln_gate_bwd(b.o, hv, vw.u, vw.ld, w.ln_gamma, w.ln_beta, a.ln_eps, b.dg, hv, b.d_o,
+                              hv, const_cast<char*>(dw.u), dw.ld, pg, pb, T, hv, bf, s),
+           "gate backward");
+  HSTU_TRY(launch_sum_rows(pg, hv, p.ln_blocks, hv, g->d_ln_gamma, s), "dgamma");
+  HSTU_TRY(launch_sum_rows(pb, hv, p.ln_blocks, hv, g->d_ln_beta, s), "dbeta");
+  // attention
+  const bool want_bias = g->d_rab_pos || g->d_rab_time;
+  if (want_bias && !p.bias_ok)
+    return fail(HSTU_UNSUPPORTED, "bias-table gradients need P + T <= %d", kMaxBiasBins);
+  AttnBwdArgs ba{};
+  ba.q = vw.q;
+  ba.k = vw.k;
+  ba.v = vw.v;
+  ba.dout = b.d_o;
+  ba.dq = const_cast<char*>(dw.q);
+  ba.dk = const_cast<char*>(dw.k);
+  ba.dv = const_cast<char*>(dw.v);
+  ba.ld_q = ba.ld_k = ba.ld_v = ba.ld_dq = ba.ld_dk = ba.ld_dv = vw.ld;
+  ba.ld_do = hv;
+  ba.offsets = off;
+  ba.ts = ts;
+  ba.rab_pos = w.rab_pos;
+  ba.rab_time = w.rab_time;
+  ba.bias_partial = want_bias ? b.bpart : nullptr;
+  ba.key_ranges = (bwd_uses_mfma(&a) && ts) ? b.kr : nullptr;
+  ba.items = b.items;
+  ba.n_items = (int)p.j.items;
+  ba.batch = a.batch;
+  ba.H = a.num_heads;
+  ba.d_qk = a.d_qk;
+  ba.d_v = a.d_v;
+  ba.P = a.num_pos_buckets;
+  ba.T = a.num_time_buckets;
+  ba.inv_n = 1.0f / (float)a.max_seq_len;
+  if (bwd_uses_mfma(&a))
+    HSTU_TRY(launch_attn_bwd_mfma(ba, s), "attention backward");
+  else
+    HSTU_TRY(launch_attn_bwd_simple(ba, bf, s), "attention backward");
+  if (want_bias)
+    HSTU_TRY(launch_bias_grad_reduce(b.bpart, ba.n_items, ba.H, ba.P, ba.T, g->d_rab_pos,
+                                     g->d_rab_time, s),
+             "bias gradient");
+  // f1: dz1 = d[U|V|Q|K] SiLU'(z1), db1, dW1 = dz1^T X, dX = dz1 W1 (+ dY)
+  HSTU_TRY(launch_silu_grad(b.z1, F1, b.dact, F1, T, (int)F1, bf, s), "SiLU backward");
+  HSTU_TRY(launch_colsum(b.dact, F1, T, (int)F1, bf, b.cpart, g->db1, s), "db1");
+  if (g->dw1) {
+    HSTU_TRY(launch_transpose(b.dact, F1, b.ta, p.Tp, T, p.Tp, (int)F1, bf, s), "transpose");
+    HSTU_TRY(launch_transpose(xl, dm, b.tb, p.Tp, T, p.Tp, dm, bf, s), "transpose");
+    if ((st = weight_grad(b.ta, b.tb, F1, dm, p.Tp, p.split1, p.ks1, bf, b.wpart, g->dw1, s)))
+      return st;
+  }
+  if (dX) {
+    HSTU_TRY(launch_transpose(w.w1, dm, b.w1t, F1, F1, F1, dm, bf, s), "transpose");
+    HSTU_TRY(launch_gemm_ex(b.dact, F1, b.w1t, F1, nullptr, d->residual ? dY : nullptr, dm, dX, dm,
+                            T, dm, (int)F1, 0, bf, 0, 1, F1, 0, s),
+             "dX");
+  }
+  return HSTU_OK;
+}
+
 }  // namespace
 
 // =========================================================================
@@ -739,6 +996,69 @@ hstu_status hstu_layer_fwd(const hstu_layer_desc* desc, const int64_t* seq_offse
     st = layer_once(desc, seq_offsets, timestamps, p.j, in, weights[l], out, b, s, false);
     if (st) return st;
     in = out;
+  }
+  return HSTU_OK;
+}
+
+hstu_status hstu_layer_bwd_workspace_size(const hstu_layer_desc* desc,
+                                          const int64_t* seq_offsets_host, size_t* bytes) {
+  if (!bytes) return fail(HSTU_INVALID_ARGUMENT, "bytes is NULL");
+  LayerBwdPlan p;
+  hstu_status st = plan_layer_bwd(desc, seq_offsets_host, &p);
+  if (st) return st;
+  *bytes = p.ws;
+  return HSTU_OK;
+}
+
+hstu_status hstu_layer_bwd(const hstu_layer_desc* desc, const int64_t* seq_offsets_host,
+                           const int64_t* seq_offsets, const int64_t* timestamps, const void* x,
+                           const hstu_layer_weights* weights, const void* d_y, void* d_x,
+                           const hstu_layer_grads* grads, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  LayerBwdPlan p;
+  hstu_status st = plan_layer_bwd(desc, seq_offsets_host, &p);
+  if (st) return st;
+  if ((st = check_weights(weights, desc->num_layers))) return st;
+  const int L = desc->num_layers;
+  if (grads && !p.bias_ok)
+    for (int l = 0; l < L; ++l)
+      if (grads[l].d_rab_pos || grads[l].d_rab_time)
+        return fail(HSTU_UNSUPPORTED, "bias-table gradients need P + T <= %d", kMaxBiasBins);
+  hipStream_t s = (hipStream_t)stream;
+  if (p.j.total == 0) {
+    if (grads)
+      for (int l = 0; l < L; ++l)
+        if ((st = zero_layer_grads(desc, &grads[l], s))) return st;
+    return HSTU_OK;
+  }
+  if (!seq_offsets) return fail(HSTU_INVALID_ARGUMENT, "device seq_offsets is NULL");
+  if (!x || !d_y) return fail(HSTU_INVALID_ARGUMENT, "x and d_y are required");
+  if (!aligned16(x) || !aligned16(d_y) || (d_x && !aligned16(d_x)))
+    return fail(HSTU_INVALID_ARGUMENT, "x, d_y and d_x must be 16-byte aligned");
+  if ((st = check_ws(workspace, workspace_bytes, p.ws, "workspace"))) return st;
+  Carver c{(char*)workspace};
+  LayerBwdBufs b;
+  carve_layer_bwd(c, desc, p, &b);
+  const hstu_attn_desc& a = desc->attn;
+  const size_t xbytes = (size_t)p.j.total * desc->d_model * elt_size(a.dtype);
+  // forward: inputs of layers 1..L-1
+  LayerBufs lb{b.items, b.kr, b.uvqk, b.o, b.g, nullptr};
+  if ((st = plan_causal(a, seq_offsets, timestamps, p.j, lb, s))) return st;
+  for (int l = 0; l + 1 < L; ++l) {
+    const void* in = l == 0 ? x : (const void*)(b.xs + (l - 1) * xbytes);
+    if ((st = layer_once(desc, seq_offsets, timestamps, p.j, in, weights[l], b.xs + l * xbytes, lb, s,
+                         false)))
+      return st;
+  }
+  // backward, last layer first; dL/dX of layer l is dL/dY of layer l - 1
+  const void* dY = d_y;
+  for (int l = L - 1; l >= 0; --l) {
+    const void* xl = l == 0 ? x : (const void*)(b.xs + (l - 1) * xbytes);
+    void* dX = l == 0 ? d_x : b.dyb[l & 1];
+    if ((st = layer_bwd_once(desc, p, seq_offsets, timestamps, xl, weights[l],
+                             grads ? &grads[l] : nullptr, dY, dX, b, s)))
+      return st;
+    dY = dX;
   }
   return HSTU_OK;
 }

@@ -65,7 +65,8 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const bf16* __restric
                                                          const bf16* __restrict__ R, int64_t ldr,
                                                          OutT* __restrict__ C, int64_t ldc, int64_t M,
                                                          int N, int K, int silu, int tiles_n,
-                                                         int tiles_total) {
+                                                         int tiles_total, int64_t ksplit,
+                                                         int64_t c_split) {
   using G = GemmShape<BM, BN>;
   constexpr int FM = G::FM, FN = G::FN, PERW = G::PERW, STAGE = G::STAGE;
   constexpr int GLD = G::GLD, GSPR = G::GSPR, CPR = G::CPR;
@@ -87,6 +88,13 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const bf16* __restric
   }
   const int64_t m0 = (int64_t)(tile / tiles_n) * BM;
   const int n0 = (tile % tiles_n) * BN;
+  {  // split-K: blockIdx.y takes K range [y * ksplit, (y + 1) * ksplit) into its own C slice
+    const int64_t kofs = (int64_t)blockIdx.y * ksplit;
+    A += kofs;
+    W += kofs;
+    C += (int64_t)blockIdx.y * c_split;
+    K = (int)(K - kofs < ksplit ? K - kofs : ksplit);
+  }
 
   // per-lane DMA sources of this wavefront's PERW instructions (byte offsets from the
   // row-block base of A or W; rows past M or N repeat the last row; pad slots fetch chunk 0)
@@ -228,10 +236,15 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const bf16* __restric
 #pragma unroll
       for (int q = 0; q < 8; ++q) y[q] += (float)rv[q];
     }
-    bf16x8 o;
+    if constexpr (std::is_same<OutT, float>::value) {
+      *reinterpret_cast<f32x4*>(&C[m * ldc + n]) = f32x4{y[0], y[1], y[2], y[3]};
+      *reinterpret_cast<f32x4*>(&C[m * ldc + n + 4]) = f32x4{y[4], y[5], y[6], y[7]};
+    } else {
+      bf16x8 o;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) o[q] = (bf16)y[q];
-    *reinterpret_cast<bf16x8*>(&C[m * ldc + n]) = o;
+      for (int q = 0; q < 8; ++q) o[q] = (bf16)y[q];
+      *reinterpret_cast<bf16x8*>(&C[m * ldc + n]) = o;
+    }
   }
 }
 
@@ -284,35 +297,55 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
   }
 }
 
-hipError_t launch_gemm(const void* A, int64_t lda, const void* W, int64_t ldw, const float* bias,
-                       const void* R, int64_t ldr, void* C, int64_t ldc, int64_t M, int N, int K,
-                       int silu, int bf16flag, hipStream_t s) {
+hipError_t launch_gemm_ex(const void* A, int64_t lda, const void* W, int64_t ldw, const float* bias,
+                          const void* R, int64_t ldr, void* C, int64_t ldc, int64_t M, int N, int K,
+                          int silu, int bf16flag, int out_f32, int splits, int64_t ksplit,
+                          int64_t c_split, hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
   if (bf16flag) {
     // the DMA and the epilogue move 16-byte rows segments
     if (N % 8 != 0 || K % 8 != 0 || lda % 8 != 0 || ldw % 8 != 0 || ldc % 8 != 0 ||
         (R && ldr % 8 != 0))
       return hipErrorInvalidValue;
+    if (splits < 1) splits = 1;
+    if (splits == 1) ksplit = K;
+    // split K ranges are whole pipeline stages; a split tail carries no bias or residual
+    if (splits > 1 && (ksplit % GBK != 0 || (int64_t)(splits - 1) * ksplit >= K || bias || R || silu))
+      return hipErrorInvalidValue;
     // 128x128 tiles when they give at least ~one workgroup per compute unit, else 64x64
-    const int64_t big = ((N + 127) / 128) * ((M + 127) / 128);
+    const int64_t big = ((N + 127) / 128) * ((M + 127) / 128) * splits;
+    auto go = [&](auto bm, auto outc) {
+      constexpr int T = decltype(bm)::value;
+      using O = typename decltype(outc)::type;
+      const int tn = (N + T - 1) / T, tm = (int)((M + T - 1) / T);
+      hipLaunchKernelGGL((gemm_bf16_kernel<T, T, O>), dim3(tn * tm, splits), dim3(256), 0, s,
+                         (const bf16*)A, lda, (const bf16*)W, ldw, bias, (const bf16*)R, ldr, (O*)C,
+                         ldc, M, N, K, silu, tn, tn * tm, ksplit, c_split);
+    };
+    using I128 = std::integral_constant<int, 128>;
+    using I64 = std::integral_constant<int, 64>;
+    struct F { using type = float; };
+    struct H { using type = bf16; };
     if (big >= 256) {
-      const int tn = (N + 127) / 128, tm = (int)((M + 127) / 128);
-      hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, bf16>), dim3(tn * tm), dim3(256), 0, s,
-                         (const bf16*)A, lda, (const bf16*)W, ldw, bias, (const bf16*)R, ldr,
-                         (bf16*)C, ldc, M, N, K, silu, tn, tn * tm);
+      if (out_f32) go(I128{}, F{}); else go(I128{}, H{});
     } else {
-      const int tn = (N + 63) / 64, tm = (int)((M + 63) / 64);
-      hipLaunchKernelGGL((gemm_bf16_kernel<64, 64, bf16>), dim3(tn * tm), dim3(256), 0, s,
-                         (const bf16*)A, lda, (const bf16*)W, ldw, bias, (const bf16*)R, ldr,
-                         (bf16*)C, ldc, M, N, K, silu, tn, tn * tm);
+      if (out_f32) go(I64{}, F{}); else go(I64{}, H{});
     }
   } else {
+    if (splits > 1) return hipErrorInvalidValue;
     const dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 63) / 64));
     hipLaunchKernelGGL(gemm_f32_kernel, grid, dim3(256), 0, s, (const float*)A, lda,
                        (const float*)W, ldw, bias, (const float*)R, ldr, (float*)C, ldc, M, N, K,
                        silu);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_gemm(const void* A, int64_t lda, const void* W, int64_t ldw, const float* bias,
+                       const void* R, int64_t ldr, void* C, int64_t ldc, int64_t M, int N, int K,
+                       int silu, int bf16flag, hipStream_t s) {
+  return launch_gemm_ex(A, lda, W, ldw, bias, R, ldr, C, ldc, M, N, K, silu, bf16flag, 0, 1, K, 0,
+                        s);
 }
 
 }  // namespace hstu

@@ -118,6 +118,15 @@ hipError_t launch_gemm(const void* A, int64_t lda, const void* W, int64_t ldw,
                        const float* bias, const void* R, int64_t ldr, void* C, int64_t ldc,
                        int64_t M, int N, int K, int silu, int use_bf16, hipStream_t s);
 
+// launch_gemm with an fp32 output (bf16 inputs; fp32 inputs always write fp32) and
+// split-K: grid dimension y = splits, split y covers K range [y*ksplit, (y+1)*ksplit)
+// (ksplit a multiple of 32) and writes C + y*c_split; splits > 1 takes no bias,
+// residual or SiLU.
+hipError_t launch_gemm_ex(const void* A, int64_t lda, const void* W, int64_t ldw, const float* bias,
+                          const void* R, int64_t ldr, void* C, int64_t ldc, int64_t M, int N, int K,
+                          int silu, int use_bf16, int out_f32, int splits, int64_t ksplit,
+                          int64_t c_split, hipStream_t s);
+
 // logit[r] = sum_c y[r, c] * w[c] (fp32 accumulate).
 hipError_t launch_rowdot(const void* y, int64_t ld_y, const float* w, float* logit, int64_t rows,
                          int d, int use_bf16, hipStream_t s);
@@ -129,6 +138,32 @@ hipError_t launch_sl_select(const int64_t* off, const int64_t* new_off, int B,
                             const uint32_t* keys, int64_t* src, hipStream_t s);
 hipError_t launch_sl_gather(const int64_t* src, int64_t rows, const void* x, int64_t row_bytes,
                             const int64_t* ts, void* out_x, int64_t* out_ts, hipStream_t s);
+
+// Layer backward helpers (layer_bwd.hip).
+// out[c][r] = in[r][c] (r < R), 0 for R <= r < Rpad; rows of `in` stride ld_in.
+hipError_t launch_transpose(const void* in, int64_t ld_in, void* out, int64_t ld_out, int64_t R,
+                            int64_t Rpad, int C, int use_bf16, hipStream_t s);
+// out[c] = sum over rows of x[r][c], fixed order; partial holds colsum_chunks(R) * C floats.
+int colsum_chunks(int64_t R);
+hipError_t launch_colsum(const void* x, int64_t ld, int64_t R, int C, int use_bf16, float* partial,
+                         float* out, hipStream_t s);
+// out[c] = sum_{k < n} partial[k * stride + c] in order of k (zeros when n == 0).
+hipError_t launch_sum_rows(const float* partial, int64_t stride, int n, int64_t C, float* out,
+                           hipStream_t s);
+// act = SiLU(z) in the activation type, rounded as the f1 GEMM epilogue rounds.
+hipError_t launch_silu_act(const float* z, int64_t ld_z, void* act, int64_t ld_a, int64_t R, int C,
+                           int use_bf16, hipStream_t s);
+// d *= SiLU'(z), in place.
+hipError_t launch_silu_grad(const float* z, int64_t ld_z, void* d, int64_t ld_d, int64_t R, int C,
+                            int use_bf16, hipStream_t s);
+// Backward of out = (LN(o) gamma + beta) (.) u for width w <= 1024: writes d_o and du, and
+// ln_gate_bwd_blocks(rows) partial rows of dgamma and dbeta.
+int ln_gate_bwd_blocks(int64_t rows);
+hipError_t launch_ln_gate_bwd(const float* o, int64_t ld_o, const void* u, int64_t ld_u,
+                              const float* gamma, const float* beta, float eps, const void* g,
+                              int64_t ld_g, void* d_o, int64_t ld_do, void* du, int64_t ld_du,
+                              float* part_gamma, float* part_beta, int64_t rows, int w,
+                              int use_bf16, hipStream_t s);
 
 hipError_t launch_debug_buckets(const int64_t* offsets, const int64_t* ts, int seq, int n, int P,
                                 int T, int32_t* pos_bucket, int32_t* time_bucket, hipStream_t s);

@@ -51,6 +51,12 @@ class mfalcon_desc(ctypes.Structure):
     _fields_ = [("layer", hstu_layer_desc), ("microbatch", ctypes.c_int32)]
 
 
+class hstu_layer_grads(ctypes.Structure):
+    _fields_ = [("dw1", ctypes.c_void_p), ("db1", ctypes.c_void_p), ("d_rab_pos", ctypes.c_void_p),
+                ("d_rab_time", ctypes.c_void_p), ("d_ln_gamma", ctypes.c_void_p),
+                ("d_ln_beta", ctypes.c_void_p), ("dw2", ctypes.c_void_p), ("db2", ctypes.c_void_p)]
+
+
 class hstu_sl_desc(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("max_seq_len", ctypes.c_int32),
                 ("alpha", ctypes.c_float)]
@@ -87,6 +93,10 @@ _sig = {
     "hstu_attn_bwd_workspace_size": ([ctypes.POINTER(hstu_attn_desc), _I64P, _SZP], ctypes.c_int),
     "hstu_attn_bwd": ([ctypes.POINTER(hstu_attn_desc), _I64P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                        _P, _P, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "hstu_layer_bwd_workspace_size": ([ctypes.POINTER(hstu_layer_desc), _I64P, _SZP], ctypes.c_int),
+    "hstu_layer_bwd": ([ctypes.POINTER(hstu_layer_desc), _I64P, _P, _P, _P,
+                        ctypes.POINTER(hstu_layer_weights), _P, _P, ctypes.POINTER(hstu_layer_grads),
+                        _P, ctypes.c_size_t, _P], ctypes.c_int),
     "hstu_sl_lengths": ([ctypes.POINTER(hstu_sl_desc), _I64P, ctypes.POINTER(ctypes.c_float), _I64P,
                          _I64P], ctypes.c_int),
     "hstu_sl_sample": ([ctypes.c_int32, _I64P, _I64P, _P, _P, _P, _P, _P, ctypes.c_int64, _P, _P,
@@ -373,6 +383,40 @@ def hstu_attn_bwd(seq_offsets, timestamps, q, k, v, d_out, rab_pos=None, rab_tim
                              _ptr(d_out), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(drp), _ptr(drt),
                              _ptr(ws), nbytes, _stream(stream)))
     return dq, dk, dv, drp, drt
+
+
+_GRAD_FIELDS = ("dw1", "db1", "d_rab_pos", "d_rab_time", "d_ln_gamma", "d_ln_beta", "dw2", "db2")
+
+
+def hstu_layer_bwd(seq_offsets, timestamps, x, layers: Sequence[LayerWeights], d_y, *, num_heads,
+                   d_qk, d_v, max_seq_len, ln_eps=1e-5, residual=0, want_dx=True, workspace=None,
+                   seq_offsets_host=None, stream=None):
+    """Gradients of hstu_layer_fwd over the stack `layers`. Returns (d_x or None, grads) where
+    grads[l] is a dict of fp32 tensors named like the C struct hstu_layer_grads."""
+    host = _host_offsets(seq_offsets, seq_offsets_host)
+    desc = layer_desc(layers, len(host) - 1, num_heads, d_qk, d_v, x.shape[1], max_seq_len,
+                      _dtype_code(x), ln_eps, residual)
+    dev_ = x.device
+    f1 = 2 * num_heads * (d_v + d_qk)
+    hv = num_heads * d_v
+    a = desc.attn
+    shapes = {"dw1": (f1, x.shape[1]), "db1": (f1,), "d_rab_pos": (num_heads, a.num_pos_buckets),
+              "d_rab_time": (num_heads, a.num_time_buckets), "d_ln_gamma": (hv,),
+              "d_ln_beta": (hv,), "dw2": (x.shape[1], hv), "db2": (x.shape[1],)}
+    grads = [{k: torch.empty(shapes[k], dtype=torch.float32, device=dev_) for k in _GRAD_FIELDS}
+             for _ in layers]
+    garr = (hstu_layer_grads * len(layers))()
+    for i, gd in enumerate(grads):
+        garr[i] = hstu_layer_grads(*[_ptr(gd[k]) for k in _GRAD_FIELDS])
+    dx = torch.empty_like(x) if want_dx else None
+    n = ctypes.c_size_t(0)
+    _check(lib.hstu_layer_bwd_workspace_size(ctypes.byref(desc), _i64p(host), ctypes.byref(n)))
+    ws, nbytes = _workspace(n.value, dev_, workspace)
+    arr = _weights_array(layers)
+    _check(lib.hstu_layer_bwd(ctypes.byref(desc), _i64p(host), _ptr(seq_offsets), _ptr(timestamps),
+                              _ptr(x), arr, _ptr(d_y), _ptr(dx), garr, _ptr(ws), nbytes,
+                              _stream(stream)))
+    return dx, grads
 
 
 def hstu_sl_lengths(offsets_host, max_seq_len: int, alpha: float, u_keep_host):

@@ -258,6 +258,47 @@ hstu_status hstu_attn_bwd(const hstu_attn_desc* desc, const int64_t* seq_offsets
                           size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * hstu_layer_bwd: gradients of hstu_layer_fwd (a stack of num_layers layers,
+ * eqs. 1-3) for training. Given d_y = dL/dY of the stack's output, it writes
+ * d_x = dL/dX (activation dtype; NULL to skip) and, for each layer l,
+ * grads[l] (host array of num_layers structs; NULL, or any NULL pointer in
+ * it, skips that gradient). Every gradient is overwritten, not accumulated.
+ * Parameter gradients are fp32 and laid out like the parameters. The bias
+ * tables of a layer get the sums of dL/dz over their buckets, as in
+ * hstu_attn_bwd.
+ * The forward pass is recomputed inside the call from x and the weights (the
+ * inputs of layers 1..L-1 are kept in the workspace), so the caller stores no
+ * activations. With g = dL/dY of a layer, z1 = X w1^T + b1 and
+ * G = (LN(O) gamma + beta) (.) U:
+ *   dW2 = g^T G, db2 = column sums of g, dG = g W2,
+ *   (dO, dU, dgamma, dbeta) from the LayerNorm-gate backward,
+ *   (dQ, dK, dV, table gradients) from the attention backward,
+ *   dz1 = d[U|V|Q|K] (.) SiLU'(z1), dW1 = dz1^T X, db1 = column sums of dz1,
+ *   dX = dz1 W1 (+ g when residual).
+ * Sums over tokens run in a fixed order, so the results repeat bit for bit,
+ * except the bias-table gradients (see hstu_attn_bwd).
+ * Support: H*d_v <= 1024. `workspace` is hstu_layer_bwd_workspace_size bytes.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  float* dw1;               /* [2H(d_v+d_qk), d_model] */
+  float* db1;               /* [2H(d_v+d_qk)] */
+  float* d_rab_pos;         /* [H][P] */
+  float* d_rab_time;        /* [H][T] */
+  float* d_ln_gamma;        /* [H*d_v] */
+  float* d_ln_beta;         /* [H*d_v] */
+  float* dw2;               /* [d_model, H*d_v] */
+  float* db2;               /* [d_model] */
+} hstu_layer_grads;
+
+hstu_status hstu_layer_bwd_workspace_size(const hstu_layer_desc* desc,
+                                          const int64_t* seq_offsets_host, size_t* bytes);
+hstu_status hstu_layer_bwd(const hstu_layer_desc* desc, const int64_t* seq_offsets_host,
+                           const int64_t* seq_offsets, const int64_t* timestamps, const void* x,
+                           const hstu_layer_weights* weights, const void* d_y, void* d_x,
+                           const hstu_layer_grads* grads, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Stochastic Length (HSTU chapter, "Three more scaling components",
  * Stochastic Length): training keeps the full history of short users and of a
  * few long ones, and cuts the rest to a random subsequence of the target

@@ -47,7 +47,7 @@ import numpy as np
 from . import hstu_oracle as F
 
 __all__ = ["silu_grad", "attention_backward", "attention_backward_rows", "gate_backward",
-           "layer_backward", "LayerGrads"]
+           "layer_backward", "layer_stack_backward", "LayerGrads"]
 
 
 def _f64(a):
@@ -192,17 +192,23 @@ class LayerGrads:
     dbeta: np.ndarray
 
 
-def layer_backward(offsets, ts, x, w, H, d_qk, d_v, N, d_y, eps=1e-5, residual=0):
+def layer_backward(offsets, ts, x, w, H, d_qk, d_v, N, d_y, eps=1e-5, residual=0, storage=None):
     """Gradients of one HSTU layer (eqs. 1-3) in fp64, given dL/dY.
 
     w has the fields of the forward oracle's layer weights (w1, b1, rab_pos, rab_time,
-    gamma, beta, w2, b2)."""
+    gamma, beta, w2, b2). storage=None keeps fp64 throughout. storage="bf16" rounds
+    the tensors that a bf16 implementation stores between its steps, the same reading
+    as the forward oracle's storage variant (the HSTU chapter sizes a layer's
+    activation state in bfloat16, "Gating instead of a separate FFN"):
+    [U|V|Q|K], G, dG, dO, dU, dQ, dK, dV, dz1 and dX. It measures how much storage
+    rounding alone moves each gradient row."""
+    r = lambda a: F.round_storage(a, storage)
     x, gy = _f64(x), _f64(d_y)
     R = x.shape[0]
     z1 = x @ _f64(w.w1).T
     if w.b1 is not None:
         z1 = z1 + _f64(w.b1)[None, :]
-    act = F.silu(z1)
+    act = r(F.silu(z1))
     cu, cq = H * d_v, H * d_qk
     U = act[:, 0:cu]
     V = act[:, cu:2 * cu].reshape(R, H, d_v)
@@ -210,21 +216,43 @@ def layer_backward(offsets, ts, x, w, H, d_qk, d_v, N, d_y, eps=1e-5, residual=0
     K = act[:, 2 * cu + cq:2 * cu + 2 * cq].reshape(R, H, d_qk)
     o = F.hstu_attention(offsets, ts, Q, K, V, w.rab_pos, w.rab_time, N).reshape(R, cu)
     y = F.layer_norm_rows(o, w.gamma, w.beta, eps)
-    G = y * U
+    G = r(y * U)
     # f2
-    dG = gy @ _f64(w.w2)
+    dG = r(gy @ _f64(w.w2))
     dw2 = gy.T @ G
     db2 = gy.sum(axis=0)
     # gate and norm
     do, dU, dgamma, dbeta = gate_backward(o, U, w.gamma, w.beta, eps, dG)
+    do, dU = r(do), r(dU)
     # attention
     dQ, dK, dV, drp, drt = attention_backward(offsets, ts, Q, K, V, w.rab_pos, w.rab_time, N,
                                               do.reshape(R, H, d_v))
-    dact = np.concatenate([dU, dV.reshape(R, cu), dQ.reshape(R, cq), dK.reshape(R, cq)], axis=1)
-    dz1 = dact * silu_grad(z1)
+    dact = np.concatenate([dU, r(dV).reshape(R, cu), r(dQ).reshape(R, cq), r(dK).reshape(R, cq)],
+                          axis=1)
+    dz1 = r(dact * silu_grad(z1))
     dw1 = dz1.T @ x
     db1 = dz1.sum(axis=0)
     dx = dz1 @ _f64(w.w1)
     if residual:
         dx = dx + gy
+    dx = r(dx)
     return LayerGrads(dx, dw1, db1, dw2, db2, drp, drt, dgamma, dbeta)
+
+
+def layer_stack_backward(offsets, ts, x, layers, H, d_qk, d_v, N, d_y, eps=1e-5, residual=0,
+                         storage=None):
+    """Gradients of a stack of layers (X_{l+1} = layer_l(X_l)) given dL/dY of the last one.
+    The inputs of each layer come from the forward oracle, then layer_backward runs from
+    the last layer to the first, each layer's dX being the previous layer's dY.
+    storage as in layer_backward (and the forward oracle, for the layer inputs).
+    Returns (dL/dX of the stack input, [LayerGrads per layer])."""
+    xs = [_f64(x)]
+    for w in layers[:-1]:
+        xs.append(F.hstu_layer(offsets, ts, xs[-1], w, H, d_qk, d_v, N, eps, residual, storage))
+    grads = [None] * len(layers)
+    g = _f64(d_y)
+    for l in range(len(layers) - 1, -1, -1):
+        grads[l] = layer_backward(offsets, ts, xs[l], layers[l], H, d_qk, d_v, N, g, eps, residual,
+                                  storage)
+        g = grads[l].dx
+    return g, grads

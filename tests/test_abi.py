@@ -217,3 +217,23 @@ def test_status_strings(ops):
     for s, name in enumerate(["HSTU_OK", "HSTU_INVALID_ARGUMENT", "HSTU_UNSUPPORTED",
                               "HSTU_WORKSPACE_TOO_SMALL", "HSTU_DEVICE_ERROR"]):
         assert ops.lib.hstu_status_string(s).decode() == name
+
+
+def test_layer_bwd_rejections(ops):
+    w = ops.hstu_layer_weights(FAKE, None, None, None, None, None, FAKE, None)
+    off = np.array([0, 5, 12], np.int64)
+
+    def call(desc, x=FAKE, dy=FAKE, ws=ctypes.c_void_p(0x100000), wsb=1 << 40):
+        return ops.lib.hstu_layer_bwd(ctypes.byref(desc), off.ctypes.data_as(ops._I64P), FAKE, None,
+                                      x, ctypes.byref(w), dy, None, None, ws, wsb, None)
+
+    good = ops.hstu_layer_desc(_desc(ops), 64, 0, 1)
+    wide = ops.hstu_layer_desc(_desc(ops, num_heads=16, d_v=128, d_qk=128), 64, 0, 1)
+    assert call(wide) == ops.HSTU_UNSUPPORTED                 # H*d_v > 1024
+    assert call(good, x=None) == ops.HSTU_INVALID_ARGUMENT    # x required
+    assert call(good, dy=None) == ops.HSTU_INVALID_ARGUMENT   # d_y required
+    assert call(good, wsb=16) == ops.HSTU_WORKSPACE_TOO_SMALL
+    assert call(ops.hstu_layer_desc(_desc(ops), 60, 0, 1)) == ops.HSTU_UNSUPPORTED  # d_model % 8
+    n = ctypes.c_size_t(0)
+    assert ops.lib.hstu_layer_bwd_workspace_size(ctypes.byref(good), off.ctypes.data_as(ops._I64P),
+                                                 ctypes.byref(n)) == ops.HSTU_OK and n.value > 0

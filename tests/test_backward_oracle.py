@@ -162,3 +162,43 @@ def test_absent_tables_count_as_zeros():
     got = BW.attention_backward(off, ts, q, k, v, None, None, N, g, P=rp.shape[1], T=rt.shape[1])
     for a, b in zip(want, got):
         assert np.array_equal(a, b)
+
+
+def test_stack_gradients_by_finite_differences():
+    x = synth.make_layer(9, lambda r: np.array([5, 7]), 2, 4, 3, 8, 4, 3, "f32", num_layers=2,
+                         random_bias=True, with_ln_affine=True, w_std=0.4, residual=1)
+    for w in x.layers:
+        for name in ("w1", "b1", "rab_pos", "rab_time", "gamma", "beta", "w2", "b2"):
+            setattr(w, name, np.asarray(getattr(w, name), np.float64).copy())
+    X = np.asarray(x.x, np.float64).copy()
+    rng = np.random.default_rng(10)
+    gy = rng.standard_normal(X.shape)
+    loss = lambda: float(np.sum(F.hstu_layer_stack(x.offsets, x.ts, X, x.layers, x.num_heads, x.d_qk,
+                                                   x.d_v, x.max_seq_len, 1e-5, 1) * gy))
+    dx, gr = BW.layer_stack_backward(x.offsets, x.ts, X, x.layers, x.num_heads, x.d_qk, x.d_v,
+                                     x.max_seq_len, gy, 1e-5, 1)
+    checks = [("x", X, dx)]
+    for l, w in enumerate(x.layers):
+        checks += [(f"w1[{l}]", w.w1, gr[l].dw1), (f"w2[{l}]", w.w2, gr[l].dw2),
+                   (f"gamma[{l}]", w.gamma, gr[l].dgamma), (f"rab_time[{l}]", w.rab_time, gr[l].d_rab_time)]
+    for name, arr, grad in checks:
+        flat = list(np.ndindex(arr.shape))
+        pick = flat if len(flat) <= 12 else [flat[i] for i in rng.choice(len(flat), 12, False)]
+        for idx in pick:
+            _close(grad[idx], _fd(loss, arr, idx), f"d{name}{idx}")
+
+
+def test_storage_rounding_moves_little_and_only_when_asked():
+    """The bf16-storage variant differs from fp64 by about bf16 rounding, and storage=None
+    is the plain fp64 result."""
+    x = synth.make_layer(12, lambda r: np.array([9, 4]), 2, 4, 4, 8, 4, 3, "bf16", num_layers=2,
+                         random_bias=True, with_ln_affine=True, w_std=0.3, residual=1)
+    gy = synth.normal(np.random.default_rng(13), x.x.shape, 1.0, "bf16")
+    args = (x.offsets, x.ts, x.x, x.layers, x.num_heads, x.d_qk, x.d_v, x.max_seq_len, gy, 1e-5, 1)
+    d0, g0 = BW.layer_stack_backward(*args)
+    d1, g1 = BW.layer_stack_backward(*args, storage=None)
+    assert np.array_equal(d0, d1) and np.array_equal(g0[0].dw1, g1[0].dw1)
+    ds, gs = BW.layer_stack_backward(*args, storage="bf16")
+    rel = np.abs(ds - d0).max() / np.abs(d0).max()
+    assert 0 < rel < 0.05
+    assert np.array_equal(F.round_storage(ds, "bf16"), ds)  # dX is stored in bf16
