@@ -56,7 +56,71 @@ hipError_t launch_transpose(const void* in, int64_t ld_in, void* out, int64_t ld
 }
 
 // ------------------------------------------------------------------ column sums
-// partial[ch][c] = sum of x[r][c] over rows r in chunk ch (rows in order).
+// Sums over rows in a fixed order. A workgroup covers 16 columns; its 16 row groups
+// (one per 16-lane slice) each add every 16th row (or chunk) in order, 8 loads in
+// flight, and the 16 group sums are then added in group order through LDS. The
+// result depends only on the data, never on timing.
+constexpr int kSumGroups = 16;
+
+template <typename T>
+__device__ __forceinline__ float grouped_column_sum(const T* __restrict__ x, int64_t stride,
+                                                    int64_t n, int64_t c, int g) {
+  float s = 0.f;
+  int64_t r = g;
+  for (; r + 7 * kSumGroups < n; r += 8 * kSumGroups) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = to_f32<T>(x[(r + u * kSumGroups) * stride + c]);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += v[u];
+  }
+  for (; r < n; r += kSumGroups) s += to_f32<T>(x[r * stride + c]);
+  return s;
+}
+
+// out[c] = sum over r < n of x[r * stride + c] (zeros when n == 0).
+template <typename T>
+__global__ __launch_bounds__(256) void column_sum_kernel(const T* __restrict__ x, int64_t stride,
+                                                         int64_t n, int64_t C,
+                                                         float* __restrict__ out) {
+  __shared__ float part[kSumGroups][16];
+  const int cl = threadIdx.x & 15, g = threadIdx.x >> 4;
+  const int64_t c = (int64_t)blockIdx.x * 16 + cl;
+  part[g][cl] = c < C ? grouped_column_sum<T>(x, stride, n, c, g) : 0.f;
+  __syncthreads();
+  if (g == 0 && c < C) {
+    float s = 0.f;
+#pragma unroll
+    for (int q = 0; q < kSumGroups; ++q) s += part[q][cl];
+    out[c] = s;
+  }
+}
+
+// out[c] = sum over k < n of partial[k * stride + c] for wide outputs (split-K sums):
+// one thread per column, the few partials in order.
+__global__ __launch_bounds__(256) void sum_rows_wide_kernel(const float* __restrict__ partial,
+                                                            int64_t stride, int n, int64_t C,
+                                                            float* __restrict__ out) {
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= C) return;
+  float s = 0.f;
+  for (int k = 0; k < n; ++k) s += partial[(int64_t)k * stride + c];
+  out[c] = s;
+}
+
+hipError_t launch_sum_rows(const float* partial, int64_t stride, int n, int64_t C, float* out,
+                           hipStream_t s) {
+  if (C <= 0 || !out) return hipSuccess;
+  if (n <= 8 && C >= 4096)
+    hipLaunchKernelGGL(sum_rows_wide_kernel, dim3((unsigned)((C + 255) / 256)), dim3(256), 0, s,
+                       partial, stride, n, C, out);
+  else
+    hipLaunchKernelGGL(column_sum_kernel<float>, dim3((unsigned)((C + 15) / 16)), dim3(256), 0, s,
+                       partial, stride, (int64_t)n, C, out);
+  return hipGetLastError();
+}
+
+// partial[ch][c] = sum of x[r][c] over the rows of chunk ch, in order, 8 loads in flight.
 template <typename T>
 __global__ __launch_bounds__(256) void colsum_partial_kernel(const T* __restrict__ x, int64_t ld,
                                                              int64_t R, int C, int64_t rows_per,
@@ -67,31 +131,20 @@ __global__ __launch_bounds__(256) void colsum_partial_kernel(const T* __restrict
   const int64_t r0 = (int64_t)ch * rows_per;
   const int64_t r1 = r0 + rows_per < R ? r0 + rows_per : R;
   float s = 0.f;
-  for (int64_t r = r0; r < r1; ++r) s += to_f32<T>(x[r * ld + c]);
+  int64_t r = r0;
+  for (; r + 7 < r1; r += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = to_f32<T>(x[(r + u) * ld + c]);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += v[u];
+  }
+  for (; r < r1; ++r) s += to_f32<T>(x[r * ld + c]);
   partial[(int64_t)ch * C + c] = s;
 }
 
-// out[c] = sum over ch of partial[ch * stride + c], in order of ch.
-__global__ __launch_bounds__(256) void sum_rows_kernel(const float* __restrict__ partial,
-                                                       int64_t stride, int n, int64_t C,
-                                                       float* __restrict__ out) {
-  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (c >= C) return;
-  float s = 0.f;
-  for (int ch = 0; ch < n; ++ch) s += partial[(int64_t)ch * stride + c];
-  out[c] = s;
-}
-
-hipError_t launch_sum_rows(const float* partial, int64_t stride, int n, int64_t C, float* out,
-                           hipStream_t s) {
-  if (C <= 0 || !out) return hipSuccess;
-  hipLaunchKernelGGL(sum_rows_kernel, dim3((unsigned)((C + 255) / 256)), dim3(256), 0, s, partial,
-                     stride, n, C, out);
-  return hipGetLastError();
-}
-
 int colsum_chunks(int64_t R) {
-  const int64_t c = (R + 255) / 256;
+  const int64_t c = (R + 63) / 64;
   return (int)(c < 1 ? 1 : (c > 256 ? 256 : c));
 }
 
