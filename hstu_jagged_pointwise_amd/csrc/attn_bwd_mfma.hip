@@ -23,10 +23,12 @@
 // The key-side kernel also sums dz per bias bucket into per-wavefront LDS bins,
 // which are written as one partial row per work item and reduced in a fixed order.
 // Most pairs of a block share a time bucket, so a per-element atomic would make the
-// 64 lanes collide on one address: time buckets are summed by wavefront
-// reductions, one per bucket in the block's range, and the clamped position bucket
-// in a register. Only position buckets below the clamp, which differ across the
-// lanes of an instruction, use LDS atomics.
+// 64 lanes collide on one address. Blocks with one or two time buckets add their
+// sums to per-lane running sums of the current bucket and the next, reduced across
+// the wavefront only when the bucket moves on; other blocks reduce once per bucket
+// of their range. The clamped position bucket is summed in a register. Only
+// position buckets below the clamp, which differ across the lanes of an
+// instruction, use LDS atomics.
 //
 // Bias per 32x32 block (wavefront-uniform): the position bucket min(i-j, P-1) is
 // the constant P-1 when every i - j >= P - 1. The time bucket is monotone in the
@@ -135,6 +137,14 @@ __device__ __forceinline__ KeyRange block_range(const AttnBwdArgs& a, const WTil
   return r;
 }
 
+// Timestamps of the streamed side's 64 rows and the ranges of its two 32-row blocks,
+// fetched into registers together with the next tile's data and stored to LDS after
+// the current tile's compute, so that their load latency is hidden by that compute.
+struct SideTs {
+  int64_t tv;
+  KeyRange r;
+};
+
 // Register-staged copy of 64 rows x D of two row-major tensors into LDS tiles
 // (rows past `rows` become zeros).
 template <int D>
@@ -169,12 +179,13 @@ bool attn_bwd_mfma_supported(int dtype_bf16, int d_qk, int d_v, int P) {
 
 // ------------------------------------------------------------------ query side
 template <int D>
-__global__ __launch_bounds__(256, 1) void attn_bwd_q_mfma(AttnBwdArgs a) {
+__global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void attn_bwd_q_mfma(AttnBwdArgs a) {
   constexpr int NKK = D / 16, NC = D / 32;
   __shared__ __attribute__((aligned(16))) bf16 Ks[2][TR * (D + 8)];
   __shared__ __attribute__((aligned(16))) bf16 Vs[2][TR * (D + 8)];
   __shared__ int64_t tks[2][TR];
   __shared__ uint32_t tks32[2][TR];  // low words, for the two-bucket test
+  __shared__ KeyRange krs[2][2];     // timestamp ranges of the tile's two key blocks
   __shared__ float rps[kMaxPosB];
   __shared__ float rts[kTimeB];
 
@@ -220,23 +231,34 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_q_mfma(AttnBwdArgs a) {
     st.load(k, a.ld_k, v, a.ld_v, t.base + k0, rows, h * D);
     return rows;
   };
-  auto load_ts = [&](int kt, int buf) {
+  auto fetch_ts = [&](int kt) {
     const int64_t k0 = (int64_t)kt * TR;
+    SideTs f{0, {0, 0}};
+    if (has_ts && tid < TR && k0 + tid < kend) f.tv = a.ts[t.base + k0 + tid];
+    if (has_ts && tid < 2 && k0 + 32 * tid < kend)
+      f.r = a.key_ranges[key_range_slot(t.base, t.seq) + k0 / 32 + tid];
+    return f;
+  };
+  auto store_ts = [&](const SideTs& f, int buf) {
     if (tid < TR) {
-      const int64_t tv = (has_ts && k0 + tid < kend) ? a.ts[t.base + k0 + tid] : 0;
-      tks[buf][tid] = tv;
-      tks32[buf][tid] = (uint32_t)tv;
+      tks[buf][tid] = f.tv;
+      tks32[buf][tid] = (uint32_t)f.tv;
     }
+    if (tid < 2) krs[buf][tid] = f.r;
   };
   load_tile(0);
   st.store(Ks[0], Vs[0]);
-  load_ts(0, 0);
+  store_ts(fetch_ts(0), 0);
   __syncthreads();
 
   for (int kt = 0; kt < nkt; ++kt) {
     const int buf = kt & 1;
     const bool more = kt + 1 < nkt;
-    if (more) load_tile(kt + 1);
+    SideTs nf{0, {0, 0}};
+    if (more) {
+      load_tile(kt + 1);
+      nf = fetch_ts(kt + 1);
+    }
     const bf16* Kt = Ks[buf];
     const bf16* Vt = Vs[buf];
 #pragma unroll
@@ -255,7 +277,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_q_mfma(AttnBwdArgs a) {
       int blo = 0, bhi = 0;
       bool fits32 = true;
       if (has_ts) {
-        const KeyRange kr = block_range(a, t, k0b);
+        const KeyRange kr = krs[buf][kb];
         blo = tbucket(qr.lo - kr.hi, a.T);
         bhi = tbucket(qr.hi - kr.lo, a.T);
         fits32 = time_fast_ok(qr.lo, qr.hi, kr.lo, kr.hi);
@@ -303,7 +325,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_q_mfma(AttnBwdArgs a) {
     }
     if (more) {
       st.store(Ks[buf ^ 1], Vs[buf ^ 1]);
-      load_ts(kt + 1, buf ^ 1);
+      store_ts(nf, buf ^ 1);
     }
     __syncthreads();
   }
@@ -326,6 +348,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kv_mfma(AttnBwdArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 Gs[2][TR * (D + 8)];
   __shared__ int64_t tqs[2][TR];
   __shared__ uint32_t tqs32[2][TR];  // low words, for the two-bucket test
+  __shared__ KeyRange qrs[2][2];     // timestamp ranges of the tile's two query blocks
   __shared__ float rps[kMaxPosB];
   __shared__ float rts[kTimeB];
   extern __shared__ float bins[];  // [4][P + TT] when bias_partial is set
@@ -367,6 +390,40 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kv_mfma(AttnBwdArgs a) {
 #pragma unroll
     for (int c = 0; c < NC; ++c) dk[c] = dv[c] = f32x16{};
     float bin_clamp = 0.f;  // this lane's share of dz in position bucket P-1 over constant blocks
+    // Time-bucket sums of constant and two-bucket blocks: this lane's running sums for
+    // buckets cur_b and cur_b + 1 (cur_b wavefront-uniform). Queries arrive in time
+    // order for typical data, so a wavefront reduction is needed only when the bucket
+    // moves on, not per block.
+    int cur_b = -1;
+    float acc0 = 0.f, acc1 = 0.f;
+    auto flush_bin = [&](int b, float v) {
+      const float tot = wave_sum64(v);
+      if (lane == 0) my_bins[a.P + b] += tot;  // lane 0 alone writes its wavefront's bins here
+    };
+    auto flush_all = [&]() {
+      if (cur_b >= 0) {
+        flush_bin(cur_b, acc0);
+        if (cur_b + 1 < TT) flush_bin(cur_b + 1, acc1);  // acc1 is 0 when cur_b is the top bucket
+      }
+      acc0 = acc1 = 0.f;
+    };
+    // add this lane's dz sums of a block in buckets b (zl) and b + 1 (zh)
+    auto add_bins = [&](int b, float zl, float zh) {
+      if (b == cur_b) {
+        acc0 += zl;
+        acc1 += zh;
+      } else if (b == cur_b + 1) {
+        flush_bin(cur_b, acc0);
+        acc0 = acc1 + zl;
+        acc1 = zh;
+        cur_b = b;
+      } else {
+        flush_all();
+        acc0 = zl;
+        acc1 = zh;
+        cur_b = b;
+      }
+    };
 
     const int64_t qbeg = t.r0;  // the first query that sees any key of the tile
     const int nqt = (int)((t.n - qbeg + TR - 1) / TR);
@@ -376,23 +433,34 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kv_mfma(AttnBwdArgs a) {
       const int rows = (int)(t.n - q0 < TR ? t.n - q0 : TR);
       st.load(q, a.ld_q, g, a.ld_do, t.base + q0, rows, h * D);
     };
-    auto load_ts = [&](int qt, int buf) {
+    auto fetch_ts = [&](int qt) {
       const int64_t q0 = qbeg + (int64_t)qt * TR;
+      SideTs f{0, {0, 0}};
+      if (has_ts && tid < TR && q0 + tid < t.n) f.tv = a.ts[t.base + q0 + tid];
+      if (has_ts && tid < 2 && q0 + 32 * tid < t.n)
+        f.r = a.key_ranges[key_range_slot(t.base, t.seq) + q0 / 32 + tid];
+      return f;
+    };
+    auto store_ts = [&](const SideTs& f, int buf) {
       if (tid < TR) {
-        const int64_t tv = (has_ts && q0 + tid < t.n) ? a.ts[t.base + q0 + tid] : 0;
-        tqs[buf][tid] = tv;
-        tqs32[buf][tid] = (uint32_t)tv;
+        tqs[buf][tid] = f.tv;
+        tqs32[buf][tid] = (uint32_t)f.tv;
       }
+      if (tid < 2) qrs[buf][tid] = f.r;
     };
     load_tile(0);
     st.store(Qs[0], Gs[0]);
-    load_ts(0, 0);
+    store_ts(fetch_ts(0), 0);
     __syncthreads();
 
     for (int qt = 0; qt < nqt; ++qt) {
       const int buf = qt & 1;
       const bool more = qt + 1 < nqt;
-      if (more) load_tile(qt + 1);
+      SideTs nf{0, {0, 0}};
+      if (more) {
+        load_tile(qt + 1);
+        nf = fetch_ts(qt + 1);
+      }
       const bf16* Qt = Qs[buf];
       const bf16* Gt = Gs[buf];
 #pragma unroll
@@ -410,7 +478,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kv_mfma(AttnBwdArgs a) {
         int blo = 0, bhi = 0;
         bool fits32 = true;
         if (has_ts) {
-          const KeyRange qr = block_range(a, t, q0b);
+          const KeyRange qr = qrs[buf][qb];
           blo = tbucket(qr.lo - kr.hi, a.T);
           bhi = tbucket(qr.hi - kr.lo, a.T);
           fits32 = time_fast_ok(qr.lo, qr.hi, kr.lo, kr.hi);
@@ -430,10 +498,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kv_mfma(AttnBwdArgs a) {
           }
           if (a.bias_partial) {
             bin_clamp += zsum;
-            if (has_ts) {
-              const float tot = wave_sum64(zsum);
-              if (lane == 0) my_bins[a.P + blo] += tot;  // lane 0 alone writes its wave's bins here
-            }
+            if (has_ts) add_bins(blo, zsum, 0.f);
           }
         } else if (full && posc && bhi == blo + 1 && fits32) {
           // two adjacent time buckets (see the query side)
@@ -455,11 +520,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kv_mfma(AttnBwdArgs a) {
           }
           if (a.bias_partial) {
             bin_clamp += zlo + zhi;
-            const float tlo = wave_sum64(zlo), thi = wave_sum64(zhi);
-            if (lane == 0) {
-              my_bins[a.P + blo] += tlo;
-              my_bins[a.P + bhi] += thi;
-            }
+            add_bins(blo, zlo, zhi);
           }
         } else {
           int btv[16];
@@ -512,11 +573,12 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kv_mfma(AttnBwdArgs a) {
       }
       if (more) {
         st.store(Qs[buf ^ 1], Gs[buf ^ 1]);
-        load_ts(qt + 1, buf ^ 1);
+        store_ts(nf, buf ^ 1);
       }
       __syncthreads();
     }
     if (a.bias_partial) {
+      if (has_ts) flush_all();
       const float tot = wave_sum64(bin_clamp);
       if (lane == 0) my_bins[a.P - 1] += tot;
     }
