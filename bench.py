@@ -12,10 +12,16 @@ resident in HBM before the timed region. The same run also times:
     included);
   * the short-history layer (B=256, lengths 20..200, d_model 128) and the
     heavy-tailed 4-layer stack (B=32, power-law lengths 64..4096, d_model 512);
+  * the softmax ablation of the attention on the same length-8192 workload (same
+    scores and bias), and the pointwise kernel's speedup over it;
+  * the backward pass: attention gradients on the length-8192 workload and whole-layer
+    gradients of both layer workloads;
+  * Stochastic Length sampling of the heavy-tailed batch (N = 4096, alpha = 1.6);
   * the fp64 CPU oracle on a bounded sample of the attention workload.
 One JSON line goes to stdout. Progress goes to stderr.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--only attn,mfalcon,layers,copy]
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+                    [--only attn,softmax,mfalcon,layers,backward,sl,cpu | copy]
 """
 from __future__ import annotations
 
@@ -166,6 +172,102 @@ def leg_layers(steps, warmup):
     return res
 
 
+def leg_softmax(steps, warmup):
+    """The softmax ablation on the length-8192 workload, same scores and bias tables."""
+    import torch
+    from hstu_jagged_pointwise_amd import ops, synth
+    from hstu_jagged_pointwise_amd.device import attn_to_device
+    x = synth.workload_long_attention()
+    d = attn_to_device(x)
+    stream = torch.cuda.Stream()
+    desc = ops.attn_desc(len(x.offsets) - 1, x.num_heads, x.d_qk, x.d_v, x.max_seq_len,
+                         x.num_pos_buckets, x.num_time_buckets, ops.HSTU_BF16)
+    import ctypes
+    n = ctypes.c_size_t(0)
+    ops._check(ops.lib.hstu_softmax_attn_workspace_size(ctypes.byref(desc), ops._i64p(x.offsets),
+                                                        ctypes.byref(n)))
+    ws = torch.empty(max(n.value, 1), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(d["v"])
+
+    def call():
+        ops.hstu_softmax_attn_fwd(d["offsets"], d["ts"], d["q"], d["k"], d["v"], d["rab_pos"],
+                                  d["rab_time"], max_seq_len=x.max_seq_len, out=out, workspace=ws,
+                                  seq_offsets_host=x.offsets, stream=stream)
+
+    with torch.cuda.stream(stream):
+        ms, _ = time_calls(call, stream, steps, warmup)
+    pairs = int(np.sum(x.lengths * (x.lengths + 1) // 2))
+    flops = pairs * x.num_heads * 2 * (x.d_qk + x.d_v)
+    mean = float(ms.mean())
+    return dict(ms=round(mean, 4), tflops=round(flops / (mean * 1e-3) / 1e12, 2))
+
+
+def leg_backward(steps, warmup):
+    """Gradients: attention alone on the length-8192 workload, and whole layers."""
+    import torch
+    from hstu_jagged_pointwise_amd import ops, synth
+    from hstu_jagged_pointwise_amd.device import attn_to_device, layer_to_device
+    res = {}
+    x = synth.workload_long_attention()
+    d = attn_to_device(x)
+    g = torch.from_numpy(synth.normal(np.random.default_rng(7), x.v.shape, 1.0, "bf16")).to(
+        torch.bfloat16).cuda()
+    stream = torch.cuda.Stream()
+
+    def call():
+        ops.hstu_attn_bwd(d["offsets"], d["ts"], d["q"], d["k"], d["v"], g, d["rab_pos"],
+                          d["rab_time"], max_seq_len=x.max_seq_len, seq_offsets_host=x.offsets,
+                          stream=stream)
+
+    with torch.cuda.stream(stream):
+        ms, _ = time_calls(call, stream, max(5, steps // 5), max(2, warmup // 5))
+    pairs = int(np.sum(x.lengths * (x.lengths + 1) // 2))
+    # dV = A^T G, dP = G V^T, dQ = dZ K, dK = dZ^T Q: four contractions per pair and head
+    flops = pairs * x.num_heads * 2 * (2 * x.d_v + 2 * x.d_qk)
+    mean = float(ms.mean())
+    res["attention_length_8192"] = dict(ms=round(mean, 4),
+                                        tflops=round(flops / (mean * 1e-3) / 1e12, 2))
+    for name, xl in (("short_history_layer", synth.workload_short_history_layer()),
+                     ("heavy_tail_4_layer_stack", synth.workload_heavy_tail_stack())):
+        dl = layer_to_device(xl)
+        gy = torch.from_numpy(synth.normal(np.random.default_rng(8), xl.x.shape, 1.0, "bf16")).to(
+            torch.bfloat16).cuda()
+
+        def lcall():
+            ops.hstu_layer_bwd(dl["offsets"], dl["ts"], dl["x"], dl["layers"], gy,
+                               num_heads=xl.num_heads, d_qk=xl.d_qk, d_v=xl.d_v,
+                               max_seq_len=xl.max_seq_len, seq_offsets_host=xl.offsets,
+                               stream=stream)
+
+        with torch.cuda.stream(stream):
+            ms, _ = time_calls(lcall, stream, max(5, steps // 5), max(2, warmup // 5))
+        res[name] = dict(ms_per_call=round(float(ms.mean()), 4), layers=len(xl.layers),
+                         note="forward recomputed inside the call")
+    return res
+
+
+def leg_sl(steps, warmup):
+    """Stochastic Length sampling of the heavy-tailed batch (rows, timestamps, indices)."""
+    import torch
+    from hstu_jagged_pointwise_amd import ops, synth
+    x = synth.workload_sl_heavy_tail()
+    new, L = ops.hstu_sl_lengths(x.offsets, x.max_seq_len, x.alpha, x.u_keep)
+    dv = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    off, nd, keys = dv(x.offsets), dv(new), dv(x.keys.view(np.int32))
+    xx = dv(x.x).to(torch.bfloat16)
+    ts = dv(x.ts)
+    stream = torch.cuda.Stream()
+
+    def call():
+        ops.hstu_sl_sample(off, nd, keys, xx, ts, offsets_host=x.offsets, new_offsets_host=new,
+                           stream=stream)
+
+    with torch.cuda.stream(stream):
+        ms, _ = time_calls(call, stream, steps, warmup)
+    return dict(ms=round(float(ms.mean()), 4), rows_in=int(x.offsets[-1]), rows_out=int(new[-1]),
+                target_length=int(L), note="includes host validation and output allocation")
+
+
 def leg_copy():
     """A plain 1 GiB device copy: the calibration for the HBM byte counters."""
     import torch
@@ -223,7 +325,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     # the clocks take a few dozen calls to settle; the timed calls start after them
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--only", default="attn,mfalcon,layers,cpu")
+    ap.add_argument("--only", default="attn,softmax,mfalcon,layers,backward,sl,cpu")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -254,6 +356,18 @@ def main():
     if "layers" in legs:
         log("layer legs")
         result["layers"] = leg_layers(args.steps, args.warmup)
+    if "softmax" in legs:
+        log("softmax-variant leg")
+        result["softmax_variant"] = leg_softmax(args.steps, args.warmup)
+        if attn is not None:
+            result["softmax_variant"]["pointwise_speedup"] = round(
+                result["softmax_variant"]["ms"] / float(attn["ms"].mean()), 3)
+    if "backward" in legs:
+        log("backward legs")
+        result["backward"] = leg_backward(args.steps, args.warmup)
+    if "sl" in legs:
+        log("Stochastic Length leg")
+        result["stochastic_length"] = leg_sl(args.steps, args.warmup)
     if attn is None:
         print(json.dumps(result))
         return

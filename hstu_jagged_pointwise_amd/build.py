@@ -22,7 +22,8 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libhstu.so")
 SOURCES = ["api.cpp", "plan.hip", "attn_simple.hip", "attn_mfma.hip", "lngate.hip", "gemm.hip",
            "misc.hip", "sl.hip",
-           "attn_bwd.hip", "attn_bwd_mfma.hip", "layer_bwd.hip"]
+           "attn_bwd.hip", "attn_bwd_mfma.hip", "layer_bwd.hip",
+           "attn_softmax.hip"]
 ARCH = os.environ.get("HSTU_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -1277,6 +1277,70 @@ hstu_status hstu_attn_bwd(const hstu_attn_desc* desc, const int64_t* seq_offsets
   return HSTU_OK;
 }
 
+hstu_status hstu_softmax_attn_workspace_size(const hstu_attn_desc* desc,
+                                             const int64_t* seq_offsets_host, size_t* bytes) {
+  if (!bytes) return fail(HSTU_INVALID_ARGUMENT, "bytes is NULL");
+  hstu_status st = check_attn_desc(desc);
+  if (st) return st;
+  if (!attn_softmax_supported(desc->dtype == HSTU_BF16, desc->d_qk, desc->d_v,
+                              desc->num_pos_buckets))
+    return fail(HSTU_UNSUPPORTED, "softmax attention needs bf16, d_qk == d_v and P <= 1024");
+  Jagged j;
+  if ((st = check_offsets(seq_offsets_host, desc->batch, desc->max_seq_len, kMfmaRows,
+                          "seq_offsets", &j)))
+    return st;
+  *bytes = align_up((size_t)j.items * sizeof(int2)) +
+           align_up((size_t)key_range_slots(j.total, desc->batch) * sizeof(KeyRange));
+  return HSTU_OK;
+}
+
+// The softmax ablation of hstu_attn_fwd (HSTU chapter, "No sequence-wise softmax").
+hstu_status hstu_softmax_attn_fwd(const hstu_attn_desc* desc, const int64_t* seq_offsets_host,
+                                  const int64_t* seq_offsets, const int64_t* timestamps,
+                                  const void* q, const void* k, const void* v,
+                                  const float* rab_pos, const float* rab_time, void* out,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  size_t need = 0;
+  hstu_status st = hstu_softmax_attn_workspace_size(desc, seq_offsets_host, &need);
+  if (st) return st;
+  Jagged j;
+  check_offsets(seq_offsets_host, desc->batch, desc->max_seq_len, kMfmaRows, "seq_offsets", &j);
+  if ((int64_t)j.items * desc->num_heads >= (int64_t(1) << 31))
+    return fail(HSTU_UNSUPPORTED, "too many query tiles for one launch");
+  if (j.total == 0) return HSTU_OK;
+  if (!seq_offsets) return fail(HSTU_INVALID_ARGUMENT, "device seq_offsets is NULL");
+  if (!q || !k || !v || !out) return fail(HSTU_INVALID_ARGUMENT, "q, k, v and out are required");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return fail(HSTU_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
+  if ((st = check_ws(workspace, workspace_bytes, need, "workspace"))) return st;
+  hipStream_t s = (hipStream_t)stream;
+  Carver c{(char*)workspace};
+  int2* items = (int2*)c.take((size_t)j.items * sizeof(int2));
+  KeyRange* kr = (KeyRange*)c.take((size_t)key_range_slots(j.total, desc->batch) * sizeof(KeyRange));
+  HSTU_TRY(launch_plan_causal(seq_offsets, desc->batch, kMfmaRows, j.max_tiles, items,
+                              (int)j.items, s),
+           "tile planner");
+  if (timestamps)
+    HSTU_TRY(launch_key_ranges(seq_offsets, timestamps, desc->batch, j.max_len, kr, s),
+             "key ranges");
+  AttnArgs a = base_args(desc);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.ld_q = a.ld_k = (int64_t)desc->num_heads * desc->d_qk;
+  a.ld_v = a.ld_o = (int64_t)desc->num_heads * desc->d_v;
+  a.q_offsets = a.k_offsets = seq_offsets;
+  a.ts_q = a.ts_k = timestamps;
+  a.rab_pos = rab_pos;
+  a.rab_time = rab_time;
+  a.key_ranges = timestamps ? kr : nullptr;
+  a.items = items;
+  a.n_items = (int)j.items;
+  HSTU_TRY(launch_attn_softmax(a, s), "softmax attention");
+  return HSTU_OK;
+}
+
 // Stochastic Length (HSTU chapter, "Three more scaling components"): the
 // target length and the keep-whole decision, in double precision on the host.
 hstu_status hstu_sl_lengths(const hstu_sl_desc* desc, const int64_t* offsets_host,

@@ -71,6 +71,11 @@ hipError_t launch_plan_causal(const int64_t* offsets, int B, int tile_rows, int 
 hipError_t launch_key_ranges(const int64_t* offsets, const int64_t* ts, int B, int64_t max_len,
                              KeyRange* out, hipStream_t s);
 hipError_t launch_attn_simple(const AttnArgs& a, int use_bf16, bool cand, hipStream_t s);
+// Causal softmax attention (the softmax ablation of the pointwise kernel): bf16,
+// d_qk == d_v in {32,64,128}, P <= 1024; items from the planner with 128-row tiles,
+// key ranges whenever ts_q is set; out is bf16 [rows, H, d_v] with stride ld_o.
+bool attn_softmax_supported(int dtype_bf16, int d_qk, int d_v, int P);
+hipError_t launch_attn_softmax(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_mfma(const AttnArgs& a, bool cand, hipStream_t s);
 
 // One attention backward launch (causal mode). Row strides (ld_*) are in elements;

@@ -97,6 +97,10 @@ _sig = {
     "hstu_layer_bwd": ([ctypes.POINTER(hstu_layer_desc), _I64P, _P, _P, _P,
                         ctypes.POINTER(hstu_layer_weights), _P, _P, ctypes.POINTER(hstu_layer_grads),
                         _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "hstu_softmax_attn_workspace_size": ([ctypes.POINTER(hstu_attn_desc), _I64P, _SZP],
+                                         ctypes.c_int),
+    "hstu_softmax_attn_fwd": ([ctypes.POINTER(hstu_attn_desc), _I64P, _P, _P, _P, _P, _P, _P, _P, _P,
+                               _P, ctypes.c_size_t, _P], ctypes.c_int),
     "hstu_sl_lengths": ([ctypes.POINTER(hstu_sl_desc), _I64P, ctypes.POINTER(ctypes.c_float), _I64P,
                          _I64P], ctypes.c_int),
     "hstu_sl_sample": ([ctypes.c_int32, _I64P, _I64P, _P, _P, _P, _P, _P, ctypes.c_int64, _P, _P,
@@ -417,6 +421,27 @@ def hstu_layer_bwd(seq_offsets, timestamps, x, layers: Sequence[LayerWeights], d
                               _ptr(x), arr, _ptr(d_y), _ptr(dx), garr, _ptr(ws), nbytes,
                               _stream(stream)))
     return dx, grads
+
+
+def hstu_softmax_attn_fwd(seq_offsets, timestamps, q, k, v, rab_pos=None, rab_time=None, *,
+                          max_seq_len: int, num_pos_buckets=None, num_time_buckets=None, out=None,
+                          workspace=None, seq_offsets_host=None, stream=None) -> torch.Tensor:
+    """Causal softmax attention over the same scores as hstu_attn_fwd (bf16 only)."""
+    host = _host_offsets(seq_offsets, seq_offsets_host)
+    T_tot, H, d_qk = q.shape
+    d_v = v.shape[2]
+    P = rab_pos.shape[1] if rab_pos is not None else (num_pos_buckets or 1)
+    T = rab_time.shape[1] if rab_time is not None else (num_time_buckets or 1)
+    desc = attn_desc(len(host) - 1, H, d_qk, d_v, max_seq_len, P, T, _dtype_code(q))
+    if out is None:
+        out = torch.empty((T_tot, H, d_v), dtype=q.dtype, device=q.device)
+    n = ctypes.c_size_t(0)
+    _check(lib.hstu_softmax_attn_workspace_size(ctypes.byref(desc), _i64p(host), ctypes.byref(n)))
+    ws, nbytes = _workspace(n.value, q.device, workspace)
+    _check(lib.hstu_softmax_attn_fwd(ctypes.byref(desc), _i64p(host), _ptr(seq_offsets),
+                                     _ptr(timestamps), _ptr(q), _ptr(k), _ptr(v), _ptr(rab_pos),
+                                     _ptr(rab_time), _ptr(out), _ptr(ws), nbytes, _stream(stream)))
+    return out
 
 
 def hstu_sl_lengths(offsets_host, max_seq_len: int, alpha: float, u_keep_host):

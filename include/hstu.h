@@ -299,6 +299,25 @@ hstu_status hstu_layer_bwd(const hstu_layer_desc* desc, const int64_t* seq_offse
                            size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * hstu_softmax_attn_fwd: the softmax variant of hstu_attn_fwd (u == NULL), the
+ * ablation of the HSTU chapter ("No sequence-wise softmax") that replaces the
+ * pointwise activation with a softmax over each query's visible keys:
+ *   out[i,h,:] = sum_{j<=i} exp(z_ij) v_j / sum_{j<=i} exp(z_ij),
+ *   z_ij = q_i.k_j + bias_h(i,j)   (the same scores, buckets and tables; no 1/sqrt(d)).
+ * It is the in-house softmax-attention baseline for the pointwise kernel. Arguments
+ * and layouts as hstu_attn_fwd. Support: dtype HSTU_BF16 (fp32 accumulation),
+ * d_qk == d_v in {32, 64, 128}, num_pos_buckets <= 1024 (HSTU_UNSUPPORTED otherwise).
+ * `workspace` is hstu_softmax_attn_workspace_size bytes.
+ * ---------------------------------------------------------------------- */
+hstu_status hstu_softmax_attn_workspace_size(const hstu_attn_desc* desc,
+                                             const int64_t* seq_offsets_host, size_t* bytes);
+hstu_status hstu_softmax_attn_fwd(const hstu_attn_desc* desc, const int64_t* seq_offsets_host,
+                                  const int64_t* seq_offsets, const int64_t* timestamps,
+                                  const void* q, const void* k, const void* v,
+                                  const float* rab_pos, const float* rab_time, void* out,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Stochastic Length (HSTU chapter, "Three more scaling components",
  * Stochastic Length): training keeps the full history of short users and of a
  * few long ones, and cuts the rest to a random subsequence of the target
