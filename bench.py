@@ -213,11 +213,15 @@ def leg_backward(steps, warmup):
     g = torch.from_numpy(synth.normal(np.random.default_rng(7), x.v.shape, 1.0, "bf16")).to(
         torch.bfloat16).cuda()
     stream = torch.cuda.Stream()
+    desc = ops.attn_desc(len(x.offsets) - 1, x.num_heads, x.d_qk, x.d_v, x.max_seq_len,
+                         x.num_pos_buckets, x.num_time_buckets, ops.HSTU_BF16)
+    ws = torch.empty(max(1, ops.hstu_attn_bwd_workspace_size(desc, x.offsets)), dtype=torch.uint8,
+                     device="cuda")
 
     def call():
         ops.hstu_attn_bwd(d["offsets"], d["ts"], d["q"], d["k"], d["v"], g, d["rab_pos"],
-                          d["rab_time"], max_seq_len=x.max_seq_len, seq_offsets_host=x.offsets,
-                          stream=stream)
+                          d["rab_time"], max_seq_len=x.max_seq_len, workspace=ws,
+                          seq_offsets_host=x.offsets, stream=stream)
 
     with torch.cuda.stream(stream):
         ms, _ = time_calls(call, stream, max(5, steps // 5), max(2, warmup // 5))
@@ -232,12 +236,16 @@ def leg_backward(steps, warmup):
         dl = layer_to_device(xl)
         gy = torch.from_numpy(synth.normal(np.random.default_rng(8), xl.x.shape, 1.0, "bf16")).to(
             torch.bfloat16).cuda()
+        ldesc = ops.layer_desc(dl["layers"], len(xl.offsets) - 1, xl.num_heads, xl.d_qk, xl.d_v,
+                               xl.d_model, xl.max_seq_len, ops.HSTU_BF16)
+        lws = torch.empty(max(1, ops.hstu_layer_bwd_workspace_size(ldesc, xl.offsets)),
+                          dtype=torch.uint8, device="cuda")
 
         def lcall():
             ops.hstu_layer_bwd(dl["offsets"], dl["ts"], dl["x"], dl["layers"], gy,
                                num_heads=xl.num_heads, d_qk=xl.d_qk, d_v=xl.d_v,
-                               max_seq_len=xl.max_seq_len, seq_offsets_host=xl.offsets,
-                               stream=stream)
+                               max_seq_len=xl.max_seq_len, workspace=lws,
+                               seq_offsets_host=xl.offsets, stream=stream)
 
         with torch.cuda.stream(stream):
             ms, _ = time_calls(lcall, stream, max(5, steps // 5), max(2, warmup // 5))

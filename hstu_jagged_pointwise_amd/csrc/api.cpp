@@ -576,11 +576,12 @@ hstu_status run_candidates(const mfalcon_desc* d, const MfPlan& p, const int64_t
                "candidate f2 projection");
       in = out;
     }
-    if (cand_logit)
-      HSTU_TRY(launch_rowdot((const char*)cand_out + (size_t)m0 * dm * es, dm, w_head,
-                             cand_logit + m0, rows, dm, bf, s),
-               "candidate logit");
   }
+  // the logits of every candidate in one launch (each row's dot product is independent
+  // of the microbatch it was scored in)
+  if (cand_logit)
+    HSTU_TRY(launch_rowdot(cand_out, dm, w_head, cand_logit, p.cand_total, dm, bf, s),
+             "candidate logit");
   return HSTU_OK;
 }
 

@@ -191,6 +191,28 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
       for (int i = 0; i < 8; ++i) qf[kk][i] = (bf16)0.f;
     }
   }
+  // candidate mode, first key range: the candidate's own key (relative position 0,
+  // elapsed time 0) is loaded with Q and its SiLU score kept for the epilogue
+  const bool add_self = CAND && blockIdx.z == 0;
+  if (add_self) {
+    const bf16* kc = (const bf16*)a.kc;
+    float part = 0.f;
+    if (row_ok) {
+      bf16x8 kf[NKK];
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk)
+        kf[kk] = load_bf16x8(kc + (t.q_local + wrow) * a.ld_kc + (int64_t)h * D + 16 * kk + 8 * hl);
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) part = fmaf((float)qf[kk][i], (float)kf[kk][i], part);
+    }
+    part += __shfl_xor(part, 32, 64);
+    float xs = part;
+    if (has_pos) xs += sload(a.rab_pos + (int64_t)h * P);
+    if (has_time) xs += sload(a.rab_time + (int64_t)h * T);
+    if (hl == 0) pself[w][l32] = row_ok ? silu_fast(xs) : 0.f;  // read back by this wavefront
+  }
   const int64_t tq = (has_time && row_ok) ? a.ts_q[t.q_base + wrow] : 0;
   const uint32_t tq1 = (uint32_t)tq + 1u;
   const int64_t qmin = uniform64(wave_min64(row_ok ? tq : INT64_MAX));
@@ -577,30 +599,23 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
     if (kt + 1 < nkt) tile_step(B1{}, kt + 1);
   }
 
-  const bool add_self = CAND && blockIdx.z == 0;
-  if (add_self) {
-    // the candidate's own key and value: relative position 0, elapsed time 0
-    const bf16* kc = (const bf16*)a.kc;
-    float part = 0.f;
-    if (row_ok) {
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        const bf16x8 kf =
-            load_bf16x8(kc + (t.q_local + wrow) * a.ld_kc + (int64_t)h * D + 16 * kk + 8 * hl);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) part = fmaf((float)qf[kk][i], (float)kf[i], part);
-      }
-    }
-    part += __shfl_xor(part, 32, 64);
-    float x = part;
-    if (has_pos) x += rp[0];
-    if (has_time) x += rt[0];
-    if (hl == 0) pself[w][l32] = row_ok ? silu_fast(x) : 0.f;
-  }
   __syncthreads();
   if (!wave_live) return;
 
-  const bf16* vc = (const bf16*)a.vc;
+  // the candidate's own value, weighted by its self score: every load is issued
+  // before the first use, so their latencies overlap
+  float vself[NC][16];
+  if constexpr (CAND) {
+    const bf16* vc = (const bf16*)a.vc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int rowl = 32 * w + 8 * (r >> 2) + 4 * hl + (r & 3);
+      const bool ok = add_self && rowl < t.rows;
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        vself[c][r] = ok ? (float)vc[(t.q_local + rowl) * a.ld_vc + (int64_t)h * D + c * 32 + l32] : 0.f;
+    }
+  }
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int rw = 8 * (r >> 2) + 4 * hl + (r & 3);  // row within the wavefront
@@ -608,12 +623,12 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
     if (rowl >= t.rows) continue;
     const int64_t orow = (CAND ? (int64_t)blockIdx.z * a.part_stride : 0) +
                          (t.q_local + rowl) * a.ld_o + (int64_t)h * D;
+    const float ps = add_self ? pself[w][rw] : 0.f;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const int col = c * 32 + l32;
       float val = o[c][r];
-      if (add_self)
-        val = fmaf(pself[w][rw], (float)vc[(t.q_local + rowl) * a.ld_vc + (int64_t)h * D + col], val);
+      if constexpr (CAND) val = fmaf(ps, vself[c][r], val);
       val *= a.inv_n;
       if (a.out_f32)
         ((float*)a.out)[orow + col] = val;

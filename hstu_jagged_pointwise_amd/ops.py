@@ -389,6 +389,20 @@ def hstu_attn_bwd(seq_offsets, timestamps, q, k, v, d_out, rab_pos=None, rab_tim
     return dq, dk, dv, drp, drt
 
 
+def hstu_attn_bwd_workspace_size(desc: hstu_attn_desc, seq_offsets_host) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib.hstu_attn_bwd_workspace_size(ctypes.byref(desc), _i64p(seq_offsets_host),
+                                            ctypes.byref(n)))
+    return n.value
+
+
+def hstu_layer_bwd_workspace_size(desc: hstu_layer_desc, seq_offsets_host) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib.hstu_layer_bwd_workspace_size(ctypes.byref(desc), _i64p(seq_offsets_host),
+                                             ctypes.byref(n)))
+    return n.value
+
+
 _GRAD_FIELDS = ("dw1", "db1", "d_rab_pos", "d_rab_time", "d_ln_gamma", "d_ln_beta", "dw2", "db2")
 
 
