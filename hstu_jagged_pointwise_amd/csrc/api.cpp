@@ -10,6 +10,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 #include <utility>
 #include <vector>
@@ -397,18 +398,64 @@ void carve_hist_ws(Carver& c, const mfalcon_desc* d, const MfPlan& p, MfHistBufs
   b->hx[1] = ld.num_layers > 2 ? c.take((size_t)nh * ld.d_model * es) : nullptr;
 }
 
-void carve_cand_ws(Carver& c, const mfalcon_desc* d, const MfPlan& p, MfCandBufs* b) {
+// Streams (and buffer sets) of the candidate pass: microbatches are dealt round robin
+// to kCandStreams streams when there is more than one microbatch, else one set runs on
+// the caller's stream. Four is the number of hardware queues HIP opens per device by
+// default, so the four streams run side by side.
+constexpr int kCandStreams = 4;
+int cand_sets(const mfalcon_desc* d, const MfPlan& p) {
+  const int64_t nmb = (p.cand_total + d->microbatch - 1) / d->microbatch;
+  return nmb > 1 ? kCandStreams : 1;
+}
+
+void carve_cand_ws(Carver& c, const mfalcon_desc* d, const MfPlan& p, MfCandBufs* bs) {
   const hstu_layer_desc& ld = d->layer;
   const hstu_attn_desc& a = ld.attn;
   const size_t es = elt_size(a.dtype);
   const int64_t f1 = 2LL * a.num_heads * (a.d_v + a.d_qk);
   const int64_t hv = (int64_t)a.num_heads * a.d_v;
   const int64_t m = std::min<int64_t>(d->microbatch, std::max<int64_t>(p.cand_total, 1));
-  b->c_uvqk = c.take((size_t)m * f1 * es);
-  b->c_o = (float*)c.take((size_t)p.kv_splits * m * hv * sizeof(float));
-  b->c_g = c.take((size_t)m * hv * es);
-  b->cx[0] = ld.num_layers > 1 ? c.take((size_t)m * ld.d_model * es) : nullptr;
-  b->cx[1] = ld.num_layers > 2 ? c.take((size_t)m * ld.d_model * es) : nullptr;
+  for (int i = 0; i < cand_sets(d, p); ++i) {
+    MfCandBufs* b = bs + i;
+    b->c_uvqk = c.take((size_t)m * f1 * es);
+    b->c_o = (float*)c.take((size_t)p.kv_splits * m * hv * sizeof(float));
+    b->c_g = c.take((size_t)m * hv * es);
+    b->cx[0] = ld.num_layers > 1 ? c.take((size_t)m * ld.d_model * es) : nullptr;
+    b->cx[1] = ld.num_layers > 2 ? c.take((size_t)m * ld.d_model * es) : nullptr;
+  }
+}
+
+// The streams of the candidate pass, with their fork and join events: one set per
+// device, created together at the first call that needs them and kept for the life of
+// the process (default priority). Streams are dealt to the device's hardware queues
+// round robin, so streams created one after the other do not share a queue (the
+// caller's stream may share one with any of them, which is why it only forks and
+// joins). The mutex makes the enqueue of one call's fork ... join sequence atomic with
+// respect to other host threads using the same device.
+struct AuxStream {
+  hipStream_t s[kCandStreams] = {};
+  hipEvent_t fork = nullptr, join[kCandStreams] = {};
+};
+constexpr int kMaxDevices = 64;
+std::mutex g_aux_mu[kMaxDevices];
+AuxStream g_aux[kMaxDevices];
+
+hstu_status aux_stream(int* dev, AuxStream** out) {
+  HSTU_TRY(hipGetDevice(dev), "current device");
+  if (*dev < 0 || *dev >= kMaxDevices) return fail(HSTU_UNSUPPORTED, "device index %d", *dev);
+  AuxStream& a = g_aux[*dev];
+  if (!a.join[kCandStreams - 1]) {
+    for (int i = 0; i < kCandStreams; ++i)
+      if (!a.s[i])
+        HSTU_TRY(hipStreamCreateWithFlags(&a.s[i], hipStreamNonBlocking), "candidate stream");
+    if (!a.fork)
+      HSTU_TRY(hipEventCreateWithFlags(&a.fork, hipEventDisableTiming), "candidate event");
+    for (int i = 0; i < kCandStreams; ++i)
+      if (!a.join[i])
+        HSTU_TRY(hipEventCreateWithFlags(&a.join[i], hipEventDisableTiming), "candidate event");
+  }
+  *out = &a;
+  return HSTU_OK;
 }
 
 // The history half of the plan (cand offsets may be NULL: then no candidate sizes).
@@ -453,8 +500,8 @@ hstu_status plan_mfalcon(const mfalcon_desc* d, const int64_t* hoff, const int64
   carve_hist_ws(h, d, *p, &hb);
   p->hist_ws = h.off;
   Carver k{nullptr};
-  MfCandBufs kb;
-  carve_cand_ws(k, d, *p, &kb);
+  MfCandBufs kb[kCandStreams];
+  carve_cand_ws(k, d, *p, kb);
   p->cand_ws = k.off;
   return HSTU_OK;
 }
@@ -501,7 +548,7 @@ hstu_status run_candidates(const mfalcon_desc* d, const MfPlan& p, const int64_t
                            const int64_t* cand_offsets_host, const int64_t* cand_offsets,
                            const int64_t* cand_ts, const void* cand_x,
                            const hstu_layer_weights* weights, const float* w_head, void* cand_out,
-                           float* cand_logit, const MfCandBufs& b, hipStream_t s) {
+                           float* cand_logit, const MfCandBufs* bufs, hipStream_t s0) {
   const hstu_layer_desc& ld = d->layer;
   const hstu_attn_desc& a = ld.attn;
   const int L = ld.num_layers;
@@ -511,76 +558,111 @@ hstu_status run_candidates(const mfalcon_desc* d, const MfPlan& p, const int64_t
   const int dm = ld.d_model;
   const int B = a.batch;
   const int64_t m = d->microbatch;
-  for (int64_t m0 = 0; m0 < p.cand_total; m0 += m) {
-    const int64_t m1 = std::min(m0 + m, p.cand_total);
-    const int64_t rows = m1 - m0;
-    // users whose candidate range overlaps [m0, m1)
-    int ub = (int)(std::upper_bound(cand_offsets_host, cand_offsets_host + B + 1, m0) -
-                   cand_offsets_host) - 1;
-    int ue = (int)(std::lower_bound(cand_offsets_host, cand_offsets_host + B + 1, m1) -
-                   cand_offsets_host);  // one past the last overlapping user
-    ub = std::max(ub, 0);
-    ue = std::min(ue, B);
-    int64_t max_rows = 0;
-    for (int u = ub; u < ue; ++u) {
-      const int64_t cs = std::max(cand_offsets_host[u], m0), ce = std::min(cand_offsets_host[u + 1], m1);
-      max_rows = std::max(max_rows, ce - cs);
-    }
-    const void* in = (const char*)cand_x + (size_t)m0 * dm * es;
-    for (int l = 0; l < L; ++l) {
-      const hstu_layer_weights& w = weights[l];
-      void* out = (l == L - 1) ? (void*)((char*)cand_out + (size_t)m0 * dm * es) : b.cx[l % 2];
-      const int64_t f1 = 2LL * a.num_heads * (a.d_v + a.d_qk);
-      HSTU_TRY(launch_gemm(in, dm, w.w1, dm, w.b1, nullptr, 0, b.c_uvqk, f1, rows, (int)f1, dm, 1,
-                           bf, s),
-               "candidate f1 projection");
-      const UVQK cv = split_view(b.c_uvqk, a);
-      const UVQK hvw = split_view(cache.uvqk[l], a);
-      AttnArgs aa = base_args(&a);
-      aa.q = cv.q;
-      aa.ld_q = cv.ld;
-      aa.kc = cv.k;
-      aa.vc = cv.v;
-      aa.ld_kc = aa.ld_vc = cv.ld;
-      aa.k = hvw.k;
-      aa.v = hvw.v;
-      aa.ld_k = aa.ld_v = hvw.ld;
-      aa.out = b.c_o;
-      aa.ld_o = hv;
-      aa.out_f32 = 1;
-      aa.q_offsets = cand_offsets;
-      aa.k_offsets = hist_offsets;
-      aa.ts_q = cand_ts;
-      aa.ts_k = hist_ts;
-      aa.rab_pos = w.rab_pos;
-      aa.rab_time = w.rab_time;
-      aa.key_ranges = (hist_ts && w.rab_time) ? cache.kr : nullptr;  // unread when no history
-      aa.row_begin = m0;
-      aa.row_end = m1;
-      aa.max_user_rows = max_rows;
-      // key-range splits of the history: fixed by the history lengths alone, so a
-      // candidate's reduction order never depends on the microbatch around it
-      aa.kv_splits = p.kv_splits;
-      aa.keys_per_split = p.keys_per_split;
-      aa.part_stride = rows * hv;
-      for (int u0 = ub; u0 < ue; u0 += 65535) {
-        aa.user_begin = u0;
-        aa.n_users = std::min(ue - u0, 65535);
-        HSTU_TRY(run_attention(&a, aa, true, s), "candidate attention");
-      }
-      HSTU_TRY(launch_ln_gate(b.c_o, hv, aa.kv_splits, aa.part_stride, cv.u, cv.ld, w.ln_gamma,
-                              w.ln_beta, a.ln_eps, b.c_g, hv, rows, hv, bf, s),
-               "candidate layer norm gate");
-      HSTU_TRY(launch_gemm(b.c_g, hv, w.w2, hv, w.b2, ld.residual ? in : nullptr, dm, out, dm, rows,
-                           dm, hv, 0, bf, s),
-               "candidate f2 projection");
-      in = out;
+  // With several microbatches, microbatch i runs on the library's stream i % 4 with
+  // buffer set i % 4, so that the projections and gates of some microbatches fill the
+  // gaps and tails of the others' attention. The streams are forked from the caller's
+  // stream after the work already queued there (the history pass) and joined back before
+  // the logits. Each microbatch's results are those of a serial run.
+  const int sets = cand_sets(d, p);
+  hipStream_t st[kCandStreams];
+  for (int i = 0; i < kCandStreams; ++i) st[i] = s0;
+  AuxStream* aux = nullptr;
+  std::unique_lock<std::mutex> lock;
+  if (sets > 1) {
+    int dev = 0;
+    hstu_status ast = aux_stream(&dev, &aux);
+    if (ast) return ast;
+    lock = std::unique_lock<std::mutex>(g_aux_mu[dev]);
+    HSTU_TRY(hipEventRecord(aux->fork, s0), "candidate fork");
+    for (int i = 0; i < kCandStreams; ++i) {
+      st[i] = aux->s[i];
+      HSTU_TRY(hipStreamWaitEvent(aux->s[i], aux->fork, 0), "candidate fork");
     }
   }
+  auto microbatches = [&]() -> hstu_status {
+    int64_t mb = 0;
+    for (int64_t m0 = 0; m0 < p.cand_total; m0 += m, ++mb) {
+      const hipStream_t s = st[mb % sets];
+      const MfCandBufs& b = bufs[mb % sets];
+      const int64_t m1 = std::min(m0 + m, p.cand_total);
+      const int64_t rows = m1 - m0;
+      // users whose candidate range overlaps [m0, m1)
+      int ub = (int)(std::upper_bound(cand_offsets_host, cand_offsets_host + B + 1, m0) -
+                     cand_offsets_host) - 1;
+      int ue = (int)(std::lower_bound(cand_offsets_host, cand_offsets_host + B + 1, m1) -
+                     cand_offsets_host);  // one past the last overlapping user
+      ub = std::max(ub, 0);
+      ue = std::min(ue, B);
+      int64_t max_rows = 0;
+      for (int u = ub; u < ue; ++u) {
+        const int64_t cs = std::max(cand_offsets_host[u], m0);
+        const int64_t ce = std::min(cand_offsets_host[u + 1], m1);
+        max_rows = std::max(max_rows, ce - cs);
+      }
+      const void* in = (const char*)cand_x + (size_t)m0 * dm * es;
+      for (int l = 0; l < L; ++l) {
+        const hstu_layer_weights& w = weights[l];
+        void* out = (l == L - 1) ? (void*)((char*)cand_out + (size_t)m0 * dm * es) : b.cx[l % 2];
+        const int64_t f1 = 2LL * a.num_heads * (a.d_v + a.d_qk);
+        HSTU_TRY(launch_gemm(in, dm, w.w1, dm, w.b1, nullptr, 0, b.c_uvqk, f1, rows, (int)f1, dm, 1,
+                             bf, s),
+                 "candidate f1 projection");
+        const UVQK cv = split_view(b.c_uvqk, a);
+        const UVQK hvw = split_view(cache.uvqk[l], a);
+        AttnArgs aa = base_args(&a);
+        aa.q = cv.q;
+        aa.ld_q = cv.ld;
+        aa.kc = cv.k;
+        aa.vc = cv.v;
+        aa.ld_kc = aa.ld_vc = cv.ld;
+        aa.k = hvw.k;
+        aa.v = hvw.v;
+        aa.ld_k = aa.ld_v = hvw.ld;
+        aa.out = b.c_o;
+        aa.ld_o = hv;
+        aa.out_f32 = 1;
+        aa.q_offsets = cand_offsets;
+        aa.k_offsets = hist_offsets;
+        aa.ts_q = cand_ts;
+        aa.ts_k = hist_ts;
+        aa.rab_pos = w.rab_pos;
+        aa.rab_time = w.rab_time;
+        aa.key_ranges = (hist_ts && w.rab_time) ? cache.kr : nullptr;  // unread when no history
+        aa.row_begin = m0;
+        aa.row_end = m1;
+        aa.max_user_rows = max_rows;
+        // key-range splits of the history: fixed by the history lengths alone, so a
+        // candidate's reduction order never depends on the microbatch around it
+        aa.kv_splits = p.kv_splits;
+        aa.keys_per_split = p.keys_per_split;
+        aa.part_stride = rows * hv;
+        for (int u0 = ub; u0 < ue; u0 += 65535) {
+          aa.user_begin = u0;
+          aa.n_users = std::min(ue - u0, 65535);
+          HSTU_TRY(run_attention(&a, aa, true, s), "candidate attention");
+        }
+        HSTU_TRY(launch_ln_gate(b.c_o, hv, aa.kv_splits, aa.part_stride, cv.u, cv.ld, w.ln_gamma,
+                                w.ln_beta, a.ln_eps, b.c_g, hv, rows, hv, bf, s),
+                 "candidate layer norm gate");
+        HSTU_TRY(launch_gemm(b.c_g, hv, w.w2, hv, w.b2, ld.residual ? in : nullptr, dm, out, dm,
+                             rows, dm, hv, 0, bf, s),
+                 "candidate f2 projection");
+        in = out;
+      }
+    }
+    return HSTU_OK;
+  };
+  const hstu_status rs = microbatches();
+  if (sets > 1)  // joined also after a failed launch, so that nothing runs past the call
+    for (int i = 0; i < kCandStreams; ++i) {
+      HSTU_TRY(hipEventRecord(aux->join[i], aux->s[i]), "candidate join");
+      HSTU_TRY(hipStreamWaitEvent(s0, aux->join[i], 0), "candidate join");
+    }
+  if (rs) return rs;
   // the logits of every candidate in one launch (each row's dot product is independent
   // of the microbatch it was scored in)
   if (cand_logit)
-    HSTU_TRY(launch_rowdot(cand_out, dm, w_head, cand_logit, p.cand_total, dm, bf, s),
+    HSTU_TRY(launch_rowdot(cand_out, dm, w_head, cand_logit, p.cand_total, dm, bf, s0),
              "candidate logit");
   return HSTU_OK;
 }
@@ -661,7 +743,7 @@ void split_k(int64_t M, int64_t N, int64_t K, bool bf, int* splits, int64_t* ks)
   int64_t sp = std::max<int64_t>(1, 512 / std::max<int64_t>(tiles, 1));
   sp = std::min<int64_t>(sp, std::max<int64_t>(1, K / 256));
   int64_t k = (K + sp - 1) / sp;
-  k = (k + 31) / 32 * 32;
+  k = (k + 63) / 64 * 64;  // whole pipeline stages of either GEMM tile shape
   *splits = (int)((K + k - 1) / k);
   *ks = k;
 }
@@ -1106,8 +1188,8 @@ hstu_status mfalcon_score(const mfalcon_desc* desc, const int64_t* hist_offsets_
   MfHistBufs hb;
   carve_hist_ws(c, desc, p, &hb);
   c.off = align_up(p.cache) + align_up(p.hist_ws);
-  MfCandBufs cb;
-  carve_cand_ws(c, desc, p, &cb);
+  MfCandBufs cb[kCandStreams];
+  carve_cand_ws(c, desc, p, cb);
   if ((st = run_history(desc, p, hist_offsets, hist_ts, hist_x, weights, cache, hb, s))) return st;
   return run_candidates(desc, p, hist_offsets, hist_ts, cache, cand_offsets_host, cand_offsets,
                         cand_ts, cand_x, weights, w_head, cand_out, cand_logit, cb, s);
@@ -1190,8 +1272,8 @@ hstu_status mfalcon_score_cached(const mfalcon_desc* desc, const int64_t* hist_o
   MfCache cb;
   carve_cache(c, desc, p, &cb);
   Carver w{(char*)workspace};
-  MfCandBufs kb;
-  carve_cand_ws(w, desc, p, &kb);
+  MfCandBufs kb[kCandStreams];
+  carve_cand_ws(w, desc, p, kb);
   return run_candidates(desc, p, hist_offsets, hist_ts, cb, cand_offsets_host, cand_offsets,
                         cand_ts, cand_x, weights, w_head, cand_out, cand_logit, kb,
                         (hipStream_t)stream);

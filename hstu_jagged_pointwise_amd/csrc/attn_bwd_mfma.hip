@@ -257,7 +257,7 @@ __global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void attn_bwd_q_mfma(AttnBwdA
 
 // ------------------------------------------------------------------ key side
 template <int D>
-__global__ __launch_bounds__(256, 1) void attn_bwd_kv_mfma(AttnBwdArgs a) {
+__global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void attn_bwd_kv_mfma(AttnBwdArgs a) {
   constexpr int NKK = D / 16, NC = D / 32;
   __shared__ __attribute__((aligned(16))) bf16 Qs[2][TR * (D + 8)];
   __shared__ __attribute__((aligned(16))) bf16 Gs[2][TR * (D + 8)];
@@ -378,7 +378,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kv_mfma(AttnBwdArgs a) {
       }
       const bf16* Qt = Qs[buf];
       const bf16* Gt = Gs[buf];
-#pragma unroll
+#pragma unroll 1
       for (int qb = 0; qb < 2; ++qb) {
         const int64_t q0b = qbeg + (int64_t)qt * TR + 32 * qb;
         if (!wave_live || q0b + 31 < k0w || q0b >= t.n) continue;  // uniform
@@ -438,24 +438,33 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kv_mfma(AttnBwdArgs a) {
             add_bins(blo, zlo, zhi);
           }
         } else {
-          int btv[16];
-          float zv[16];
-          float csum = 0.f;  // this lane's dz in position bucket P-1
+          // positions within a sequence fit in 32 bits
+          const int i0 = (int)(qbeg + (int64_t)qt * TR), n32 = (int)t.n, j32 = (int)j;
+          const uint32_t tk32 = (uint32_t)tk;
+          float csum = 0.f;                   // this lane's dz in position bucket P-1
+          float zb[4] = {0.f, 0.f, 0.f, 0.f};  // ... in time buckets blo .. blo+3
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int ir = 32 * qb + acc_row(r, hl);  // query row within the tile
-            const int64_t i = qbeg + (int64_t)qt * TR + ir;
-            const bool vis = key_ok && i < t.n && j <= i;
-            const int bp = pos_bucket((int)(i - j), a.P);
-            const int bt = has_ts ? tbucket(tqs[buf][ir] - tk, a.T) : 0;
+            const int i = i0 + ir;
+            const bool vis = key_ok && i < n32 && j32 <= i;
+            const int bp = pos_bucket(i - j32, a.P);
+            int bt = 0;
+            if (has_ts) {
+              if (fits32) {  // t_i + 1 - t_j fits 32 bits; it is <= 0 for negative elapsed times
+                const int d1 = (int)(tqs32[buf][ir] + 1u - tk32);
+                bt = d1 <= 0 ? 0 : 31 - __builtin_clz((uint32_t)d1);
+                bt = bt < a.T - 1 ? bt : a.T - 1;
+              } else {
+                bt = tbucket(tqs[buf][ir] - tk, a.T);
+              }
+            }
             const float z = s[r] + rps[bp] + rts[bt];
             float p, dsl;
             silu2(z, a.inv_n, p, dsl);
             const float dz = vis ? dp[r] * dsl : 0.f;
             pp[r >> 3][r & 7] = (bf16)(vis ? p : 0.f);
             pz[r >> 3][r & 7] = (bf16)dz;
-            btv[r] = bt;
-            zv[r] = dz;
             // below the clamp, the lanes of one slot (one query, 32 keys) hold distinct
             // buckets, so these atomics do not collide
             if (a.bias_partial) {
@@ -463,18 +472,20 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_kv_mfma(AttnBwdArgs a) {
                 csum += dz;
               else if (vis)
                 atomicAdd(&my_bins[bp], dz);
+              if (has_ts) {  // every visible pair's time bucket lies in [blo, bhi]
+                const int kb = bt - blo;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) zb[q] += kb == q ? dz : 0.f;
+                if (kb >= 4 && vis) atomicAdd(&my_bins[a.P + bt], dz);  // spans past 4 buckets
+              }
             }
           }
           if (a.bias_partial) {
             bin_clamp += csum;
-            // every visible pair's time bucket lies in [blo, bhi]: one reduction per bucket
-            if (has_ts)
-              for (int b = blo; b <= bhi; ++b) {
-                float tb = 0.f;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) tb += btv[r] == b ? zv[r] : 0.f;
-                tb = wave_sum64(tb);
-                if (lane == 0) my_bins[a.P + b] += tb;
+            if (has_ts)  // one reduction per bucket
+              for (int q = 0; q < 4 && blo + q <= bhi; ++q) {
+                const float tb = wave_sum64(zb[q]);
+                if (lane == 0) my_bins[a.P + blo + q] += tb;
               }
           }
         }

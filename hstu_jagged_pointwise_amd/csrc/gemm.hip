@@ -9,8 +9,10 @@
 // W is stored [out, in], so both operands are contiguous along the reduction
 // dimension and feed v_mfma_f32_32x32x16_bf16 directly from LDS rows. Workgroup
 // tiles are 128x128, or 64x64 when the grid would otherwise leave compute units
-// idle. K streams through a 4-stage LDS ring 32 at a time, with three stages in
-// flight, filled by global_load_lds. Tiles are ordered so that the tiles of one
+// idle. K streams through a 4-stage LDS ring, with three stages in flight, filled by
+// global_load_lds: 32 of K per stage for 128x128 tiles, 64 for 64x64 tiles (whose
+// workgroups do 4x less MFMA work per stage, so they need more of K in flight to
+// cover the load latency). Tiles are ordered so that the tiles of one
 // row block of A run on one XCD (sharing its L2). The epilogue stages each
 // wavefront's tile in LDS and writes whole 16-byte row segments. fp32 inputs
 // take a plain vector-ALU tiled kernel.
@@ -22,8 +24,9 @@
 namespace hstu {
 
 namespace {
-constexpr int GBK = 32;  // K per pipeline stage
-constexpr int NST = 4;   // LDS ring stages: NST-1 stages load while one is multiplied
+constexpr int NST = 4;  // LDS ring stages: NST-1 stages load while one is multiplied
+// K per pipeline stage of a BM-row tile
+constexpr int stage_k(int bm) { return bm >= 128 ? 32 : 64; }
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -44,6 +47,7 @@ __device__ __forceinline__ void lds_barrier() {
 // per-wavefront waits count instructions).
 template <int BM, int BN>
 struct GemmShape {
+  static constexpr int GBK = stage_k(BM);
   static constexpr int GLD = GBK + 8, GSPR = GLD / 8, CPR = GBK / 8;
   static constexpr int WM = BM / 2, WN = BN / 2;
   static constexpr int FM = WM / 32, FN = WN / 32;
@@ -68,6 +72,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const bf16* __restric
                                                          int tiles_total, int64_t ksplit,
                                                          int64_t c_split) {
   using G = GemmShape<BM, BN>;
+  constexpr int GBK = G::GBK;
   constexpr int FM = G::FM, FN = G::FN, PERW = G::PERW, STAGE = G::STAGE;
   constexpr int GLD = G::GLD, GSPR = G::GSPR, CPR = G::CPR;
   __shared__ __attribute__((aligned(16))) bf16 S0[STAGE];
@@ -309,11 +314,12 @@ hipError_t launch_gemm_ex(const void* A, int64_t lda, const void* W, int64_t ldw
       return hipErrorInvalidValue;
     if (splits < 1) splits = 1;
     if (splits == 1) ksplit = K;
-    // split K ranges are whole pipeline stages; a split tail carries no bias or residual
-    if (splits > 1 && (ksplit % GBK != 0 || (int64_t)(splits - 1) * ksplit >= K || bias || R || silu))
-      return hipErrorInvalidValue;
     // 128x128 tiles when they give at least ~one workgroup per compute unit, else 64x64
     const int64_t big = ((N + 127) / 128) * ((M + 127) / 128) * splits;
+    // split K ranges are whole pipeline stages; a split tail carries no bias or residual
+    const int gbk = stage_k(big >= 256 ? 128 : 64);
+    if (splits > 1 && (ksplit % gbk != 0 || (int64_t)(splits - 1) * ksplit >= K || bias || R || silu))
+      return hipErrorInvalidValue;
     auto go = [&](auto bm, auto outc) {
       constexpr int T = decltype(bm)::value;
       using O = typename decltype(outc)::type;

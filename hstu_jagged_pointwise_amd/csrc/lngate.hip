@@ -13,6 +13,8 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <type_traits>
+
 namespace hstu {
 
 template <typename T, int NPL>
@@ -73,6 +75,94 @@ __global__ __launch_bounds__(256) void ln_gate_reg_kernel(const float* __restric
   }
 }
 
+// Vector form for rows whose width is a multiple of 4 with 16-byte aligned fp32 rows: a
+// lane owns 4 adjacent columns per 256, so every load and store moves 16 (or 8) bytes.
+// The gate row, gamma and beta are requested first, then the partial rows of up to SB
+// splits at once, so that one wavefront has all of its row's traffic in flight.
+template <typename T, int NV>
+__global__ __launch_bounds__(256) void ln_gate_vec_kernel(const float* __restrict__ o, int64_t ld_o,
+                                                          int nsplit, int64_t split_stride,
+                                                          const T* __restrict__ u, int64_t ld_u,
+                                                          const float* __restrict__ gamma,
+                                                          const float* __restrict__ beta, float eps,
+                                                          T* __restrict__ out, int64_t ld_out,
+                                                          int64_t rows, int w) {
+  constexpr int SB = NV <= 1 ? 16 : 16 / NV;  // splits per batch of loads
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const float* orow = o + row * ld_o;
+  const T* urow = u + row * ld_u;
+  f32x4 uv[NV], gv[NV], bv[NV], x[NV];
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const int c = 4 * lane + 256 * v;
+    const bool ok = c < w;
+    if constexpr (std::is_same<T, float>::value) {
+      uv[v] = ok ? *reinterpret_cast<const f32x4*>(urow + c) : f32x4{};
+    } else {
+      const bf16x4 ub = ok ? *reinterpret_cast<const bf16x4*>(urow + c) : bf16x4{};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) uv[v][e] = (float)ub[e];
+    }
+    gv[v] = (ok && gamma) ? *reinterpret_cast<const f32x4*>(gamma + c) : f32x4{1.f, 1.f, 1.f, 1.f};
+    bv[v] = (ok && beta) ? *reinterpret_cast<const f32x4*>(beta + c) : f32x4{};
+    x[v] = f32x4{};
+  }
+  for (int sp0 = 0; sp0 < nsplit; sp0 += SB) {
+    f32x4 part[SB][NV];
+#pragma unroll
+    for (int q = 0; q < SB; ++q)
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        const int c = 4 * lane + 256 * v;
+        part[q][v] = (sp0 + q < nsplit && c < w)
+                         ? *reinterpret_cast<const f32x4*>(orow + (int64_t)(sp0 + q) * split_stride + c)
+                         : f32x4{};
+      }
+#pragma unroll
+    for (int q = 0; q < SB; ++q)  // in split order
+#pragma unroll
+      for (int v = 0; v < NV; ++v)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[v][e] += part[q][v][e];
+  }
+  float sum = 0.f;
+#pragma unroll
+  for (int v = 0; v < NV; ++v)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sum += x[v][e];
+  const float mean = wave_sum(sum) / (float)w;
+  float sq = 0.f;
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const bool ok = 4 * lane + 256 * v < w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float d = ok ? x[v][e] - mean : 0.f;
+      sq = fmaf(d, d, sq);
+    }
+  }
+  const float rstd = rsqrtf(wave_sum(sq) / (float)w + eps);
+  T* dst = out + row * ld_out;
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const int c = 4 * lane + 256 * v;
+    if (c >= w) continue;
+    float y[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) y[e] = ((x[v][e] - mean) * rstd * gv[v][e] + bv[v][e]) * uv[v][e];
+    if constexpr (std::is_same<T, float>::value) {
+      *reinterpret_cast<f32x4*>(dst + c) = f32x4{y[0], y[1], y[2], y[3]};
+    } else {
+      bf16x4 ob;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ob[e] = (bf16)y[e];
+      *reinterpret_cast<bf16x4*>(dst + c) = ob;
+    }
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void ln_gate_loop_kernel(const float* __restrict__ o, int64_t ld_o,
                                                            int nsplit, int64_t split_stride,
@@ -118,6 +208,23 @@ static hipError_t ln_dispatch(const float* o, int64_t ld_o, int nsplit, int64_t 
   const T* uu = (const T*)u;
   T* oo = (T*)out;
   const int npl = (w + 63) / 64;
+  // 16-byte fp32 rows, 8- (bf16) or 16-byte (fp32) gate and output rows
+  auto al = [](const void* p, unsigned b) { return ((uintptr_t)p & (b - 1)) == 0; };
+  const unsigned ub = (unsigned)(4 * sizeof(T));
+  const bool vec = w % 4 == 0 && w <= 1024 && ld_o % 4 == 0 && split_stride % 4 == 0 &&
+                   ld_u % 4 == 0 && ld_out % 4 == 0 && al(o, 16) && al(u, ub) && al(out, ub) &&
+                   (!gamma || al(gamma, 16)) && (!beta || al(beta, 16));
+  if (vec) {
+    const int nv = (w + 255) / 256;
+#define HSTU_LNV_CASE(N)                                                                         \
+    if (nv <= N) {                                                                               \
+      hipLaunchKernelGGL((ln_gate_vec_kernel<T, N>), grid, block, 0, s, o, ld_o, nsplit,         \
+                         split_stride, uu, ld_u, gamma, beta, eps, oo, ld_out, rows, w);         \
+      return hipGetLastError();                                                                  \
+    }
+    HSTU_LNV_CASE(1) HSTU_LNV_CASE(2) HSTU_LNV_CASE(4)
+#undef HSTU_LNV_CASE
+  }
 #define HSTU_LN_CASE(N)                                                                          \
   if (npl <= N) {                                                                                \
     hipLaunchKernelGGL((ln_gate_reg_kernel<T, N>), grid, block, 0, s, o, ld_o, nsplit,           \
