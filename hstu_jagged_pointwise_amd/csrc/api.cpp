@@ -811,12 +811,12 @@ hstu_status weight_grad(const void* A, const void* W, int64_t M, int N, int64_t 
                         int64_t ks, bool bf, float* wpart, float* out, hipStream_t s) {
   if (splits <= 1) {
     HSTU_TRY(launch_gemm_ex(A, K, W, K, nullptr, nullptr, 0, out, N, M, N, (int)K, 0, bf, 1, 1, K, 0,
-                            s),
+                            nullptr, s),
              "weight gradient");
     return HSTU_OK;
   }
   HSTU_TRY(launch_gemm_ex(A, K, W, K, nullptr, nullptr, 0, wpart, N, M, N, (int)K, 0, bf, 1, splits,
-                          ks, M * N, s),
+                          ks, M * N, nullptr, s),
            "weight gradient");
   HSTU_TRY(launch_sum_rows(wpart, M * N, splits, M * N, out, s), "split-K sum");
   return HSTU_OK;
@@ -849,10 +849,11 @@ hstu_status layer_bwd_once(const hstu_layer_desc* d, const LayerBwdPlan& p, cons
   const hstu_layer_grads none{};
   if (!g) g = &none;
   // forward pieces: z1, SiLU(z1), attention output, gate
+  // (bf16: the GEMM writes SiLU(z1) too)
   HSTU_TRY(launch_gemm_ex(xl, dm, w.w1, dm, w.b1, nullptr, 0, b.z1, F1, T, (int)F1, dm, 0, bf, 1, 1,
-                          dm, 0, s),
+                          dm, 0, bf ? b.uvqk : nullptr, s),
            "f1 pre-activation");
-  HSTU_TRY(launch_silu_act(b.z1, F1, b.uvqk, F1, T, (int)F1, bf, s), "f1 activation");
+  if (!bf) HSTU_TRY(launch_silu_act(b.z1, F1, b.uvqk, F1, T, (int)F1, bf, s), "f1 activation");
   const UVQK vw = split_view(b.uvqk, a);
   AttnArgs aa = base_args(&a);
   aa.q = vw.q;
@@ -876,7 +877,7 @@ hstu_status layer_bwd_once(const hstu_layer_desc* d, const LayerBwdPlan& p, cons
   // f2: dG = dY W2, dW2 = dY^T G, db2 = column sums of dY
   HSTU_TRY(launch_transpose(w.w2, hv, b.w2t, dm, dm, dm, hv, bf, s), "transpose");
   HSTU_TRY(launch_gemm_ex(dY, dm, b.w2t, dm, nullptr, nullptr, 0, b.dg, hv, T, hv, dm, 0, bf, 0, 1,
-                          dm, 0, s),
+                          dm, 0, nullptr, s),
            "dG");
   hstu_status st;
   if (g->dw2) {
@@ -944,7 +945,7 @@ hstu_status layer_bwd_once(const hstu_layer_desc* d, const LayerBwdPlan& p, cons
   if (dX) {
     HSTU_TRY(launch_transpose(w.w1, dm, b.w1t, F1, F1, F1, dm, bf, s), "transpose");
     HSTU_TRY(launch_gemm_ex(b.dact, F1, b.w1t, F1, nullptr, d->residual ? dY : nullptr, dm, dX, dm,
-                            T, dm, (int)F1, 0, bf, 0, 1, F1, 0, s),
+                            T, dm, (int)F1, 0, bf, 0, 1, F1, 0, nullptr, s),
              "dX");
   }
   return HSTU_OK;

@@ -70,7 +70,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const bf16* __restric
                                                          OutT* __restrict__ C, int64_t ldc, int64_t M,
                                                          int N, int K, int silu, int tiles_n,
                                                          int tiles_total, int64_t ksplit,
-                                                         int64_t c_split) {
+                                                         int64_t c_split, bf16* __restrict__ act) {
   using G = GemmShape<BM, BN>;
   constexpr int GBK = G::GBK;
   constexpr int FM = G::FM, FN = G::FN, PERW = G::PERW, STAGE = G::STAGE;
@@ -244,6 +244,12 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const bf16* __restric
     if constexpr (std::is_same<OutT, float>::value) {
       *reinterpret_cast<f32x4*>(&C[m * ldc + n]) = f32x4{y[0], y[1], y[2], y[3]};
       *reinterpret_cast<f32x4*>(&C[m * ldc + n + 4]) = f32x4{y[4], y[5], y[6], y[7]};
+      if (act) {  // SiLU of the fp32 result too, in bf16 (the f1 activation of a recompute)
+        bf16x8 o;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) o[q] = (bf16)silu_fast(y[q]);
+        *reinterpret_cast<bf16x8*>(&act[m * ldc + n]) = o;
+      }
     } else {
       bf16x8 o;
 #pragma unroll
@@ -305,8 +311,9 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 hipError_t launch_gemm_ex(const void* A, int64_t lda, const void* W, int64_t ldw, const float* bias,
                           const void* R, int64_t ldr, void* C, int64_t ldc, int64_t M, int N, int K,
                           int silu, int bf16flag, int out_f32, int splits, int64_t ksplit,
-                          int64_t c_split, hipStream_t s) {
+                          int64_t c_split, void* act, hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
+  if (act && (!bf16flag || !out_f32 || splits > 1 || silu)) return hipErrorInvalidValue;
   if (bf16flag) {
     // the DMA and the epilogue move 16-byte rows segments
     if (N % 8 != 0 || K % 8 != 0 || lda % 8 != 0 || ldw % 8 != 0 || ldc % 8 != 0 ||
@@ -326,7 +333,7 @@ hipError_t launch_gemm_ex(const void* A, int64_t lda, const void* W, int64_t ldw
       const int tn = (N + T - 1) / T, tm = (int)((M + T - 1) / T);
       hipLaunchKernelGGL((gemm_bf16_kernel<T, T, O>), dim3(tn * tm, splits), dim3(256), 0, s,
                          (const bf16*)A, lda, (const bf16*)W, ldw, bias, (const bf16*)R, ldr, (O*)C,
-                         ldc, M, N, K, silu, tn, tn * tm, ksplit, c_split);
+                         ldc, M, N, K, silu, tn, tn * tm, ksplit, c_split, (bf16*)act);
     };
     using I128 = std::integral_constant<int, 128>;
     using I64 = std::integral_constant<int, 64>;
@@ -351,7 +358,7 @@ hipError_t launch_gemm(const void* A, int64_t lda, const void* W, int64_t ldw, c
                        const void* R, int64_t ldr, void* C, int64_t ldc, int64_t M, int N, int K,
                        int silu, int bf16flag, hipStream_t s) {
   return launch_gemm_ex(A, lda, W, ldw, bias, R, ldr, C, ldc, M, N, K, silu, bf16flag, 0, 1, K, 0,
-                        s);
+                        nullptr, s);
 }
 
 }  // namespace hstu

@@ -125,12 +125,13 @@ hipError_t launch_gemm(const void* A, int64_t lda, const void* W, int64_t ldw,
 
 // launch_gemm with an fp32 output (bf16 inputs; fp32 inputs always write fp32) and
 // split-K: grid dimension y = splits, split y covers K range [y*ksplit, (y+1)*ksplit)
-// (ksplit a multiple of 32) and writes C + y*c_split; splits > 1 takes no bias,
-// residual or SiLU.
+// (ksplit a multiple of 64) and writes C + y*c_split; splits > 1 takes no bias,
+// residual or SiLU. act (bf16 inputs, fp32 output, one split, no SiLU, else NULL) also
+// receives SiLU(C) in bf16, same leading dimension, rounded as launch_silu_act rounds.
 hipError_t launch_gemm_ex(const void* A, int64_t lda, const void* W, int64_t ldw, const float* bias,
                           const void* R, int64_t ldr, void* C, int64_t ldc, int64_t M, int N, int K,
                           int silu, int use_bf16, int out_f32, int splits, int64_t ksplit,
-                          int64_t c_split, hipStream_t s);
+                          int64_t c_split, void* act, hipStream_t s);
 
 // logit[r] = sum_c y[r, c] * w[c] (fp32 accumulate).
 hipError_t launch_rowdot(const void* y, int64_t ld_y, const float* w, float* logit, int64_t rows,

@@ -195,6 +195,29 @@ __global__ __launch_bounds__(256) void silu_grad_kernel(const float* __restrict_
   d[r * ld_d + c] = from_f32<T>(to_f32<T>(d[r * ld_d + c]) * dsl);
 }
 
+// The same for bf16 rows of 8-column groups (C and both leading dimensions multiples
+// of 8, 16-byte aligned rows): one thread per group, 16-byte loads and stores.
+__global__ __launch_bounds__(256) void silu_grad_vec_kernel(const float* __restrict__ z,
+                                                            int64_t ld_z, bf16* __restrict__ d,
+                                                            int64_t ld_d, int64_t R, int C) {
+  const int G = C / 8;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= R * G) return;
+  const int64_t r = idx / G;
+  const int c = 8 * (int)(idx % G);
+  const f32x4 z0 = *reinterpret_cast<const f32x4*>(z + r * ld_z + c);
+  const f32x4 z1 = *reinterpret_cast<const f32x4*>(z + r * ld_z + c + 4);
+  bf16x8 v = *reinterpret_cast<const bf16x8*>(d + r * ld_d + c);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float x = e < 4 ? z0[e] : z1[e - 4];
+    const float sg = 1.0f / (1.0f + expf(-x));
+    const float dsl = sg * (1.0f + x * (1.0f - sg));
+    v[e] = (bf16)((float)v[e] * dsl);
+  }
+  *reinterpret_cast<bf16x8*>(d + r * ld_d + c) = v;
+}
+
 hipError_t launch_silu_act(const float* z, int64_t ld_z, void* act, int64_t ld_a, int64_t R, int C,
                            int use_bf16, hipStream_t s) {
   const int64_t n = R * C;
@@ -213,7 +236,12 @@ hipError_t launch_silu_grad(const float* z, int64_t ld_z, void* d, int64_t ld_d,
   const int64_t n = R * C;
   if (n <= 0) return hipSuccess;
   const dim3 grid((unsigned)((n + 255) / 256));
-  if (use_bf16)
+  const bool vec = use_bf16 && C % 8 == 0 && ld_z % 8 == 0 && ld_d % 8 == 0 &&
+                   ((uintptr_t)z & 15) == 0 && ((uintptr_t)d & 15) == 0;
+  if (vec)
+    hipLaunchKernelGGL(silu_grad_vec_kernel, dim3((unsigned)((n / 8 + 255) / 256)), dim3(256), 0, s,
+                       z, ld_z, (bf16*)d, ld_d, R, C);
+  else if (use_bf16)
     hipLaunchKernelGGL(silu_grad_kernel<bf16>, grid, dim3(256), 0, s, z, ld_z, (bf16*)d, ld_d, R, C);
   else
     hipLaunchKernelGGL(silu_grad_kernel<float>, grid, dim3(256), 0, s, z, ld_z, (float*)d, ld_d, R,
