@@ -765,8 +765,9 @@ void carve_layer_bwd(Carver& c, const hstu_layer_desc* d, const LayerBwdPlan& p,
   b->d_o = c.take((size_t)T * hv * es);
   b->dact = c.take((size_t)T * F1 * es);
   for (int i = 0; i < 2; ++i) b->dyb[i] = c.take(d->num_layers > 1 ? (size_t)T * dm * es : 0);
-  b->ta = c.take((size_t)std::max(dm, F1) * p.Tp * es);
-  b->tb = c.take((size_t)std::max(hv, dm) * p.Tp * es);
+  // transposed activations: only the fp32 weight gradients use them (bf16 reads rows)
+  b->ta = c.take(bf ? 0 : (size_t)std::max(dm, F1) * p.Tp * es);
+  b->tb = c.take(bf ? 0 : (size_t)std::max(hv, dm) * p.Tp * es);
   b->w1t = c.take((size_t)dm * F1 * es);
   b->w2t = c.take((size_t)hv * dm * es);
   const int64_t wp = std::max<int64_t>(p.split1 > 1 ? p.split1 * F1 * dm : 0,
@@ -795,8 +796,8 @@ hstu_status plan_layer_bwd(const hstu_layer_desc* d, const int64_t* off_host, La
   const int64_t T = p->j.total, F1 = 2LL * a.num_heads * (a.d_v + a.d_qk);
   const int64_t hv = (int64_t)a.num_heads * a.d_v, dm = d->d_model;
   p->Tp = (T + 31) / 32 * 32;
-  split_k(F1, dm, p->Tp, bf, &p->split1, &p->ks1);
-  split_k(dm, hv, p->Tp, bf, &p->split2, &p->ks2);
+  split_k(F1, dm, bf ? T : p->Tp, bf, &p->split1, &p->ks1);
+  split_k(dm, hv, bf ? T : p->Tp, bf, &p->split2, &p->ks2);
   p->ln_blocks = ln_gate_bwd_blocks(T);
   p->bias_ok = (int64_t)a.num_pos_buckets + a.num_time_buckets <= kMaxBiasBins;
   Carver c{nullptr};
@@ -807,6 +808,22 @@ hstu_status plan_layer_bwd(const hstu_layer_desc* d, const int64_t* off_host, La
 }
 
 // dW [M, N] (fp32) = A [M, K] W [N, K]^T, both operands transposed activations.
+// dW[M, N] = sum over the T rows of A[t, m] B[t, n] (bf16 row-major activations),
+// split over rows into fp32 partials added in a fixed order when splits > 1
+hstu_status weight_grad_tn(const void* A, int64_t lda, const void* B, int64_t ldb, int64_t M,
+                           int N, int64_t T, int splits, int64_t ks, float* wpart, float* out,
+                           hipStream_t s) {
+  if (splits <= 1) {
+    HSTU_TRY(launch_gemm_tn(A, lda, B, ldb, out, N, (int)M, N, T, 1, T, 0, s), "weight gradient");
+    return HSTU_OK;
+  }
+  HSTU_TRY(launch_gemm_tn(A, lda, B, ldb, wpart, N, (int)M, N, T, splits, ks, M * N, s),
+           "weight gradient");
+  HSTU_TRY(launch_sum_rows(wpart, M * N, splits, M * N, out, s), "split-K sum");
+  return HSTU_OK;
+}
+
+// The same from transposed copies (fp32: A [M, K] and W [N, K], K contiguous).
 hstu_status weight_grad(const void* A, const void* W, int64_t M, int N, int64_t K, int splits,
                         int64_t ks, bool bf, float* wpart, float* out, hipStream_t s) {
   if (splits <= 1) {
@@ -880,7 +897,10 @@ hstu_status layer_bwd_once(const hstu_layer_desc* d, const LayerBwdPlan& p, cons
                           dm, 0, nullptr, s),
            "dG");
   hstu_status st;
-  if (g->dw2) {
+  if (g->dw2 && bf) {
+    if ((st = weight_grad_tn(dY, dm, b.g, hv, dm, hv, T, p.split2, p.ks2, b.wpart, g->dw2, s)))
+      return st;
+  } else if (g->dw2) {
     HSTU_TRY(launch_transpose(dY, dm, b.ta, p.Tp, T, p.Tp, dm, bf, s), "transpose");
     HSTU_TRY(launch_transpose(b.g, hv, b.tb, p.Tp, T, p.Tp, hv, bf, s), "transpose");
     if ((st = weight_grad(b.ta, b.tb, dm, hv, p.Tp, p.split2, p.ks2, bf, b.wpart, g->dw2, s)))
@@ -936,7 +956,10 @@ hstu_status layer_bwd_once(const hstu_layer_desc* d, const LayerBwdPlan& p, cons
   // f1: dz1 = d[U|V|Q|K] SiLU'(z1), db1, dW1 = dz1^T X, dX = dz1 W1 (+ dY)
   HSTU_TRY(launch_silu_grad(b.z1, F1, b.dact, F1, T, (int)F1, bf, s), "SiLU backward");
   HSTU_TRY(launch_colsum(b.dact, F1, T, (int)F1, bf, b.cpart, g->db1, s), "db1");
-  if (g->dw1) {
+  if (g->dw1 && bf) {
+    if ((st = weight_grad_tn(b.dact, F1, xl, dm, F1, dm, T, p.split1, p.ks1, b.wpart, g->dw1, s)))
+      return st;
+  } else if (g->dw1) {
     HSTU_TRY(launch_transpose(b.dact, F1, b.ta, p.Tp, T, p.Tp, (int)F1, bf, s), "transpose");
     HSTU_TRY(launch_transpose(xl, dm, b.tb, p.Tp, T, p.Tp, dm, bf, s), "transpose");
     if ((st = weight_grad(b.ta, b.tb, F1, dm, p.Tp, p.split1, p.ks1, bf, b.wpart, g->dw1, s)))

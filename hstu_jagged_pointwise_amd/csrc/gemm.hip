@@ -18,6 +18,7 @@
 // take a plain vector-ALU tiled kernel.
 #include "common.h"
 #include "kernels.h"
+#include "mfma_tiles.h"
 
 #include <type_traits>
 
@@ -259,6 +260,184 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const bf16* __restric
   }
 }
 
+// TN form for weight gradients: C[M,N] = sum_k A[k,m] B[k,n] with A [K, lda] and
+// B [K, ldb] row-major (the contraction runs over rows, e.g. tokens), fp32 out. A stage
+// holds GBK rows of A (BM wide) then GBK rows of B (BN wide), each as stored, rows
+// padded by 8; the MFMA fragments are read transposed (ds_read_b64_tr_b16), so no
+// transposed copy of either operand is made. Both operands take the same contraction
+// order within a 16-row step, so their products pair up. Columns past M or N repeat
+// the last 8-column chunk; rows past K are zeroed in LDS.
+template <int BM, int BN>
+struct GemmTnShape {
+  static constexpr int GBK = stage_k(BM);
+  static constexpr int SPA = BM / 8 + 1, SPB = BN / 8 + 1;  // 16-byte slots per padded row
+  static constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 32, FN = WN / 32;
+  static constexpr int A_SLOTS = GBK * SPA, SLOTS = GBK * (SPA + SPB);
+  static constexpr int INSTR = (SLOTS + 63) / 64;
+  static constexpr int PERW = (INSTR + 3) / 4;
+  static constexpr int STAGE = 4 * PERW * 512;  // bf16 elements per stage (incl. junk)
+  static constexpr int BOFF = GBK * (BM + 8);    // B rows start here within a stage
+};
+
+template <int BM, int BN>
+__global__ __launch_bounds__(256, 2) void gemm_tn_kernel(const bf16* __restrict__ A, int64_t lda,
+                                                       const bf16* __restrict__ B, int64_t ldb,
+                                                       float* __restrict__ C, int64_t ldc, int M,
+                                                       int N, int64_t K, int tiles_n,
+                                                       int tiles_total, int64_t ksplit,
+                                                       int64_t c_split) {
+  using G = GemmTnShape<BM, BN>;
+  constexpr int GBK = G::GBK, FM = G::FM, FN = G::FN, PERW = G::PERW, STAGE = G::STAGE;
+  __shared__ __attribute__((aligned(16))) bf16 S0[STAGE];
+  __shared__ __attribute__((aligned(16))) bf16 S1[STAGE];
+  __shared__ __attribute__((aligned(16))) bf16 S2[STAGE];
+  __shared__ __attribute__((aligned(16))) bf16 S3[STAGE];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const int l32 = lane & 31, hl = lane >> 5;
+  const int wm = w >> 1, wn = w & 1;
+  int tile;  // XCD-aware order, as in the NT kernel
+  {
+    const int b = blockIdx.x, x = b & 7, j = b >> 3;
+    const int per = tiles_total >> 3, rem = tiles_total & 7;
+    tile = (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + j;
+  }
+  const int m0 = (tile / tiles_n) * BM;
+  const int n0 = (tile % tiles_n) * BN;
+  {  // split-K: blockIdx.y takes rows [y * ksplit, (y + 1) * ksplit) into its own C slice
+    const int64_t kofs = (int64_t)blockIdx.y * ksplit;
+    A += kofs * lda;
+    B += kofs * ldb;
+    C += (int64_t)blockIdx.y * c_split;
+    K = K - kofs < ksplit ? K - kofs : ksplit;
+  }
+  // per-lane DMA source of each of this wavefront's instructions: matrix, row within the
+  // stage, byte column (junk slots of the padded last instruction fetch A row 0, chunk 0)
+  int srow[PERW];
+  uint32_t scol[PERW];
+  bool isA[PERW];
+#pragma unroll
+  for (int j = 0; j < PERW; ++j) {
+    const int i = wu + 4 * j;
+    const int slot = 64 * i + lane;
+    if (i >= G::INSTR || slot >= G::SLOTS) {
+      isA[j] = true;
+      srow[j] = 0;
+      scol[j] = 0;
+    } else if (slot < G::A_SLOTS) {
+      isA[j] = true;
+      srow[j] = slot / G::SPA;
+      const int pc = slot % G::SPA, c = pc < G::SPA - 1 ? pc : 0;
+      scol[j] = (uint32_t)(2 * (min(m0 + 8 * c, M - 8) - m0));
+    } else {
+      const int sb = slot - G::A_SLOTS;
+      isA[j] = false;
+      srow[j] = sb / G::SPB;
+      const int pc = sb % G::SPB, c = pc < G::SPB - 1 ? pc : 0;
+      scol[j] = (uint32_t)(2 * (min(n0 + 8 * c, N - 8) - n0));
+    }
+  }
+  const char* abase = (const char*)(A + m0);
+  const char* bbase = (const char*)(B + n0);
+  const int nks = (int)((K + GBK - 1) / GBK);
+  auto issue = [&](auto bufc, int ks) {
+    constexpr int buf = decltype(bufc)::value;
+    bf16* D = buf == 0 ? S0 : buf == 1 ? S1 : buf == 2 ? S2 : S3;
+#pragma unroll
+    for (int j = 0; j < PERW; ++j) {
+      const int i = wu + 4 * j;
+      const int64_t r = min((int64_t)ks * GBK + srow[j], K - 1);  // rows past K: zeroed later
+      const char* src = isA[j] ? abase + r * lda * 2 + scol[j] : bbase + r * ldb * 2 + scol[j];
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                       (__attribute__((address_space(3))) void*)(&D[512 * i]), 16,
+                                       0, 0);
+    }
+  };
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  auto compute = [&](auto bufc, int ks) {
+    constexpr int buf = decltype(bufc)::value;
+    bf16* D = buf == 0 ? S0 : buf == 1 ? S1 : buf == 2 ? S2 : S3;
+    if ((int64_t)(ks + 1) * GBK > K) {  // rows past K (uniform branch, last stage only)
+      lds_barrier();
+      const int kv = (int)(K - (int64_t)ks * GBK);
+      for (int e = tid; e < (GBK - kv) * (G::SPA + G::SPB - 2); e += 256) {
+        const int row = kv + e / (G::SPA + G::SPB - 2), c = e % (G::SPA + G::SPB - 2);
+        const int off = c < G::SPA - 1 ? row * (BM + 8) + 8 * c
+                                       : G::BOFF + row * (BN + 8) + 8 * (c - (G::SPA - 1));
+        *reinterpret_cast<u32x4*>(&D[off]) = u32x4{0u, 0u, 0u, 0u};
+      }
+      lds_barrier();
+    }
+#pragma unroll
+    for (int kk = 0; kk < GBK / 16; ++kk) {
+      bf16x8 af[FM], bfr[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) af[i] = mt::trfrag<BM>(D, 16 * kk, wm * FM + i, lane);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) bfr[j] = mt::trfrag<BN>(D + G::BOFF, 16 * kk, wn * FN + j, lane);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+  };
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  using B2 = std::integral_constant<int, 2>;
+  using B3 = std::integral_constant<int, 3>;
+  if (0 < nks) issue(B0{}, 0);
+  if (1 < nks) issue(B1{}, 1);
+  if (2 < nks) issue(B2{}, 2);
+  auto step = [&](auto bufc, int ks) {
+    constexpr int buf = decltype(bufc)::value;
+    using BI = std::integral_constant<int, (buf + NST - 1) % NST>;
+    if (ks + 2 < nks) wait_vmcnt<2 * PERW>();
+    else if (ks + 1 < nks) wait_vmcnt<PERW>();
+    else wait_vmcnt<0>();
+    lds_barrier();
+    if (ks + NST - 1 < nks) issue(BI{}, ks + NST - 1);
+    compute(bufc, ks);
+  };
+  for (int ks = 0; ks < nks; ks += NST) {
+    step(B0{}, ks);
+    if (ks + 1 < nks) step(B1{}, ks + 1);
+    if (ks + 2 < nks) step(B2{}, ks + 2);
+    if (ks + 3 < nks) step(B3{}, ks + 3);
+  }
+  __syncthreads();  // every wavefront is done with the ring; reuse it for the epilogue
+
+  constexpr int EP = G::WN + 4;  // padded fp32 row
+  static_assert(G::WM * EP * 4 <= STAGE * 2, "epilogue tile fits one ring buffer");
+  float* E = (float*)(w == 0 ? S0 : w == 1 ? S1 : w == 2 ? S2 : S3);
+#pragma unroll
+  for (int j = 0; j < FN; ++j)
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        E[(32 * i + 8 * (r >> 2) + 4 * hl + (r & 3)) * EP + 32 * j + l32] = acc[i][j][r];
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): own LDS writes done (same wavefront reads)
+  constexpr int SEGS = G::WM * (G::WN / 8);
+#pragma unroll
+  for (int sg = lane; sg < SEGS; sg += 64) {
+    const int ml = sg / (G::WN / 8), cs = sg % (G::WN / 8);
+    const int m = m0 + wm * G::WM + ml;
+    const int n = n0 + wn * G::WN + 8 * cs;
+    if (m >= M || n >= N) continue;
+    const f32x4 lo = *reinterpret_cast<const f32x4*>(&E[ml * EP + 8 * cs]);
+    const f32x4 hi = *reinterpret_cast<const f32x4*>(&E[ml * EP + 8 * cs + 4]);
+    *reinterpret_cast<f32x4*>(&C[(int64_t)m * ldc + n]) = lo;
+    *reinterpret_cast<f32x4*>(&C[(int64_t)m * ldc + n + 4]) = hi;
+  }
+}
+
 // fp32: 64x64 tile, 256 threads with 4x4 outputs each, K staged 16 at a time
 __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__ A, int64_t lda,
                                                        const float* __restrict__ W, int64_t ldw,
@@ -351,6 +530,32 @@ hipError_t launch_gemm_ex(const void* A, int64_t lda, const void* W, int64_t ldw
                        (const float*)W, ldw, bias, (const float*)R, ldr, (float*)C, ldc, M, N, K,
                        silu);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_tn(const void* A, int64_t lda, const void* B, int64_t ldb, float* C,
+                          int64_t ldc, int M, int N, int64_t K, int splits, int64_t ksplit,
+                          int64_t c_split, hipStream_t s) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  if (M % 8 != 0 || N % 8 != 0 || lda % 8 != 0 || ldb % 8 != 0 || ldc % 4 != 0 || K <= 0)
+    return hipErrorInvalidValue;
+  if (splits < 1) splits = 1;
+  if (splits == 1) ksplit = K;
+  const int64_t big = (int64_t)((N + 127) / 128) * ((M + 127) / 128) * splits;
+  const int gbk = stage_k(big >= 256 ? 128 : 64);
+  if (splits > 1 && (ksplit % gbk != 0 || (int64_t)(splits - 1) * ksplit >= K))
+    return hipErrorInvalidValue;
+  auto go = [&](auto bm) {
+    constexpr int T = decltype(bm)::value;
+    const int tn = (N + T - 1) / T, tm = (M + T - 1) / T;
+    hipLaunchKernelGGL((gemm_tn_kernel<T, T>), dim3(tn * tm, splits), dim3(256), 0, s,
+                       (const bf16*)A, lda, (const bf16*)B, ldb, C, ldc, M, N, K, tn, tn * tm,
+                       ksplit, c_split);
+  };
+  if (big >= 256)
+    go(std::integral_constant<int, 128>{});
+  else
+    go(std::integral_constant<int, 64>{});
   return hipGetLastError();
 }
 

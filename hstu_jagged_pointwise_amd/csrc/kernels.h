@@ -133,6 +133,14 @@ hipError_t launch_gemm_ex(const void* A, int64_t lda, const void* W, int64_t ldw
                           int silu, int use_bf16, int out_f32, int splits, int64_t ksplit,
                           int64_t c_split, void* act, hipStream_t s);
 
+// C[M,N] = sum_k A[k,m] B[k,n] (bf16 A [K, lda] and B [K, ldb] row-major, fp32 C): the
+// weight-gradient form, contraction over rows. M, N and both leading dimensions multiples
+// of 8. Split-K as launch_gemm_ex over rows: split y covers rows [y*ksplit, (y+1)*ksplit)
+// (ksplit a multiple of 64) and writes C + y*c_split.
+hipError_t launch_gemm_tn(const void* A, int64_t lda, const void* B, int64_t ldb, float* C,
+                          int64_t ldc, int M, int N, int64_t K, int splits, int64_t ksplit,
+                          int64_t c_split, hipStream_t s);
+
 // logit[r] = sum_c y[r, c] * w[c] (fp32 accumulate).
 hipError_t launch_rowdot(const void* y, int64_t ld_y, const float* w, float* logit, int64_t rows,
                          int d, int use_bf16, hipStream_t s);
