@@ -176,6 +176,13 @@ hstu_status hstu_layer_fwd(const hstu_layer_desc* desc, const int64_t* seq_offse
  * hist_ts and cand_ts are both NULL or both set.
  * w_head [d_model] fp32 or NULL; cand_logit [C_tot] fp32 = cand_out . w_head,
  * or NULL.
+ * Streams: with more than one microbatch, the microbatches run on four streams
+ * the library creates per device at first use (default priority, kept until
+ * the process ends). They are forked from `stream` after the work already
+ * queued on it and joined back into it before the call returns, so the call
+ * behaves as if every launch were on `stream`: later work on `stream` sees all
+ * of its results. Results equal those of a serial run bit for bit. Calls from
+ * several host threads on one device are serialized while they queue work.
  * ---------------------------------------------------------------------- */
 hstu_status mfalcon_workspace_size(const mfalcon_desc* desc, const int64_t* hist_offsets_host,
                                    const int64_t* cand_offsets_host, size_t* bytes);
