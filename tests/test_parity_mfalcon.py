@@ -197,3 +197,30 @@ def test_cached_history_equals_one_shot(dt):
                                        cand_offsets_host=x.cand_offsets, **kw)
     torch.cuda.synchronize()
     assert torch.equal(got3, ref)
+
+
+def test_work_queued_after_the_call_sees_every_microbatch():
+    """The microbatches run on the library's own streams, forked from and joined back into
+    the caller's stream. Work queued on the caller's stream right after the call, with no
+    synchronisation in between, must read the final outputs of every microbatch, the last
+    ones included (16,384 candidates in 16 microbatches)."""
+    from hstu_jagged_pointwise_amd import ops
+    x = synth.workload_mfalcon()
+    announce("mfalcon join: work queued after the call")
+    ref_out, ref_logit = mf_on_gpu(x)
+    dt = act_dtype(x.dtype)
+    args = (dev(x.hist_offsets), dev(x.hist_ts), dev(x.hist_x, dt), dev(x.cand_offsets),
+            dev(x.cand_ts), dev(x.cand_x, dt), layer_weights_on_gpu(x.layers, x.dtype))
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        for rep in range(3):
+            out, logit = ops.mfalcon_score(*args, num_heads=x.num_heads, d_qk=x.d_qk, d_v=x.d_v,
+                                           max_seq_len=x.max_seq_len, microbatch=x.microbatch,
+                                           w_head=dev(x.w_head), ln_eps=x.eps,
+                                           residual=x.residual, hist_offsets_host=x.hist_offsets,
+                                           cand_offsets_host=x.cand_offsets, stream=s)
+            out_copy, logit_copy = out.clone(), logit.clone()  # queued on s, no sync
+            torch.cuda.synchronize()
+            assert torch.equal(out_copy, ref_out), f"repeat {rep}: outputs"
+            assert torch.equal(logit_copy, ref_logit), f"repeat {rep}: logits"
