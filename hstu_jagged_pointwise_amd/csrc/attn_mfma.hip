@@ -44,7 +44,10 @@
 //
 // Candidate mode (M-FALCON): the queries are one user's candidates, all at
 // position n_h. The keys are that user's history, all visible. Each
-// candidate's own key and value are added in the epilogue.
+// candidate's own key and value are added in the epilogue. When a wavefront's
+// candidates share one timestamp, a pair's whole bias depends on its key only;
+// the bias step then multiplies a per-key bias by ones, and every unmasked block
+// takes the fast path whatever its buckets.
 #include "attn_common.h"
 
 #include <type_traits>
@@ -222,6 +225,9 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
   const int qpos = CAND ? qpos0 : qpos0 + wrow;
   const int wrow0 = qpos0 + 32 * wu;                        // the wavefront's first row
   const int wlast = qpos0 + min(32 * wu + 31, t.rows - 1);  // its last live row
+  // candidate mode: the wavefront's candidates share one timestamp (or there is no time
+  // bias), so a pair's bias depends on the key alone
+  const bool keyb_ok = CAND && (!has_time || qmin == qmax);
 
   // constant A fragment for the bias k-step, A[key][0] = A[key][1] = 1, rebuilt at
   // each use (one select and three zero moves) rather than held in registers
@@ -428,6 +434,15 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
     const bf16* Vt = buf ? Vs1 : Vs0;
     // both blocks active, unmasked, one position bucket, one time bucket
     const bool fast = (cls.f & 0x1f1fu) == 0x0505u;
+    // candidate mode with one timestamp per wavefront: both blocks live and unmasked suffice
+    const bool keyb_tile = CAND && keyb_ok && (cls.f & 0x0303u) == 0x0101u;
+    // this lane's key's whole bias (candidate mode): position n_h - j, elapsed time t_c - t_j
+    auto key_bias = [&](int kb0) {
+      const int j = kb0 + l32;
+      float b = has_pos ? rp[min(qpos0 - j, P - 1)] : 0.f;
+      if (has_time) b += rt[bucket_of(qmin - tk64[buf][j - k0], T)];
+      return b;
+    };
     constexpr int E = 16 / NKK;  // scores activated per interleaved step
     // SiLU of accumulator slots st*E .. st*E+E-1 into bf16 A fragments
     auto act_step = [&](const f32x16& x, bf16x8* pa, int st) {
@@ -437,12 +452,18 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
         pa[r >> 3][r & 7] = (bf16)silu_fast(x[r]);
       }
     };
+    // the bias k-step: a bias per query (ones on the key side), or, given keyA, a bias
+    // per key (keyA on the key side, ones on the query side)
+    auto bias_step = [&](float bias, const bf16x8* keyA) {
+      if (keyA) return __builtin_amdgcn_mfma_f32_32x32x16_bf16(*keyA, ones(), f32x16{}, 0, 0, 0);
+      return __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones(), bias_frag(bias), f32x16{}, 0, 0, 0);
+    };
     // S^T of one block, with the constant part of its bias through the bias k-step
-    auto s_chain = [&](int kb, float bias, bool with_dma) {
+    auto s_chain = [&](int kb, float bias, const bf16x8* keyA, bool with_dma) {
       bf16x8 kq[NKK];
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) kq[kk] = kfrag(Kt, kb, kk);
-      f32x16 x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones(), bias_frag(bias), f32x16{}, 0, 0, 0);
+      f32x16 x = bias_step(bias, keyA);
       if (with_dma) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
@@ -468,13 +489,22 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
     // the in-order wavefront issues one MFMA, then the independent vector work
     // that fits under it: block 0's S^T chain; block 1's S^T chain, each step
     // carrying the SiLU of 16/NKK of block 0's scores.
-    auto fast_path = [&]() {
-      const f32x16 s0 = s_chain(0, pb + c0.tlo, true);
+    //
+    // Candidate mode, when the wavefront's candidates share one timestamp: every
+    // candidate sits at position n_h, so the whole bias of a pair depends on its key
+    // alone. The bias step then carries a per-key bias (key-side fragment) times ones
+    // (query side), and any unmasked block takes this path, whatever its buckets.
+    auto fast_path = [&](bool keyb) {
+      bf16x8 kA[2];
+      if constexpr (CAND) {
+        kA[0] = bias_frag(key_bias(k0));
+        kA[1] = bias_frag(key_bias(k0 + 32));
+      }
+      const f32x16 s0 = s_chain(0, pb + c0.tlo, CAND && keyb ? &kA[0] : nullptr, true);
       bf16x8 k1[NKK];
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) k1[kk] = kfrag(Kt, 1, kk);
-      f32x16 s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones(), bias_frag(pb + c1.tlo), f32x16{},
-                                                          0, 0, 0);
+      f32x16 s1 = bias_step(pb + c1.tlo, CAND && keyb ? &kA[1] : nullptr);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
@@ -491,7 +521,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
     auto general_block = [&](int kb, const BlockClass& bc) {
       if (!bc.act()) return f32x16{};
       const int kb0 = k0 + 32 * kb;
-      f32x16 x = s_chain(kb, (bc.pos_c() ? pb : 0.f) + (bc.tmode() < 2 ? bc.tlo : 0.f), false);
+      f32x16 x = s_chain(kb, (bc.pos_c() ? pb : 0.f) + (bc.tmode() < 2 ? bc.tlo : 0.f), nullptr, false);
       // i - j = dbase - (8*(r/4) + r%4) for accumulator slot r
       const int dbase = qpos - kb0 - 4 * hl;
       if (!bc.pos_c()) {
@@ -554,8 +584,8 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
     };
 
     if (wave_live) {
-      if (fast)
-        fast_path();
+      if (fast || keyb_tile)
+        fast_path(keyb_tile);
       else
         general_path();
     } else {
