@@ -4,6 +4,8 @@ A candidate's output must not depend on the other candidates. So permuting
 candidates permutes outputs, adding one leaves the others unchanged, and the
 microbatch size does not matter. On the GPU these hold bit for bit, because
 every output row has a fixed reduction order."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -131,13 +133,15 @@ def test_mfalcon_workload_sampled_candidates():
     assert np.all(np.abs(lgn - want @ x.w_head.astype(np.float64)) <= 2e-2 * scale)
 
 
-@pytest.mark.parametrize("L", [1, 2])
-def test_split_history_multi_user(L):
+@pytest.mark.parametrize("L,shared", [(1, False), (2, False), (1, True), (2, True)])
+def test_split_history_multi_user(L, shared):
     """Histories longer than one key range (512 keys) are split across workgroups and the
     partials summed in a fixed order: parity against the oracle, and outputs bit-for-bit
-    independent of the microbatch size and of the candidate order."""
-    x = _small("bf16", L, seed=11, hist=(1300, 0, 700, 2000), cands=(37, 5, 20, 64), mb=50)
-    announce(f"mfalcon split history L={L}")
+    independent of the microbatch size and of the candidate order. With a shared request
+    time per user the per-key bias path runs (ragged tails take the masked path)."""
+    x = _small("bf16", L, seed=11, hist=(1300, 0, 700, 2000), cands=(37, 5, 20, 64), mb=50,
+               shared=shared)
+    announce(f"mfalcon split history L={L} shared_ts={shared}")
     out, lg = mf_on_gpu(x)
     want, _ = mf_oracle(x)
     want_s = mf_oracle(x, "bf16")[0]
@@ -224,3 +228,22 @@ def test_work_queued_after_the_call_sees_every_microbatch():
             torch.cuda.synchronize()
             assert torch.equal(out_copy, ref_out), f"repeat {rep}: outputs"
             assert torch.equal(logit_copy, ref_logit), f"repeat {rep}: logits"
+
+
+@pytest.mark.parametrize("variant", ["no_timestamps", "no_time_table", "no_tables"])
+def test_bias_variants(variant):
+    """Candidates without timestamps (position bias only), without a time table, and without
+    any table, on split multi-user histories, against the oracle."""
+    x = _small("bf16", 1, seed=13, shared=True, hist=(1300, 40, 600), cands=(20, 7, 33), mb=16)
+    if variant == "no_timestamps":
+        x = dataclasses.replace(x, hist_ts=None, cand_ts=None)
+    else:
+        drop = dict(rab_time=None) if variant == "no_time_table" else dict(rab_pos=None,
+                                                                            rab_time=None)
+        x = dataclasses.replace(x, layers=[dataclasses.replace(w, **drop) for w in x.layers])
+    announce(f"mfalcon bias variant {variant}")
+    out, lg = mf_on_gpu(x)
+    want, _ = mf_oracle(x)
+    want_s = mf_oracle(x, "bf16")[0]
+    check_rows(to_np(out), x, want, want_s, f"mfalcon {variant}")
+    _check_logits(lg, want_s, x, TOL["bf16"])
