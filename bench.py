@@ -57,20 +57,33 @@ def source_hash() -> str:
 
 
 def time_calls(fn, stream, steps, warmup):
-    """Per-call durations (ms) from HIP events recorded on the library's stream."""
+    """Per-call durations (ms) from HIP events recorded on the library's stream.
+
+    Python's cyclic garbage collector is run before the timed calls and paused during
+    them, as timeit does: a full collection holds the host for tens of milliseconds, and
+    one landing between a call's start event and its launches would be counted as GPU
+    time of that call."""
+    import gc
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    t0 = time.perf_counter()
-    for i in range(steps):
-        starts[i].record(stream)
-        fn()
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    gc.collect()
+    gc_was_on = gc.isenabled()
+    gc.disable()
+    try:
+        t0 = time.perf_counter()
+        for i in range(steps):
+            starts[i].record(stream)
+            fn()
+            ends[i].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    finally:
+        if gc_was_on:
+            gc.enable()
     return np.array([s.elapsed_time(e) for s, e in zip(starts, ends)]), wall
 
 
