@@ -355,7 +355,7 @@ struct MfPlan {
   size_t cand_ws = 0;         // candidate-pass workspace
 };
 
-constexpr int64_t kKeysPerSplit = 512;  // history keys per candidate-attention workgroup
+constexpr int64_t kKeysPerSplit = 1024;  // history keys per candidate-attention workgroup
 constexpr int kMaxSplits = 16;
 
 struct MfCache {

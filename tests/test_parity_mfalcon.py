@@ -135,7 +135,7 @@ def test_mfalcon_workload_sampled_candidates():
 
 @pytest.mark.parametrize("L,shared", [(1, False), (2, False), (1, True), (2, True)])
 def test_split_history_multi_user(L, shared):
-    """Histories longer than one key range (512 keys) are split across workgroups and the
+    """Histories longer than one key range (1024 keys) are split across workgroups and the
     partials summed in a fixed order: parity against the oracle, and outputs bit-for-bit
     independent of the microbatch size and of the candidate order. With a shared request
     time per user the per-key bias path runs (ragged tails take the masked path)."""
