@@ -114,6 +114,30 @@ def leg_attention(steps, warmup):
                 out=out)
 
 
+# Vector-ALU side of the attention's roofline. Every score goes through SiLU on the vector
+# ALU: in the kernel's fast path, per score, one exp2 and one reciprocal (transcendental)
+# plus a multiply, an add, a multiply and half of a two-value bf16 convert (ordinary fp32
+# ops, packed fp32 disabled). Rates from the chip's unit counts: 256 CUs x 4 SIMDs x 16
+# lanes x 2.4 GHz ordinary lane-ops/s; transcendentals at half that (measured on the
+# device: a wave64 exp2 or reciprocal takes twice the cycles of an fp32 FMA).
+VALU_PLAIN_PER_S = 256 * 4 * 16 * 2.4e9
+VALU_TRANS_PER_S = VALU_PLAIN_PER_S / 2
+SILU_OPS = {"transcendental": 2.0, "plain": 3.5}
+
+
+def valu_ceiling(attn):
+    scores = attn["pairs"] * attn["x"].num_heads
+    t_valu = scores * (SILU_OPS["plain"] / VALU_PLAIN_PER_S +
+                       SILU_OPS["transcendental"] / VALU_TRANS_PER_S)
+    valu_tf = attn["flops"] / t_valu / 1e12
+    both_tf = 1.0 / (1.0 / PEAK_BF16_TFLOPS + 1.0 / valu_tf)
+    return {"scores": int(scores), "ops_per_score": SILU_OPS,
+            "ceiling": round(valu_tf, 1), "mfma_plus_valu_ceiling": round(both_tf, 1),
+            "unit": "TFLOP/s", "frac_of_mfma_plus_valu": round(attn["tflops"] / both_tf, 4),
+            "note": "ceiling: the SiLU vector work alone at the vector-ALU rate; "
+                    "mfma_plus_valu: MFMA at peak and SiLU at that rate, not overlapped"}
+
+
 def leg_mfalcon(steps, warmup):
     import torch
     from hstu_jagged_pointwise_amd import ops, synth
@@ -139,8 +163,25 @@ def leg_mfalcon(steps, warmup):
 
     with torch.cuda.stream(stream):
         ms, wall = time_calls(call, stream, max(3, steps // 2), max(1, warmup // 2))
+    # the candidate pass alone, against a history cache built once (mfalcon_history)
+    kw = dict(num_heads=x.num_heads, d_qk=x.d_qk, d_v=x.d_v, max_seq_len=x.max_seq_len,
+              microbatch=x.microbatch, hist_offsets_host=x.hist_offsets, stream=stream)
+    with torch.cuda.stream(stream):
+        cache = ops.mfalcon_history(d["hist_offsets"], d["hist_ts"], d["hist_x"], d["layers"], **kw)
+        cws = torch.empty(max(1, ops.mfalcon_cached_workspace_size(desc, x.hist_offsets,
+                                                                   x.cand_offsets)),
+                          dtype=torch.uint8, device="cuda")
+
+        def cand_call():
+            ops.mfalcon_score_cached(cache, d["hist_offsets"], d["hist_ts"], d["cand_offsets"],
+                                     d["cand_ts"], d["cand_x"], d["layers"], w_head=d["w_head"],
+                                     out=out, logit=logit, workspace=cws,
+                                     cand_offsets_host=x.cand_offsets, **kw)
+
+        cms, _ = time_calls(cand_call, stream, max(3, steps // 2), max(1, warmup // 2))
     C = int(x.cand_offsets[-1])
     mean = float(ms.mean())
+    cmean = float(cms.mean())
     n_h = int(x.hist_offsets[-1])
     hd = x.num_heads
     attn_flops = C * (n_h + 1) * hd * 2 * (x.d_qk + x.d_v)
@@ -148,6 +189,9 @@ def leg_mfalcon(steps, warmup):
     hist_flops = n_h * 2 * x.d_model * 2 * hd * (x.d_qk + x.d_v)
     return dict(candidates=C, ms=mean, candidates_per_s=C / (mean * 1e-3),
                 tflops=(attn_flops + proj_flops + hist_flops) / (mean * 1e-3) / 1e12,
+                candidates_only=dict(ms=round(cmean, 4), candidates_per_s=C / (cmean * 1e-3),
+                                     note="mfalcon_score_cached against a history cache built "
+                                          "once by mfalcon_history"),
                 microbatch=x.microbatch, history=n_h, layers=1)
 
 
@@ -429,6 +473,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(attn["tflops"], 3),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(attn["tflops"] / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
+        "valu": valu_ceiling(attn),
     }
     line.update(result)
     if "cpu" in legs:

@@ -314,6 +314,13 @@ def mfalcon_cache_size(desc, hist_offsets_host) -> int:
     return n.value
 
 
+def mfalcon_cached_workspace_size(desc, hist_offsets_host, cand_offsets_host) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib.mfalcon_cached_workspace_size(ctypes.byref(desc), _i64p(hist_offsets_host),
+                                             _i64p(cand_offsets_host), ctypes.byref(n)))
+    return n.value
+
+
 def mfalcon_history(hist_offsets, hist_ts, hist_x, layers: Sequence[LayerWeights], *, num_heads,
                     d_qk, d_v, max_seq_len, microbatch=1, ln_eps=1e-5, residual=0, cache=None,
                     workspace=None, hist_offsets_host=None, stream=None):
