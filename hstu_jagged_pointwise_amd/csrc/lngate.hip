@@ -76,10 +76,12 @@ __global__ __launch_bounds__(256) void ln_gate_reg_kernel(const float* __restric
 }
 
 // Vector form for rows whose width is a multiple of 4 with 16-byte aligned fp32 rows: a
-// lane owns 4 adjacent columns per 256, so every load and store moves 16 (or 8) bytes.
-// The gate row, gamma and beta are requested first, then the partial rows of up to SB
-// splits at once, so that one wavefront has all of its row's traffic in flight.
-template <typename T, int NV>
+// lane owns 4 adjacent columns per 4*LPR, so every load and store moves 16 (or 8) bytes.
+// LPR lanes own a row: the whole wavefront (64), or for rows of at most 128 (64) values
+// half (a quarter) of it, so that narrow rows keep every lane busy. The gate row, gamma
+// and beta are requested first, then the partial rows of up to SB splits at once, so
+// that a row's traffic is in flight together.
+template <typename T, int NV, int LPR>
 __global__ __launch_bounds__(256) void ln_gate_vec_kernel(const float* __restrict__ o, int64_t ld_o,
                                                           int nsplit, int64_t split_stride,
                                                           const T* __restrict__ u, int64_t ld_u,
@@ -88,16 +90,22 @@ __global__ __launch_bounds__(256) void ln_gate_vec_kernel(const float* __restric
                                                           T* __restrict__ out, int64_t ld_out,
                                                           int64_t rows, int w) {
   constexpr int SB = NV <= 1 ? 16 : 16 / NV;  // splits per batch of loads
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
+  constexpr int RPW = 64 / LPR;               // rows per wavefront
+  const int lane = threadIdx.x & 63, sl = lane % LPR;
+  const int64_t row = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW + lane / LPR;
+  const bool live = row < rows;  // no early exit: the row sums shuffle across lanes
   const float* orow = o + row * ld_o;
   const T* urow = u + row * ld_u;
+  auto seg_sum = [](float v) {  // sum over the LPR lanes of this row (xor stays inside them)
+#pragma unroll
+    for (int off = LPR / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+  };
   f32x4 uv[NV], gv[NV], bv[NV], x[NV];
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
-    const int c = 4 * lane + 256 * v;
-    const bool ok = c < w;
+    const int c = 4 * sl + 4 * LPR * v;
+    const bool ok = live && c < w;
     if constexpr (std::is_same<T, float>::value) {
       uv[v] = ok ? *reinterpret_cast<const f32x4*>(urow + c) : f32x4{};
     } else {
@@ -115,8 +123,8 @@ __global__ __launch_bounds__(256) void ln_gate_vec_kernel(const float* __restric
     for (int q = 0; q < SB; ++q)
 #pragma unroll
       for (int v = 0; v < NV; ++v) {
-        const int c = 4 * lane + 256 * v;
-        part[q][v] = (sp0 + q < nsplit && c < w)
+        const int c = 4 * sl + 4 * LPR * v;
+        part[q][v] = (live && sp0 + q < nsplit && c < w)
                          ? *reinterpret_cast<const f32x4*>(orow + (int64_t)(sp0 + q) * split_stride + c)
                          : f32x4{};
       }
@@ -132,22 +140,23 @@ __global__ __launch_bounds__(256) void ln_gate_vec_kernel(const float* __restric
   for (int v = 0; v < NV; ++v)
 #pragma unroll
     for (int e = 0; e < 4; ++e) sum += x[v][e];
-  const float mean = wave_sum(sum) / (float)w;
+  const float mean = seg_sum(sum) / (float)w;
   float sq = 0.f;
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
-    const bool ok = 4 * lane + 256 * v < w;
+    const bool ok = 4 * sl + 4 * LPR * v < w;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const float d = ok ? x[v][e] - mean : 0.f;
       sq = fmaf(d, d, sq);
     }
   }
-  const float rstd = rsqrtf(wave_sum(sq) / (float)w + eps);
+  const float rstd = rsqrtf(seg_sum(sq) / (float)w + eps);
+  if (!live) return;
   T* dst = out + row * ld_out;
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
-    const int c = 4 * lane + 256 * v;
+    const int c = 4 * sl + 4 * LPR * v;
     if (c >= w) continue;
     float y[4];
 #pragma unroll
@@ -216,13 +225,17 @@ static hipError_t ln_dispatch(const float* o, int64_t ld_o, int nsplit, int64_t 
                    (!gamma || al(gamma, 16)) && (!beta || al(beta, 16));
   if (vec) {
     const int nv = (w + 255) / 256;
-#define HSTU_LNV_CASE(N)                                                                         \
-    if (nv <= N) {                                                                               \
-      hipLaunchKernelGGL((ln_gate_vec_kernel<T, N>), grid, block, 0, s, o, ld_o, nsplit,         \
+    // rows of at most 64 or 128 values: 4 or 2 rows per wavefront
+    const int lpr = w <= 64 ? 16 : w <= 128 ? 32 : 64;
+    const dim3 vgrid((unsigned)((rows + 4 * (64 / lpr) - 1) / (4 * (64 / lpr))));
+#define HSTU_LNV_CASE(N, L)                                                                      \
+    if (nv <= N && lpr == L) {                                                                   \
+      hipLaunchKernelGGL((ln_gate_vec_kernel<T, N, L>), vgrid, block, 0, s, o, ld_o, nsplit,     \
                          split_stride, uu, ld_u, gamma, beta, eps, oo, ld_out, rows, w);         \
       return hipGetLastError();                                                                  \
     }
-    HSTU_LNV_CASE(1) HSTU_LNV_CASE(2) HSTU_LNV_CASE(4)
+    HSTU_LNV_CASE(1, 16) HSTU_LNV_CASE(1, 32) HSTU_LNV_CASE(1, 64) HSTU_LNV_CASE(2, 64)
+    HSTU_LNV_CASE(4, 64)
 #undef HSTU_LNV_CASE
   }
 #define HSTU_LN_CASE(N)                                                                          \
