@@ -20,8 +20,12 @@ resident in HBM before the timed region. The same run also times:
   * the fp64 CPU oracle on a bounded sample of the attention workload.
 One JSON line goes to stdout. Progress goes to stderr.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--warm-seconds S]
                     [--only attn,softmax,mfalcon,layers,backward,sl,cpu | copy]
+
+Defaults: K = 200 timed calls of the attention (fewer for the slower legs), W = 20 warm-up
+calls, and S = 2 s of untimed near-continuous load before the first timed call, so that the
+clock has settled (the first ~100 calls of an idle device run up to 15% slower).
 """
 from __future__ import annotations
 
@@ -56,24 +60,36 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def time_calls(fn, stream, steps, warmup):
+def time_calls(fn, stream, steps, warmup, warm_s=0.0):
     """Per-call durations (ms) from HIP events recorded on the library's stream.
 
-    Python's cyclic garbage collector is run before the timed calls and paused during
-    them, as timeit does: a full collection holds the host for tens of milliseconds, and
-    one landing between a call's start event and its launches would be counted as GPU
-    time of that call."""
+    After the `warmup` calls, further untimed calls run until `warm_s` seconds have
+    passed: a device that was idle takes a second or so of load to reach its steady clock,
+    and calls timed before that measure the ramp rather than the kernel. Anything that
+    idles the device (here: the garbage collection and the event set-up) happens before the
+    warm-up, so only the synchronize separates the last warm-up call from the first timed
+    one.
+
+    Python's cyclic garbage collector is run before the warm-up and paused until the timed
+    calls are done, as timeit does: a full collection holds the host for tens of
+    milliseconds, and one landing between a call's start event and its launches would be
+    counted as GPU time of that call."""
     import gc
     import torch
-    for _ in range(warmup):
-        fn()
-    torch.cuda.synchronize()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     gc.collect()
     gc_was_on = gc.isenabled()
     gc.disable()
     try:
+        t_warm = time.perf_counter()
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        while time.perf_counter() - t_warm < warm_s:  # near-continuous load
+            for _ in range(100):
+                fn()
+            torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(steps):
             starts[i].record(stream)
@@ -87,7 +103,7 @@ def time_calls(fn, stream, steps, warmup):
     return np.array([s.elapsed_time(e) for s, e in zip(starts, ends)]), wall
 
 
-def leg_attention(steps, warmup):
+def leg_attention(steps, warmup, warm_s=0.0):
     import torch
     from hstu_jagged_pointwise_amd import ops, synth
     from hstu_jagged_pointwise_amd.device import attn_to_device
@@ -106,7 +122,7 @@ def leg_attention(steps, warmup):
                           seq_offsets_host=x.offsets, stream=stream)
 
     with torch.cuda.stream(stream):
-        ms, wall = time_calls(call, stream, steps, warmup)
+        ms, wall = time_calls(call, stream, steps, warmup, warm_s)
     pairs = int(np.sum(x.lengths * (x.lengths + 1) // 2))
     flops = pairs * x.num_heads * 2 * (x.d_qk + x.d_v)
     mean = float(ms.mean())
@@ -387,9 +403,12 @@ def cpu_baseline(x, budget_s=12.0):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=200)
     # the clocks take a few dozen calls to settle; the timed calls start after them
     ap.add_argument("--warmup", type=int, default=20)
+    # the first leg also keeps warming for this many seconds, so that an idle device has
+    # reached its steady clock before the first timed call
+    ap.add_argument("--warm-seconds", type=float, default=2.0)
     ap.add_argument("--only", default="attn,softmax,mfalcon,layers,backward,sl,cpu")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     args = ap.parse_args()
@@ -412,7 +431,7 @@ def main():
     attn = None
     if "attn" in legs:
         log("attention leg (length-8192 workload)")
-        attn = leg_attention(args.steps, args.warmup)
+        attn = leg_attention(args.steps, args.warmup, args.warm_seconds)
         log(f"attention: {attn['ms'].mean():.3f} ms/call, {attn['tflops']:.1f} TFLOP/s")
     if "mfalcon" in legs:
         log("M-FALCON leg")
@@ -468,6 +487,7 @@ def main():
                    "ms_p50": round(float(np.median(attn["ms"])), 4),
                    "ms_p90": round(float(np.quantile(attn["ms"], 0.9)), 4),
                    "wall_s": round(attn["wall"], 4),
+                   "warm_seconds": args.warm_seconds,
                    "note": "per-call HIP events on the library's stream; a call is the tile "
                            "planner plus the attention kernel"},
         "roofline": {"bound": "mfma", "achieved": round(attn["tflops"], 3),
