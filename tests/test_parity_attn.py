@@ -83,6 +83,16 @@ def test_wide_and_unsorted_timestamps(dt):
     assert_rows_close(g, _oracle(x, ts=wide), TOL[dt], "wide timestamps")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_largest_tables_on_mfma_kernel(d):
+    """P = 1024, the largest position table the MFMA kernel keeps in LDS, and T = 64 time
+    buckets, with a sequence long enough (1,300) to reach position bucket 1023."""
+    x = synth.make_attn(12, lambda r: np.array([1300, 5, 257]), 2, d, d, 1024, 64, "bf16",
+                        rab_std=0.5)
+    announce(f"bf16 P=1024 T=64 d={d}")
+    assert_rows_close(to_np(attn_on_gpu(x)), _oracle(x), TOL["bf16"], f"P=1024 d={d}")
+
+
 def test_large_position_table_falls_back_to_vector_kernel():
     x = synth.make_attn(10, lambda r: np.array([1500, 40]), 2, 64, 64, 2048, 64, "bf16",
                         rab_std=0.5)
