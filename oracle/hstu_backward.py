@@ -72,14 +72,17 @@ def _buckets(n, t, P, T):
     return bp, bt
 
 
-def attention_backward(offsets, ts, q, k, v, rab_pos, rab_time, N, d_out, P=None, T=None):
+def attention_backward(offsets, ts, q, k, v, rab_pos, rab_time, N, d_out, P=None, T=None,
+                       term_scale=None):
     """Gradients of causal jagged attention without the gate (eq. 2).
 
     q, k [T_tot, H, d_qk]; v, d_out [T_tot, H, d_v]. Returns
     (dq, dk, dv, d_rab_pos [H, P] or None, d_rab_time [H, T] or None), fp64.
     P and T give the table widths when a table is absent but its gradient is wanted: an
     absent table counts as zeros, and the time table's gradient needs timestamps (it is
-    zero without them)."""
+    zero without them).
+    term_scale, a dict, receives "d_rab_pos" and "d_rab_time": the same sums over |dz|, the
+    size of the terms each table entry adds up (the scale of its rounding error)."""
     offsets = np.asarray(offsets, dtype=np.int64)
     q, k, v, g = _f64(q), _f64(k), _f64(v), _f64(d_out)
     Ttot, H, dqk = q.shape
@@ -92,6 +95,8 @@ def attention_backward(offsets, ts, q, k, v, rab_pos, rab_time, N, d_out, P=None
     use_time = rab_time is not None and have_ts
     drp = np.zeros((H, P)) if P else None
     drt = np.zeros((H, T)) if T else None  # stays zero without timestamps
+    arp = np.zeros((H, P)) if P else None
+    art = np.zeros((H, T)) if T else None
     for b in range(len(offsets) - 1):
         s, e = int(offsets[b]), int(offsets[b + 1])
         n = e - s
@@ -112,8 +117,12 @@ def attention_backward(offsets, ts, q, k, v, rab_pos, rab_time, N, d_out, P=None
             dk[s:e, h] = dz.T @ q[s:e, h]
             if drp is not None:
                 drp[h] += np.bincount(bp[vis], weights=dz[vis], minlength=P)
+                arp[h] += np.bincount(bp[vis], weights=np.abs(dz[vis]), minlength=P)
             if drt is not None and have_ts:
                 drt[h] += np.bincount(bt[vis], weights=dz[vis], minlength=T)
+                art[h] += np.bincount(bt[vis], weights=np.abs(dz[vis]), minlength=T)
+    if term_scale is not None:
+        term_scale["d_rab_pos"], term_scale["d_rab_time"] = arp, art
     return dq, dk, dv, drp, drt
 
 
@@ -190,6 +199,14 @@ class LayerGrads:
     d_rab_time: Optional[np.ndarray]
     dgamma: np.ndarray
     dbeta: np.ndarray
+    # the size of the terms each reduction adds up: sums over |dz| for the two tables,
+    # |A|^T |B| for a weight gradient A^T B, column sums of |A| for a bias gradient
+    d_rab_pos_terms: Optional[np.ndarray] = None
+    d_rab_time_terms: Optional[np.ndarray] = None
+    dw1_terms: Optional[np.ndarray] = None
+    db1_terms: Optional[np.ndarray] = None
+    dw2_terms: Optional[np.ndarray] = None
+    db2_terms: Optional[np.ndarray] = None
 
 
 def layer_backward(offsets, ts, x, w, H, d_qk, d_v, N, d_y, eps=1e-5, residual=0, storage=None):
@@ -225,8 +242,9 @@ def layer_backward(offsets, ts, x, w, H, d_qk, d_v, N, d_y, eps=1e-5, residual=0
     do, dU, dgamma, dbeta = gate_backward(o, U, w.gamma, w.beta, eps, dG)
     do, dU = r(do), r(dU)
     # attention
+    terms = {}
     dQ, dK, dV, drp, drt = attention_backward(offsets, ts, Q, K, V, w.rab_pos, w.rab_time, N,
-                                              do.reshape(R, H, d_v))
+                                              do.reshape(R, H, d_v), term_scale=terms)
     dact = np.concatenate([dU, r(dV).reshape(R, cu), r(dQ).reshape(R, cq), r(dK).reshape(R, cq)],
                           axis=1)
     dz1 = r(dact * silu_grad(z1))
@@ -236,7 +254,9 @@ def layer_backward(offsets, ts, x, w, H, d_qk, d_v, N, d_y, eps=1e-5, residual=0
     if residual:
         dx = dx + gy
     dx = r(dx)
-    return LayerGrads(dx, dw1, db1, dw2, db2, drp, drt, dgamma, dbeta)
+    return LayerGrads(dx, dw1, db1, dw2, db2, drp, drt, dgamma, dbeta, terms["d_rab_pos"],
+                      terms["d_rab_time"], np.abs(dz1).T @ np.abs(x), np.abs(dz1).sum(axis=0),
+                      np.abs(gy).T @ np.abs(G), np.abs(gy).sum(axis=0))
 
 
 def layer_stack_backward(offsets, ts, x, layers, H, d_qk, d_v, N, d_y, eps=1e-5, residual=0,

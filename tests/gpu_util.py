@@ -78,6 +78,33 @@ def layer_weights_on_gpu(layers, dtype_name):
                              ln_gamma=dev(w.gamma), ln_beta=dev(w.beta)) for w in layers]
 
 
+FP32_TINY = 2.0 ** -126  # smallest normal fp32 value
+
+
+def assert_sums_close(g, o, o_storage, terms, tol, k=4.0, what=""):
+    """Gradients that are sums over many tokens or pairs (weight, bias and bias-table
+    gradients). Per entry, |g - o| <= max(tol |o_row|_inf, k |o_s - o|_row_inf,
+    tol * terms, FP32_TINY): besides the row bounds of assert_rows_close_storage, the error
+    may reach tol times the sum of the magnitudes of the terms added up (terms, from the
+    oracle), the standard error bound of a sum whose terms each carry a relative error.
+    That matters where the terms cancel: a table entry of 1e-25 made of 1e7 terms of 1e-28
+    has no meaningful relative error at the size of the result. Below the fp32 normal
+    range (the device accumulates in fp32 and flushes denormals) differences are not
+    resolved at all, hence the absolute floor."""
+    assert np.all(np.isfinite(g)), f"{what}: non-finite output"
+    g = np.asarray(g, np.float64).reshape(len(g), -1)
+    o = np.asarray(o, np.float64).reshape(len(o), -1)
+    s = np.asarray(o_storage, np.float64).reshape(len(o), -1)
+    t = np.asarray(terms, np.float64).reshape(len(o), -1)
+    err = np.abs(g - o)
+    row = np.maximum(tol * np.abs(o).max(axis=1), k * np.abs(s - o).max(axis=1))[:, None]
+    bound = np.maximum(np.maximum(row, tol * t), FP32_TINY)
+    bad = err > bound
+    assert not bad.any(), f"{what}: {int(bad.sum())} entries outside the bound; worst excess " \
+                          f"{float((err / np.maximum(bound, 1e-300)).max()):.3f}"
+    return float((err / np.maximum(np.maximum(np.abs(o).max(axis=1)[:, None], t), 1e-300)).max())
+
+
 def assert_rows_close_storage(g, o, o_storage, tol, k=4.0, what=""):
     """bf16 multi-step paths: per row, |g - o|_inf <= max(tol |o|_inf, k |o_s - o|_inf).
     Here o is the fp64 oracle and o_s is the oracle with bf16 storage of the tensors
