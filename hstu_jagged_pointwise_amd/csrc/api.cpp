@@ -371,6 +371,7 @@ struct MfHistBufs {
 struct MfCandBufs {
   void* c_uvqk;
   float* c_o;
+  float* c_self;  // self weights of the candidates, [rows][H] (MFMA attention kernel)
   void* c_g;
   void* cx[2];
 };
@@ -419,6 +420,7 @@ void carve_cand_ws(Carver& c, const mfalcon_desc* d, const MfPlan& p, MfCandBufs
     MfCandBufs* b = bs + i;
     b->c_uvqk = c.take((size_t)m * f1 * es);
     b->c_o = (float*)c.take((size_t)p.kv_splits * m * hv * sizeof(float));
+    b->c_self = uses_mfma(&a) ? (float*)c.take((size_t)m * a.num_heads * sizeof(float)) : nullptr;
     b->c_g = c.take((size_t)m * hv * es);
     b->cx[0] = ld.num_layers > 1 ? c.take((size_t)m * ld.d_model * es) : nullptr;
     b->cx[1] = ld.num_layers > 2 ? c.take((size_t)m * ld.d_model * es) : nullptr;
@@ -636,13 +638,16 @@ hstu_status run_candidates(const mfalcon_desc* d, const MfPlan& p, const int64_t
         aa.kv_splits = p.kv_splits;
         aa.keys_per_split = p.keys_per_split;
         aa.part_stride = rows * hv;
+        // the MFMA kernel leaves the candidates' own values to the layer norm
+        aa.self_w = b.c_self;
         for (int u0 = ub; u0 < ue; u0 += 65535) {
           aa.user_begin = u0;
           aa.n_users = std::min(ue - u0, 65535);
           HSTU_TRY(run_attention(&a, aa, true, s), "candidate attention");
         }
         HSTU_TRY(launch_ln_gate(b.c_o, hv, aa.kv_splits, aa.part_stride, cv.u, cv.ld, w.ln_gamma,
-                                w.ln_beta, a.ln_eps, b.c_g, hv, rows, hv, bf, s),
+                                w.ln_beta, a.ln_eps, b.c_g, hv, rows, hv, bf, s, aa.self_w, cv.v,
+                                cv.ld, a.d_v),
                  "candidate layer norm gate");
         HSTU_TRY(launch_gemm(b.c_g, hv, w.w2, hv, w.b2, ld.residual ? in : nullptr, dm, out, dm,
                              rows, dm, hv, 0, bf, s),

@@ -43,8 +43,10 @@
 // Blocks entirely above the diagonal are skipped.
 //
 // Candidate mode (M-FALCON): the queries are one user's candidates, all at
-// position n_h. The keys are that user's history, all visible. Each
-// candidate's own key and value are added in the epilogue. When a wavefront's
+// position n_h. The keys are that user's history, all visible. The first key
+// range also scores each candidate against its own key and stores the weight
+// SiLU(score) / N per row and head; the layer norm that reads the summed rows
+// adds weight * v_c there, so no split rereads V of the candidates. When a wavefront's
 // candidates share one timestamp, a pair's whole bias depends on its key only;
 // the bias step then multiplies a per-key bias by ones, and every unmasked block
 // takes the fast path whatever its buckets.
@@ -153,7 +155,6 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
   __shared__ float rp[kMaxP];
   __shared__ float rt[kTimeTab];
   __shared__ float rtc[32];
-  __shared__ float pself[4][32];
 
   const TileDecode t = decode<CAND>(a, MBM);
   if (!t.valid) return;  // uniform across the workgroup
@@ -195,9 +196,9 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
     }
   }
   // candidate mode, first key range: the candidate's own key (relative position 0,
-  // elapsed time 0) is loaded with Q and its SiLU score kept for the epilogue
-  const bool add_self = CAND && blockIdx.z == 0;
-  if (add_self) {
+  // elapsed time 0) is loaded with Q and its weight SiLU(score) / N stored per row and
+  // head, for the layer norm that follows to add weight * v_c (it reads the row anyway)
+  if (CAND && blockIdx.z == 0) {
     const bf16* kc = (const bf16*)a.kc;
     float part = 0.f;
     if (row_ok) {
@@ -214,7 +215,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
     float xs = part;
     if (has_pos) xs += sload(a.rab_pos + (int64_t)h * P);
     if (has_time) xs += sload(a.rab_time + (int64_t)h * T);
-    if (hl == 0) pself[w][l32] = row_ok ? silu_fast(xs) : 0.f;  // read back by this wavefront
+    if (hl == 0 && row_ok) a.self_w[(t.q_local + wrow) * a.H + h] = silu_fast(xs) * a.inv_n;
   }
   const int64_t tq = (has_time && row_ok) ? a.ts_q[t.q_base + wrow] : 0;
   const uint32_t tq1 = (uint32_t)tq + 1u;
@@ -632,20 +633,6 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
   __syncthreads();
   if (!wave_live) return;
 
-  // the candidate's own value, weighted by its self score: every load is issued
-  // before the first use, so their latencies overlap
-  float vself[NC][16];
-  if constexpr (CAND) {
-    const bf16* vc = (const bf16*)a.vc;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int rowl = 32 * w + 8 * (r >> 2) + 4 * hl + (r & 3);
-      const bool ok = add_self && rowl < t.rows;
-#pragma unroll
-      for (int c = 0; c < NC; ++c)
-        vself[c][r] = ok ? (float)vc[(t.q_local + rowl) * a.ld_vc + (int64_t)h * D + c * 32 + l32] : 0.f;
-    }
-  }
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int rw = 8 * (r >> 2) + 4 * hl + (r & 3);  // row within the wavefront
@@ -653,13 +640,10 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
     if (rowl >= t.rows) continue;
     const int64_t orow = (CAND ? (int64_t)blockIdx.z * a.part_stride : 0) +
                          (t.q_local + rowl) * a.ld_o + (int64_t)h * D;
-    const float ps = add_self ? pself[w][rw] : 0.f;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const int col = c * 32 + l32;
-      float val = o[c][r];
-      if constexpr (CAND) val = fmaf(ps, vself[c][r], val);
-      val *= a.inv_n;
+      const float val = o[c][r] * a.inv_n;
       if (a.out_f32)
         ((float*)a.out)[orow + col] = val;
       else

@@ -53,6 +53,10 @@ struct AttnArgs {
   int kv_splits;
   int64_t keys_per_split;
   int64_t part_stride;
+  // candidate mode, MFMA kernel: where split 0 writes each candidate's self weight
+  // SiLU(q_c.k_c + rab_pos[0] + rab_time[0]) / N, [microbatch rows][H], for the LN gate to
+  // add self_w * v_c (the vector-ALU kernel adds the self term itself and ignores this)
+  float* self_w;
 };
 
 // Tile sizes (query rows per work item) of the two attention kernels.
@@ -116,7 +120,8 @@ hipError_t launch_bias_grad_reduce(const float* partial, int n_items, int H, int
 hipError_t launch_ln_gate(const float* o, int64_t ld_o, int nsplit, int64_t split_stride,
                           const void* u, int64_t ld_u, const float* gamma, const float* beta,
                           float eps, void* out, int64_t ld_out, int64_t rows, int w, int use_bf16,
-                          hipStream_t s);
+                          hipStream_t s, const float* self_w = nullptr,
+                          const void* vself = nullptr, int64_t ld_vself = 0, int dv = 0);
 
 // C[M,N] = epi(A[M,K] W[N,K]^T + bias[N]); epi = SiLU when silu, + R[M,N] when R.
 hipError_t launch_gemm(const void* A, int64_t lda, const void* W, int64_t ldw,
