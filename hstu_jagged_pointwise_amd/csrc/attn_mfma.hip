@@ -24,7 +24,9 @@
 // works on block 1 while the vector ALU activates block 0.
 //
 // Bias classes, decided per (wavefront, 32-key block) from exact integer
-// ranges, one tile ahead of their use and in scalar registers:
+// ranges. The lanes decide them in bulk, lane i for key block i of a group of
+// 64 (32 tiles), and each tile reads its two blocks' classes from their lanes
+// (v_readlane), so the per-tile cost is a few instructions:
 //   * The position bucket min(i-j, P-1) is one constant when every i-j >= P-1.
 //   * The time bucket is monotone in the elapsed time, so over the block's
 //     elapsed-time range [min t_i - max t_j, max t_i - min t_j] (the key side
@@ -179,7 +181,6 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
     }
   }
   const float pb = has_pos ? sload(a.rab_pos + (int64_t)h * P + P - 1) : 0.f;  // bucket P-1
-  const float* rtg = a.rab_time + (int64_t)h * T;
 
   // this lane's query row (the S^T column it holds) and its Q fragment
   const int wrow = 32 * w + l32;
@@ -272,10 +273,11 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
     const char* vb;
     uint32_t lim;  // last key row of the data in the tile
   };
-  auto dma_src = [&](int k0) {
-    return DmaSrc{kg + (t.k_base + k0) * a.ld_k * 2, vg + (t.k_base + k0) * a.ld_v * 2,
-                  (uint32_t)(nk - 1 - k0)};
-  };
+  // the source of the tile being fetched: set for the first tile, then advanced by one
+  // tile of rows per step (K and V share the row stride)
+  DmaSrc nsrc{kg + (t.k_base + kbeg) * a.ld_k * 2, vg + (t.k_base + kbeg) * a.ld_v * 2,
+              (uint32_t)(nk - 1 - kbeg)};
+  const int64_t tile_bytes = (int64_t)MBN * a.ld_k * 2;
   // this wavefront's instruction pairs (K and V) for one tile
   auto dma_pair = [&](auto bufc, const DmaSrc& src, int j) {
     constexpr int buf = decltype(bufc)::value;
@@ -316,42 +318,53 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
     }
   };
 
-  // ---- bias classes (scalar), from the key blocks' precomputed timestamp ranges
+  // ---- bias classes, from the key blocks' precomputed timestamp ranges. Lane i of
+  // the wavefront classifies key block 64 g + i of the range (32 keys each) for a
+  // group g of 64 blocks, 32 tiles; each tile then reads its two blocks' classes
+  // from their lanes. The ranges of the next group are fetched a group ahead.
   const KeyRange* krs = has_time ? a.key_ranges + key_range_slot(t.k_base, t.seq) : nullptr;
-  auto load_ranges = [&](int k0, KeyRange* r) {
-    if (has_time && wave_live) {
-      const KeyRange* p = krs + (k0 >> 5);  // p + 1 is a valid slot even past the last block
-      r[0].lo = sload(&p[0].lo);
-      r[0].hi = sload(&p[0].hi);
-      r[1].lo = sload(&p[1].lo);
-      r[1].hi = sload(&p[1].hi);
-    }
+  struct LaneClass {
+    uint32_t bits;  // a TileClass byte in bits 0-6, the highest time bucket in bits 8-13
+    float tlo, thi;
   };
-  auto classify = [&](int k0, const KeyRange* r) {
-    TileClass c;
-    c.f = 0;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int kb0 = k0 + 32 * kb;
-      const bool act = wave_live && kb0 < kend && (CAND || kb0 <= wlast);
-      const bool mask = CAND ? (kb0 + 32 > kend) : (kb0 + 31 > wrow0);
-      const int min_dpos = (CAND ? qpos0 : wrow0) - (kb0 + 31);
-      const bool pos_c = !has_pos || min_dpos >= P - 1;
-      uint32_t bits = (act ? 1u : 0u) | (mask ? 2u : 0u) | (pos_c ? 4u : 0u) | 32u | 64u;
-      c.tlo[kb] = 0.f;
-      c.thi[kb] = 0.f;
-      if (has_time && act) {
-        const int64_t lo = qmin - r[kb].hi, hi = qmax - r[kb].lo;  // elapsed-time range
-        const int blo = bucket_of(lo, T), bhi = bucket_of(hi, T);
-        const bool tfast = time_fast_ok(qmin, qmax, r[kb].lo, r[kb].hi);
-        const uint32_t tmode = blo == bhi ? 0u : ((bhi == blo + 1 && tfast) ? 1u : 2u);
-        bits = (bits & 7u) | (tmode << 3) | (tfast ? 32u : 0u) | (lo >= 0 ? 64u : 0u);
-        c.f |= (uint32_t)bhi << (16 + 8 * kb);
-        c.tlo[kb] = sload(rtg + blo);
-        c.thi[kb] = sload(rtg + bhi);
-      }
-      c.f |= bits << (8 * kb);
+  auto lane_range = [&](int g) {
+    KeyRange r{0, 0};
+    const int kb0 = kbeg + 32 * (64 * g + lane);
+    if (has_time && wave_live && kb0 < kend) r = krs[kb0 >> 5];
+    return r;
+  };
+  auto lane_classify = [&](int g, const KeyRange& r) {
+    const int kb0 = kbeg + 32 * (64 * g + lane);
+    const bool act = wave_live && kb0 < kend && (CAND || kb0 <= wlast);
+    const bool mask = CAND ? (kb0 + 32 > kend) : (kb0 + 31 > wrow0);
+    const int min_dpos = (CAND ? qpos0 : wrow0) - (kb0 + 31);
+    const bool pos_c = !has_pos || min_dpos >= P - 1;
+    LaneClass c{(act ? 1u : 0u) | (mask ? 2u : 0u) | (pos_c ? 4u : 0u) | 32u | 64u, 0.f, 0.f};
+    if (has_time && act) {
+      const int64_t lo = qmin - r.hi, hi = qmax - r.lo;  // elapsed-time range
+      const int blo = bucket_of(lo, T), bhi = bucket_of(hi, T);
+      const bool tfast = time_fast_ok(qmin, qmax, r.lo, r.hi);
+      const uint32_t tmode = blo == bhi ? 0u : ((bhi == blo + 1 && tfast) ? 1u : 2u);
+      c.bits = (c.bits & 7u) | (tmode << 3) | (tfast ? 32u : 0u) | (lo >= 0 ? 64u : 0u) |
+               ((uint32_t)bhi << 8);
+      c.tlo = rt[blo];
+      c.thi = rt[bhi];
     }
+    return c;
+  };
+  auto tile_class = [&](const LaneClass& lc, int kt) {
+    const int l0 = (2 * kt) & 63;  // the tile's first block's lane
+    const uint32_t b0 = __builtin_amdgcn_readlane(lc.bits, l0);
+    const uint32_t b1 = __builtin_amdgcn_readlane(lc.bits, l0 + 1);
+    auto rdf = [&](float v, int l) {
+      return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+    };
+    TileClass c;
+    c.f = (b0 & 0xffu) | ((b1 & 0xffu) << 8) | ((b0 >> 8) << 16) | ((b1 >> 8) << 24);
+    c.tlo[0] = rdf(lc.tlo, l0);
+    c.tlo[1] = rdf(lc.tlo, l0 + 1);
+    c.thi[0] = rdf(lc.thi, l0);
+    c.thi[1] = rdf(lc.thi, l0 + 1);
     return c;
   };
 
@@ -359,21 +372,21 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
   // Pipeline: tile t computes while tile t+1's keys and values stream into the
-  // idle buffer. At the start of tile t the bias classes of tile t+1 are
-  // decided from timestamp ranges requested one tile earlier, and those of tile
-  // t+2 are requested, so no scalar load is waited for on the way.
-  TileClass cls{};
-  KeyRange rnx[2];  // timestamp ranges of the next tile's key blocks
+  // idle buffer. Every 32 tiles the lanes classify the next 64 key blocks from
+  // timestamp ranges fetched 32 tiles earlier.
+  LaneClass lcl{0u, 0.f, 0.f};
+  KeyRange lrn{0, 0};  // this lane's timestamp range in the next group
   if (nkt > 0) {
-    dma_tile(B0{}, dma_src(kbeg));
+    dma_tile(B0{}, nsrc);
     ts_fetch(kbeg);
-    KeyRange r[2];
-    load_ranges(kbeg, r);
-    cls = classify(kbeg, r);
-    if (nkt > 1) load_ranges(kbeg + MBN, rnx);
+    lrn = lane_range(0);
     finish_tile(B0{}, true);
   }
-  __syncthreads();
+  __syncthreads();  // also publishes the bias tables in LDS
+  if (nkt > 0) {
+    lcl = lane_classify(0, lrn);
+    if (nkt > 32) lrn = lane_range(1);
+  }
 
   auto kfrag = [&](const bf16* Kt, int kb, int kk) {
     return load_bf16x8(&Kt[tile_off<D>(32 * kb + l32, 16 * kk + 8 * hl)]);
@@ -417,18 +430,19 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
     const int kn = k0 + MBN;  // the next tile's first key
     // the last tile refills the idle buffer with its own keys (harmless), so
     // that the DMA inside the fenced fast path needs no branch
-    const DmaSrc nsrc = dma_src(more ? kn : k0);
+    if (more) {
+      nsrc.kb += tile_bytes;
+      nsrc.vb += tile_bytes;
+      nsrc.lim -= MBN;
+    }
     auto dma = [&](int j) { dma_pair(BN_{}, nsrc, j); };
     if (wu == 0) dma(NIW - 1);
     if (more) ts_fetch(kn);
-    // the next tile's classes, from timestamp ranges requested a tile ago; the
-    // scalar loads of their table values then have this whole tile to land
-    TileClass cn = cls;
-    KeyRange rn2[2] = {};
-    if (more) {
-      cn = classify(kn, rnx);
-      if (kt + 2 < nkt) load_ranges(kn + MBN, rn2);
+    if (kt > 0 && (kt & 31) == 0) {  // a new group of 64 key blocks
+      lcl = lane_classify(kt >> 5, lrn);
+      if (kt + 32 < nkt) lrn = lane_range((kt >> 5) + 1);
     }
+    const TileClass cls = tile_class(lcl, kt);
     const BlockClass c0 = block_class(cls, 0);
     const BlockClass c1 = block_class(cls, 1);
     const bf16* Kt = buf ? Ks1 : Ks0;
@@ -621,9 +635,6 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
     }
     finish_tile(BN_{}, more);
     __syncthreads();
-    cls = cn;
-    rnx[0] = rn2[0];
-    rnx[1] = rn2[1];
   };
   for (int kt = 0; kt < nkt; kt += 2) {
     tile_step(B0{}, kt);

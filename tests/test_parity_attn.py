@@ -93,6 +93,17 @@ def test_largest_tables_on_mfma_kernel(d):
     assert_rows_close(to_np(attn_on_gpu(x)), _oracle(x), TOL["bf16"], f"P=1024 d={d}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_key_block_groups(d):
+    """The MFMA kernel decides the bias path of 64 key blocks (2,048 keys) at a time: rows
+    that see exactly 2,048 keys, one more, and 4,160 (into a third group), beside a short
+    sequence, with both bias tables."""
+    x = synth.make_attn(13, lambda r: np.array([2048, 2049, 31, 4160]), 2, d, d, 128, 64, "bf16",
+                        rab_std=0.5)
+    announce(f"bf16 key-block groups d={d}")
+    assert_rows_close(to_np(attn_on_gpu(x)), _oracle(x), TOL["bf16"], f"key-block groups d={d}")
+
+
 def test_large_position_table_falls_back_to_vector_kernel():
     x = synth.make_attn(10, lambda r: np.array([1500, 40]), 2, 64, 64, 2048, 64, "bf16",
                         rab_std=0.5)
