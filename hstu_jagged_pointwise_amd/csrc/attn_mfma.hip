@@ -91,6 +91,19 @@ template <int D>
 constexpr int tile_elems() {
   return MBN * (D + 8);
 }
+// V tiles: unpadded rows whose 16-byte chunks are permuted by an XOR of the row. A
+// transposing read (ds_read_b64_tr_b16) of 16 lanes covers 4 consecutive rows and 2
+// adjacent chunks, and the lanes of the next 16 the next 2 chunks of the same rows;
+// the XOR moves each of the 4 rows' chunks to a different quarter of the row, so the
+// 32 lanes touch 32 distinct bank pairs.
+template <int D>
+__device__ __forceinline__ int vswz(int row) {
+  return (row & 3) * (D / 32);
+}
+template <int D>
+__device__ __forceinline__ int vtile_off(int row, int col) {
+  return row * D + ((((col >> 3) ^ vswz<D>(row))) << 3) + (col & 7);
+}
 
 // exact time bucket of an elapsed time (negative counts as 0), clamped to the table
 __device__ __forceinline__ int bucket_of(int64_t dt, int T) {
@@ -141,7 +154,7 @@ bool attn_mfma_strides_ok(const AttnArgs& a) {
 }
 
 template <int D, bool CAND>
-__global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256, D <= 64 ? 3 : 2) void attn_mfma_kernel(AttnArgs a) {
   constexpr int NKK = D / 16;  // k-steps of the S^T contraction
   constexpr int NC = D / 32;   // 32-wide output column blocks
   constexpr int CPR = D / 8;   // 16-byte chunks per row
@@ -150,8 +163,8 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
   // the in-flight DMA target from the buffer being read (no conservative waits)
   __shared__ __attribute__((aligned(16))) bf16 Ks0[TE];
   __shared__ __attribute__((aligned(16))) bf16 Ks1[TE];
-  __shared__ __attribute__((aligned(16))) bf16 Vs0[TE];
-  __shared__ __attribute__((aligned(16))) bf16 Vs1[TE];
+  __shared__ __attribute__((aligned(16))) bf16 Vs0[MBN * D];
+  __shared__ __attribute__((aligned(16))) bf16 Vs1[MBN * D];
   __shared__ __attribute__((aligned(16))) uint32_t tk_lo[2][MBN];
   __shared__ int64_t tk64[2][MBN];
   __shared__ float rp[kMaxP];
@@ -246,25 +259,34 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
     for (int r = 0; r < 16; ++r) o[c][r] = 0.f;
 
   // ---- key tiles go global -> LDS directly (global_load_lds_dwordx4): lane L of one
-  // instruction fills 16-byte slot L of a contiguous 1 KiB span, so the padded
-  // layout comes from which source chunk each lane fetches. Rows past the data
-  // repeat the last valid row: their scores are masked and multiply finite values.
-  constexpr int SPR = CPR + 1;        // 16-byte slots per LDS row
-  constexpr int NSLOT = MBN * SPR;    // slots per matrix tile
-  constexpr int NINSTR = NSLOT / 64;  // wave-instructions per matrix tile
+  // instruction fills 16-byte slot L of a contiguous 1 KiB span, so the LDS layout
+  // comes from which source chunk each lane fetches. K rows are padded by one slot
+  // (row-fragment reads, see tile_off); V rows are unpadded with their 16-byte chunks
+  // permuted by an XOR of the row (see vtile_off). Rows past the data repeat the
+  // last valid row: their scores are masked and multiply finite values.
+  constexpr int SPR = CPR + 1;        // 16-byte slots per K row
+  constexpr int NSLOT = MBN * SPR;    // slots per K tile
+  constexpr int NINSTR = NSLOT / 64;  // wave-instructions per K tile
   constexpr int NIW = (NINSTR + 3) / 4;
   static_assert(NSLOT % 64 == 0, "every DMA instruction fills 64 slots");
+  static_assert(MBN * CPR == 4 * 64 * (NIW - 1), "each wavefront issues NIW - 1 V instructions");
   // Wavefront w issues instructions w, w+4, w+8, ... of each matrix tile. The
   // (key row, byte column) source of each of its slots is packed into one word,
   // computed once; K and V share the row stride. The address is a uniform base
   // plus a 32-bit offset (the scalar-base form of the instruction).
   const uint32_t ldb = (uint32_t)(a.ld_k * 2);
-  uint32_t spk[NIW];
+  uint32_t spk[NIW], spv[NIW - 1];
 #pragma unroll
   for (int j = 0; j < NIW; ++j) {
     const int slot = 64 * (w + 4 * j) + lane;
     const int row = slot / SPR, pc = slot % SPR;
     spk[j] = (uint32_t)row | ((uint32_t)(pc < CPR ? pc : 0) << 10);
+  }
+#pragma unroll
+  for (int j = 0; j < NIW - 1; ++j) {
+    const int slot = 64 * (w + 4 * j) + lane;
+    const int row = slot / CPR;
+    spv[j] = (uint32_t)row | ((uint32_t)((slot % CPR) ^ vswz<D>(row)) << 10);
   }
   const char* kg = (const char*)a.k + (int64_t)h * D * 2;
   const char* vg = (const char*)a.v + (int64_t)h * D * 2;
@@ -278,24 +300,29 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
   DmaSrc nsrc{kg + (t.k_base + kbeg) * a.ld_k * 2, vg + (t.k_base + kbeg) * a.ld_v * 2,
               (uint32_t)(nk - 1 - kbeg)};
   const int64_t tile_bytes = (int64_t)MBN * a.ld_k * 2;
-  // this wavefront's instruction pairs (K and V) for one tile
+  // this wavefront's instruction pair j (K and V; the last K instruction has no V
+  // partner) for one tile
   auto dma_pair = [&](auto bufc, const DmaSrc& src, int j) {
     constexpr int buf = decltype(bufc)::value;
     bf16* Kd = buf ? Ks1 : Ks0;
     bf16* Vd = buf ? Vs1 : Vs0;
+    const int i = wu + 4 * j;
     {
-      const int i = wu + 4 * j;
       const uint32_t row = min(spk[j] & 1023u, src.lim);
       const uint32_t off = row * ldb + 16u * (spk[j] >> 10);
       __builtin_amdgcn_global_load_lds(
           (const __attribute__((address_space(1))) void*)(src.kb + off),
           (__attribute__((address_space(3))) void*)(&Kd[512 * i]), 16, 0, 0);
+    }
+    if (j < NIW - 1) {
+      const uint32_t row = min(spv[j] & 1023u, src.lim);
+      const uint32_t off = row * ldb + 16u * (spv[j] >> 10);
       __builtin_amdgcn_global_load_lds(
           (const __attribute__((address_space(1))) void*)(src.vb + off),
           (__attribute__((address_space(3))) void*)(&Vd[512 * i]), 16, 0, 0);
     }
   };
-  static_assert(NINSTR == 4 * (NIW - 1) + 1, "only wavefront 0 issues a last pair");
+  static_assert(NINSTR == 4 * (NIW - 1) + 1, "only wavefront 0 issues a last K instruction");
   auto dma_tile = [&](auto bufc, const DmaSrc& src) {
 #pragma unroll
     for (int j = 0; j < NIW - 1; ++j) dma_pair(bufc, src, j);
@@ -411,8 +438,8 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
     const int s2 = m / NC, c = m % NC;
     const int krow = 32 * kb + 16 * s2 + 4 * hl + (rho >> 2);
     const int col = c * 32 + 16 * (g16 & 1) + 4 * (rho & 3);
-    const bf16x4 v1 = tr_read(&Vt[tile_off<D>(krow, col)]);
-    const bf16x4 v2 = tr_read(&Vt[tile_off<D>(krow + 8, col)]);
+    const bf16x4 v1 = tr_read(&Vt[vtile_off<D>(krow, col)]);
+    const bf16x4 v2 = tr_read(&Vt[vtile_off<D>(krow + 8, col)]);
     bf16x8 bv;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
