@@ -37,8 +37,9 @@
 //         t_i + 1 - t_j >= 2^(b+1), one 32-bit compare and select per element;
 //       - more: the bucket of each element from the count of leading zeros of
 //         the 32-bit t_i + 1 - t_j (a 64-bit path covers spans past 2^31 s).
-//   * A constant bias enters through one extra MFMA k-step (below), at no cost
-//     per element. A block whose position bucket varies gathers it per element
+//   * A constant bias is the starting value of the S^T accumulator (exact fp32,
+//     16 moves per block; candidate mode adds it as an extra MFMA k-step, see
+//     bias_step). A block whose position bucket varies gathers it per element
 //     from an LDS-resident table.
 // Masking is a select after SiLU (SiLU(-inf) would be NaN). It runs only on
 // blocks that cross the causal diagonal (or the history tail for candidates).
@@ -50,7 +51,7 @@
 // SiLU(score) / N per row and head; the layer norm that reads the summed rows
 // adds weight * v_c there, so no split rereads V of the candidates. When a wavefront's
 // candidates share one timestamp, a pair's whole bias depends on its key only;
-// the bias step then multiplies a per-key bias by ones, and every unmasked block
+// an extra MFMA k-step then multiplies a per-key bias by ones, and every unmasked block
 // takes the fast path whatever its buckets.
 #include "attn_common.h"
 
@@ -244,8 +245,8 @@ __global__ __launch_bounds__(256, D <= 64 ? 3 : 2) void attn_mfma_kernel(AttnArg
   // bias), so a pair's bias depends on the key alone
   const bool keyb_ok = CAND && (!has_time || qmin == qmax);
 
-  // constant A fragment for the bias k-step, A[key][0] = A[key][1] = 1, rebuilt at
-  // each use (one select and three zero moves) rather than held in registers
+  // constant fragment of the bias k-step (candidate mode), [0] = [1] = 1 in the first
+  // half-wavefront, rebuilt at each use rather than held in registers
   const uint32_t ones_w = hl == 0 ? 0x3f803f80u : 0u;  // two bf16 ones in one word
   auto ones = [&]() {
     u32x4 f = {ones_w, 0u, 0u, 0u};
@@ -418,8 +419,8 @@ __global__ __launch_bounds__(256, D <= 64 ? 3 : 2) void attn_mfma_kernel(AttnArg
   auto kfrag = [&](const bf16* Kt, int kb, int kk) {
     return load_bf16x8(&Kt[tile_off<D>(32 * kb + l32, 16 * kk + 8 * hl)]);
   };
-  // B fragment of the bias k-step: rows 0 and 1 hold bias_hi and bias_lo (a bf16
-  // split, exact to ~2^-16 relative) for every query column
+  // fragment of the bias k-step: k-slots 0 and 1 hold bias_hi and bias_lo (a bf16
+  // split, exact to ~2^-16 relative) of this lane's query or, for a per-key bias, key
   auto bias_frag = [&](float bias) {
     bf16x8 bfrag;
 #pragma unroll
@@ -494,13 +495,21 @@ __global__ __launch_bounds__(256, D <= 64 ? 3 : 2) void attn_mfma_kernel(AttnArg
         pa[r >> 3][r & 7] = (bf16)silu_fast(x[r]);
       }
     };
-    // the bias k-step: a bias per query (ones on the key side), or, given keyA, a bias
-    // per key (keyA on the key side, ones on the query side)
-    auto bias_step = [&](float bias, const bf16x8* keyA) {
+    // the start of a block's S^T accumulator: the block's constant bias, or, given keyA,
+    // a bias per key through one MFMA k-step (keyA on the key side, ones on the query
+    // side). Candidate mode takes its constant bias through the same k-step (ones times
+    // a bf16 hi/lo split), so that a candidate's scores round the same way whichever of
+    // the two its wavefront takes.
+    auto bias_step = [&](float bias, const bf16x8* keyA) -> f32x16 {
       if (keyA) return __builtin_amdgcn_mfma_f32_32x32x16_bf16(*keyA, ones(), f32x16{}, 0, 0, 0);
-      return __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones(), bias_frag(bias), f32x16{}, 0, 0, 0);
+      if constexpr (CAND)
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones(), bias_frag(bias), f32x16{}, 0, 0, 0);
+      f32x16 xb;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xb[r] = bias;
+      return xb;
     };
-    // S^T of one block, with the constant part of its bias through the bias k-step
+    // S^T of one block, starting from the constant part of its bias
     auto s_chain = [&](int kb, float bias, const bf16x8* keyA, bool with_dma) {
       bf16x8 kq[NKK];
 #pragma unroll
@@ -525,7 +534,7 @@ __global__ __launch_bounds__(256, D <= 64 ? 3 : 2) void attn_mfma_kernel(AttnArg
     bf16x8 pa0[2];
     f32x16 x1;
     // Common case: both blocks live, no mask, one position bucket and one time
-    // bucket per block, so the bias is a constant that the bias k-step adds. The
+    // bucket per block, so the bias is a constant that starts the accumulator. The
     // path is one basic block (no branch, so nothing moves across the fences);
     // its instruction order is written out and fenced (sched_barrier) so that
     // the in-order wavefront issues one MFMA, then the independent vector work
@@ -559,7 +568,7 @@ __global__ __launch_bounds__(256, D <= 64 ? 3 : 2) void attn_mfma_kernel(AttnArg
 
     // General path, one 32-key block at a time: any mix of masks, per-element
     // position buckets and per-element time buckets; the constant part of the
-    // bias (the lower time bucket when two) goes through the bias k-step.
+    // bias (the lower time bucket when two) starts the accumulator.
     auto general_block = [&](int kb, const BlockClass& bc) {
       if (!bc.act()) return f32x16{};
       const int kb0 = k0 + 32 * kb;
