@@ -290,11 +290,9 @@ UVQK split_view(const void* base, const hstu_attn_desc& a) {
 // and timestamps only, so one call serves every layer.
 hstu_status plan_causal(const hstu_attn_desc& a, const int64_t* off_dev, const int64_t* ts,
                         const Jagged& j, const LayerBufs& b, hipStream_t s) {
-  HSTU_TRY(launch_plan_causal(off_dev, a.batch, attn_tile_rows(&a), j.max_tiles, b.items,
-                              (int)j.items, s),
-           "tile planner");
-  if (ts && b.kr)
-    HSTU_TRY(launch_key_ranges(off_dev, ts, a.batch, j.max_len, b.kr, s), "key ranges");
+  HSTU_TRY(launch_plan(off_dev, a.batch, attn_tile_rows(&a), j.max_tiles, b.items, (int)j.items,
+                       ts && b.kr ? ts : nullptr, j.max_len, b.kr, s),
+           "tile planner and key ranges");
   return HSTU_OK;
 }
 
@@ -1034,13 +1032,10 @@ hstu_status hstu_attn_fwd(const hstu_attn_desc* desc, const int64_t* seq_offsets
   int2* items = (int2*)c.take((size_t)p.j.items * sizeof(int2));
   KeyRange* kr = (KeyRange*)c.take(key_range_bytes(desc, p.j.total));
   float* o32 = u ? (float*)c.take((size_t)p.j.total * desc->num_heads * desc->d_v * 4) : nullptr;
-  HSTU_TRY(launch_plan_causal(seq_offsets, desc->batch, attn_tile_rows(desc), p.j.max_tiles, items,
-                              (int)p.j.items, s),
-           "tile planner");
   const bool timed = rab_time && timestamps && kr;
-  if (timed)
-    HSTU_TRY(launch_key_ranges(seq_offsets, timestamps, desc->batch, p.j.max_len, kr, s),
-             "key ranges");
+  HSTU_TRY(launch_plan(seq_offsets, desc->batch, attn_tile_rows(desc), p.j.max_tiles, items,
+                       (int)p.j.items, timed ? timestamps : nullptr, p.j.max_len, kr, s),
+           "tile planner and key ranges");
   AttnArgs a = base_args(desc);
   a.q = q;
   a.k = k;
@@ -1348,12 +1343,10 @@ hstu_status hstu_attn_bwd(const hstu_attn_desc* desc, const int64_t* seq_offsets
   int2* items = (int2*)c.take(p.items);
   KeyRange* kr = (KeyRange*)c.take(p.ranges);
   float* partial = (float*)c.take(p.partial);
-  HSTU_TRY(launch_plan_causal(seq_offsets, desc->batch, bwd_tile_rows(desc), p.j.max_tiles, items,
-                              (int)p.j.items, s),
-           "tile planner");
-  if (p.mfma && timestamps)
-    HSTU_TRY(launch_key_ranges(seq_offsets, timestamps, desc->batch, p.j.max_len, kr, s),
-             "key ranges");
+  HSTU_TRY(launch_plan(seq_offsets, desc->batch, bwd_tile_rows(desc), p.j.max_tiles, items,
+                       (int)p.j.items, p.mfma && timestamps ? timestamps : nullptr, p.j.max_len,
+                       kr, s),
+           "tile planner and key ranges");
   AttnBwdArgs a{};
   a.q = q;
   a.k = k;
@@ -1429,12 +1422,9 @@ hstu_status hstu_softmax_attn_fwd(const hstu_attn_desc* desc, const int64_t* seq
   Carver c{(char*)workspace};
   int2* items = (int2*)c.take((size_t)j.items * sizeof(int2));
   KeyRange* kr = (KeyRange*)c.take((size_t)key_range_slots(j.total, desc->batch) * sizeof(KeyRange));
-  HSTU_TRY(launch_plan_causal(seq_offsets, desc->batch, kMfmaRows, j.max_tiles, items,
-                              (int)j.items, s),
-           "tile planner");
-  if (timestamps)
-    HSTU_TRY(launch_key_ranges(seq_offsets, timestamps, desc->batch, j.max_len, kr, s),
-             "key ranges");
+  HSTU_TRY(launch_plan(seq_offsets, desc->batch, kMfmaRows, j.max_tiles, items, (int)j.items,
+                       timestamps, j.max_len, kr, s),
+           "tile planner and key ranges");
   AttnArgs a = base_args(desc);
   a.q = q;
   a.k = k;

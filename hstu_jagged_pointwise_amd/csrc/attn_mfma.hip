@@ -479,6 +479,9 @@ __global__ __launch_bounds__(256, D <= 64 ? 3 : 2) void attn_mfma_kernel(AttnArg
     const bool fast = (cls.f & 0x1f1fu) == 0x0505u;
     // candidate mode with one timestamp per wavefront: both blocks live and unmasked suffice
     const bool keyb_tile = CAND && keyb_ok && (cls.f & 0x0303u) == 0x0101u;
+    // causal mode: both blocks live, unmasked, one position bucket, one or two time
+    // buckets each (the fast path's schedule plus a per-element two-bucket select)
+    const bool fast2 = !CAND && (cls.f & 0x1717u) == 0x0505u;
     // this lane's key's whole bias (candidate mode): position n_h - j, elapsed time t_c - t_j
     auto key_bias = [&](int kb0) {
       const int j = kb0 + l32;
@@ -569,6 +572,41 @@ __global__ __launch_bounds__(256, D <= 64 ? 3 : 2) void attn_mfma_kernel(AttnArg
     // General path, one 32-key block at a time: any mix of masks, per-element
     // position buckets and per-element time buckets; the constant part of the
     // bias (the lower time bucket when two) starts the accumulator.
+    // The upper bucket's excess over the constant, for the elements whose elapsed time
+    // reaches it (two-bucket blocks); the general path uses the same code.
+    auto two_bucket = [&](f32x16& x, int kb, const BlockClass& bc) {
+      const uint32_t* tkl = tk_lo[buf] + 32 * kb + 4 * hl;
+      const float dl = bc.thi - bc.tlo;
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const u32x4 tk4 = *reinterpret_cast<const u32x4*>(tkl + 8 * g4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int d = (int)(tq1 - tk4[e]);
+          x[4 * g4 + e] += d >= bc.thr() ? dl : 0.f;
+        }
+      }
+    };
+    // Fast path with two-bucket blocks (causal mode): the fast path's order, each
+    // block's scores corrected right after its S^T chain.
+    auto fast2_path = [&]() {
+      f32x16 s0 = s_chain(0, pb + c0.tlo, nullptr, true);
+      if (c0.tmode() == 1) two_bucket(s0, 0, c0);
+      bf16x8 k1[NKK];
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) k1[kk] = kfrag(Kt, 1, kk);
+      f32x16 s1 = bias_step(pb + c1.tlo, nullptr);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1[kk], qf[kk], s1, 0, 0, 0);
+        act_step(s0, pa0, kk);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (c1.tmode() == 1) two_bucket(s1, 1, c1);
+      x1 = s1;
+    };
+
     auto general_block = [&](int kb, const BlockClass& bc) {
       if (!bc.act()) return f32x16{};
       const int kb0 = k0 + 32 * kb;
@@ -585,17 +623,7 @@ __global__ __launch_bounds__(256, D <= 64 ? 3 : 2) void attn_mfma_kernel(AttnArg
       }
       const uint32_t* tkl = tk_lo[buf] + 32 * kb + 4 * hl;
       if (bc.tmode() == 1) {
-        // two adjacent buckets: the upper one's excess over the constant
-        const float dl = bc.thi - bc.tlo;
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const u32x4 tk4 = *reinterpret_cast<const u32x4*>(tkl + 8 * g4);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int d = (int)(tq1 - tk4[e]);
-            x[4 * g4 + e] += d >= bc.thr() ? dl : 0.f;
-          }
-        }
+        two_bucket(x, kb, bc);  // two adjacent buckets
       } else if (bc.tmode() == 2) {
         if (bc.tfast()) {
 #pragma unroll
@@ -637,6 +665,8 @@ __global__ __launch_bounds__(256, D <= 64 ? 3 : 2) void attn_mfma_kernel(AttnArg
     if (wave_live) {
       if (fast || keyb_tile)
         fast_path(keyb_tile);
+      else if (fast2)
+        fast2_path();
       else
         general_path();
     } else {

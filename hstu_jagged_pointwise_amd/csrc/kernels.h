@@ -69,11 +69,12 @@ bool attn_mfma_supported(int dtype_bf16, int d_qk, int d_v, int P, int T);
 // True when the MFMA kernel can take these row strides (K and V strides equal).
 bool attn_mfma_strides_ok(const AttnArgs& a);
 
-hipError_t launch_plan_causal(const int64_t* offsets, int B, int tile_rows, int max_tiles,
-                              int2* items, int n_items, hipStream_t s);
-// Fills the per-block timestamp ranges of B jagged sequences (see KeyRange).
-hipError_t launch_key_ranges(const int64_t* offsets, const int64_t* ts, int B, int64_t max_len,
-                             KeyRange* out, hipStream_t s);
+// Causal work list (sequence, query tile of tile_rows), longest first, and, when ts and kr
+// are set, the per-32-key timestamp ranges of the B jagged sequences (see KeyRange); one
+// launch.
+hipError_t launch_plan(const int64_t* offsets, int B, int tile_rows, int max_tiles, int2* items,
+                       int n_items, const int64_t* ts, int64_t max_len, KeyRange* kr,
+                       hipStream_t s);
 hipError_t launch_attn_simple(const AttnArgs& a, int use_bf16, bool cand, hipStream_t s);
 // Causal softmax attention (the softmax ablation of the pointwise kernel): bf16,
 // d_qk == d_v in {32,64,128}, P <= 1024; items from the planner with 128-row tiles,

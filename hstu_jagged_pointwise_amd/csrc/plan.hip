@@ -17,10 +17,9 @@ namespace hstu {
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanBins = 2048;
 
-__global__ __launch_bounds__(kPlanThreads) void plan_causal_kernel(const int64_t* __restrict__ off,
-                                                                   int B, int tile_rows, int nbins,
-                                                                   int2* __restrict__ items,
-                                                                   int n_items) {
+// one workgroup of kPlanThreads threads
+__device__ void plan_block(const int64_t* __restrict__ off, int B, int tile_rows, int nbins,
+                           int2* __restrict__ items, int n_items) {
   __shared__ int cnt[kPlanBins];
   __shared__ int start[kPlanBins];
   const int tid = threadIdx.x;
@@ -73,15 +72,15 @@ __global__ __launch_bounds__(kPlanThreads) void plan_causal_kernel(const int64_t
 // classifies at a time). Each half-wavefront reduces one block; the attention
 // kernel then decides a block's bias class from two scalar loads instead of
 // reducing timestamps itself on every key tile.
-__global__ __launch_bounds__(256) void key_range_kernel(const int64_t* __restrict__ off,
-                                                        const int64_t* __restrict__ ts,
-                                                        KeyRange* __restrict__ out) {
-  const int b = blockIdx.x;
+__device__ void key_range_block(const int64_t* __restrict__ off, const int64_t* __restrict__ ts,
+                                KeyRange* __restrict__ out, int b) {
   const int64_t s0 = off[b], n = off[b + 1] - s0;
   const int64_t nblk = (n + 31) / 32;
   const int64_t base = key_range_slot(s0, b);
+  constexpr int kHalves = kPlanThreads / 32;
   const int l32 = threadIdx.x & 31, half = threadIdx.x >> 5;
-  for (int64_t j = (int64_t)blockIdx.y * 8 + half; j < nblk; j += (int64_t)gridDim.y * 8) {
+  for (int64_t j = (int64_t)blockIdx.y * kHalves + half; j < nblk;
+       j += (int64_t)gridDim.y * kHalves) {
     const int64_t key = 32 * j + l32;
     const bool ok = key < n;
     int64_t mn = ok ? ts[s0 + key] : INT64_MAX;
@@ -96,20 +95,33 @@ __global__ __launch_bounds__(256) void key_range_kernel(const int64_t* __restric
   }
 }
 
-hipError_t launch_key_ranges(const int64_t* offsets, const int64_t* ts, int B, int64_t max_len,
-                             KeyRange* out, hipStream_t s) {
-  if (B <= 0 || max_len <= 0) return hipSuccess;
-  const int64_t blocks = (max_len + 31) / 32;
-  const unsigned gy = (unsigned)std::min<int64_t>((blocks + 7) / 8, 64);
-  hipLaunchKernelGGL(key_range_kernel, dim3((unsigned)B, gy), dim3(256), 0, s, offsets, ts, out);
-  return hipGetLastError();
+// The planner (workgroup (0, 0)) and, given timestamps, the key ranges of sequence b
+// (workgroups (1 + b, y)) in one launch: they are independent and both small.
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int64_t* __restrict__ off, int B,
+                                                            int tile_rows, int nbins,
+                                                            int2* __restrict__ items, int n_items,
+                                                            const int64_t* __restrict__ ts,
+                                                            KeyRange* __restrict__ kr) {
+  if (blockIdx.x == 0) {
+    if (blockIdx.y == 0) plan_block(off, B, tile_rows, nbins, items, n_items);
+    return;
+  }
+  key_range_block(off, ts, kr, (int)blockIdx.x - 1);
 }
 
-hipError_t launch_plan_causal(const int64_t* offsets, int B, int tile_rows, int max_tiles,
-                              int2* items, int n_items, hipStream_t s) {
-  int nbins = max_tiles < 1 ? 1 : (max_tiles > kPlanBins ? kPlanBins : max_tiles);
-  hipLaunchKernelGGL(plan_causal_kernel, dim3(1), dim3(kPlanThreads), 0, s, offsets, B, tile_rows,
-                     nbins, items, n_items);
+hipError_t launch_plan(const int64_t* offsets, int B, int tile_rows, int max_tiles, int2* items,
+                       int n_items, const int64_t* ts, int64_t max_len, KeyRange* kr,
+                       hipStream_t s) {
+  if (B <= 0) return hipSuccess;
+  const int nbins = max_tiles < 1 ? 1 : (max_tiles > kPlanBins ? kPlanBins : max_tiles);
+  const bool ranges = ts && kr && max_len > 0;
+  const int64_t blocks = (max_len + 31) / 32;
+  const unsigned gy =
+      ranges ? (unsigned)std::min<int64_t>((blocks + kPlanThreads / 32 - 1) / (kPlanThreads / 32), 64)
+             : 1u;
+  const dim3 grid(1u + (ranges ? (unsigned)B : 0u), gy);
+  hipLaunchKernelGGL(plan_kernel, grid, dim3(kPlanThreads), 0, s, offsets, B, tile_rows, nbins,
+                     items, n_items, ranges ? ts : nullptr, ranges ? kr : nullptr);
   return hipGetLastError();
 }
 
