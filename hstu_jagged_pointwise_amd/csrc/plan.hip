@@ -15,6 +15,7 @@
 namespace hstu {
 
 constexpr int kPlanThreads = 1024;
+constexpr int kPlanGroup = 32;  // threads per sequence in the planner's passes
 constexpr int kPlanBins = 2048;
 
 // one workgroup of kPlanThreads threads
@@ -26,10 +27,13 @@ __device__ void plan_block(const int64_t* __restrict__ off, int B, int tile_rows
   for (int i = tid; i < nbins; i += kPlanThreads) cnt[i] = 0;
   __syncthreads();
   // histogram of items by query-tile index (clamped into the last bin)
-  for (int b = tid; b < B; b += kPlanThreads) {
+  // kPlanGroup threads per sequence, striding over its query tiles, so that a few long
+  // sequences do not leave one thread to count all of their tiles
+  const int grp = tid / kPlanGroup, gl = tid % kPlanGroup;
+  for (int b = grp; b < B; b += kPlanThreads / kPlanGroup) {
     const int64_t n = off[b + 1] - off[b];
     const int nq = (int)((n + tile_rows - 1) / tile_rows);
-    for (int t = 0; t < nq; ++t) atomicAdd(&cnt[t < nbins ? t : nbins - 1], 1);
+    for (int t = gl; t < nq; t += kPlanGroup) atomicAdd(&cnt[t < nbins ? t : nbins - 1], 1);
   }
   __syncthreads();
   // start[t] = number of items with a larger bin (descending order), by a
@@ -57,10 +61,10 @@ __device__ void plan_block(const int64_t* __restrict__ off, int B, int tile_rows
     cnt[i] = 0;
   }
   __syncthreads();
-  for (int b = tid; b < B; b += kPlanThreads) {
+  for (int b = grp; b < B; b += kPlanThreads / kPlanGroup) {
     const int64_t n = off[b + 1] - off[b];
     const int nq = (int)((n + tile_rows - 1) / tile_rows);
-    for (int t = 0; t < nq; ++t) {
+    for (int t = gl; t < nq; t += kPlanGroup) {
       const int bin = t < nbins ? t : nbins - 1;
       const int pos = start[bin] + atomicAdd(&cnt[bin], 1);
       if (pos < n_items) items[pos] = make_int2(b, t);
