@@ -102,31 +102,36 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const bf16* __restric
     K = (int)(K - kofs < ksplit ? K - kofs : ksplit);
   }
 
-  // per-lane DMA sources of this wavefront's PERW instructions (byte offsets from the
-  // row-block base of A or W; rows past M or N repeat the last row; pad slots fetch chunk 0)
-  uint32_t soff[PERW];
+  // per-lane DMA sources of this wavefront's PERW instructions: the byte offset of the
+  // row from the row-block base of A or W (rows past M or N repeat the last row) and the
+  // byte offset of the 16-byte chunk within a stage (pad slots fetch chunk 0)
+  uint32_t soff[PERW], coff[PERW];
   bool isA[PERW];
 #pragma unroll
   for (int j = 0; j < PERW; ++j) {
     const int i = wu + 4 * j;
     const int slot = 64 * i + lane;
     const int row = slot / GSPR, pc = slot % GSPR;
-    const int c = pc < CPR ? pc : 0;
+    coff[j] = 16u * (uint32_t)(pc < CPR ? pc : 0);
     isA[j] = i < G::A_INSTR;
     if (i >= G::INSTR) {  // junk instruction: any valid A chunk
       soff[j] = 0;
       isA[j] = true;
     } else if (isA[j]) {
       const int64_t r = min(m0 + row, M - 1) - m0;
-      soff[j] = (uint32_t)(r * lda * 2 + 16 * c);
+      soff[j] = (uint32_t)(r * lda * 2);
     } else {
       const int r = min(n0 + (row - BM), N - 1) - n0;
-      soff[j] = (uint32_t)((int64_t)r * ldw * 2 + 16 * c);
+      soff[j] = (uint32_t)((int64_t)r * ldw * 2);
     }
   }
   const char* abase = (const char*)(A + m0 * lda);
   const char* wbase = (const char*)(W + (int64_t)n0 * ldw);
   const int nks = (K + GBK - 1) / GBK;
+  // byte offset of the last 16-byte chunk of a row inside K: chunks of the last stage
+  // that lie past K fetch that one instead (they are zeroed in LDS before use), so no
+  // load leaves the row
+  const uint32_t klast = (uint32_t)(K - 8) * 2u;
   auto issue = [&](auto bufc, int ks) {
     constexpr int buf = decltype(bufc)::value;
     bf16* D = buf == 0 ? S0 : buf == 1 ? S1 : buf == 2 ? S2 : S3;
@@ -134,7 +139,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const bf16* __restric
 #pragma unroll
     for (int j = 0; j < PERW; ++j) {
       const int i = wu + 4 * j;
-      const char* src = (isA[j] ? abase : wbase) + soff[j] + kb;
+      const char* src = (isA[j] ? abase : wbase) + soff[j] + min(kb + coff[j], klast);
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
                                        (__attribute__((address_space(3))) void*)(&D[512 * i]), 16,
                                        0, 0);
