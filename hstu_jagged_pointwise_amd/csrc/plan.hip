@@ -5,8 +5,10 @@
 // causal mask a query tile t needs key tiles 0..t only, so its cost grows with
 // t. Items are ordered by decreasing t (longest first), which makes the
 // dispatch order approximate longest-processing-time scheduling across the
-// compute units. The order never changes results: every item writes its own
-// output rows and no reduction crosses items.
+// compute units. Within one t the order follows LDS atomics, so it can change
+// from run to run. The forward outputs and dq, dk, dv never depend on it: every
+// item writes its own rows. The bias-table gradients do, in their last bits:
+// their per-item partial sums are added in item order.
 #include "common.h"
 #include "kernels.h"
 
@@ -17,6 +19,7 @@ namespace hstu {
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanGroup = 32;  // threads per sequence in the planner's passes
 constexpr int kPlanBins = 2048;
+constexpr int kPlanMaxRangeGroups = 8192;  // key-range workgroups along x at most
 
 // one workgroup of kPlanThreads threads
 __device__ void plan_block(const int64_t* __restrict__ off, int B, int tile_rows, int nbins,
@@ -99,8 +102,9 @@ __device__ void key_range_block(const int64_t* __restrict__ off, const int64_t* 
   }
 }
 
-// The planner (workgroup (0, 0)) and, given timestamps, the key ranges of sequence b
-// (workgroups (1 + b, y)) in one launch: they are independent and both small.
+// The planner (workgroup (0, 0)) and, given timestamps, the key ranges (workgroups
+// (1 + i, y), which take sequences i, i + gridDim.x - 1, ...) in one launch: they are
+// independent and both small.
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int64_t* __restrict__ off, int B,
                                                             int tile_rows, int nbins,
                                                             int2* __restrict__ items, int n_items,
@@ -110,7 +114,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int64_t* __res
     if (blockIdx.y == 0) plan_block(off, B, tile_rows, nbins, items, n_items);
     return;
   }
-  key_range_block(off, ts, kr, (int)blockIdx.x - 1);
+  for (int b = (int)blockIdx.x - 1; b < B; b += (int)gridDim.x - 1) key_range_block(off, ts, kr, b);
 }
 
 hipError_t launch_plan(const int64_t* offsets, int B, int tile_rows, int max_tiles, int2* items,
@@ -123,7 +127,9 @@ hipError_t launch_plan(const int64_t* offsets, int B, int tile_rows, int max_til
   const unsigned gy =
       ranges ? (unsigned)std::min<int64_t>((blocks + kPlanThreads / 32 - 1) / (kPlanThreads / 32), 64)
              : 1u;
-  const dim3 grid(1u + (ranges ? (unsigned)B : 0u), gy);
+  // key-range workgroups stride over the sequences, so any batch size fits the grid
+  const unsigned gx = ranges ? (unsigned)std::min<int64_t>(B, kPlanMaxRangeGroups) : 0u;
+  const dim3 grid(1u + gx, gy);
   hipLaunchKernelGGL(plan_kernel, grid, dim3(kPlanThreads), 0, s, offsets, B, tile_rows, nbins,
                      items, n_items, ranges ? ts : nullptr, ranges ? kr : nullptr);
   return hipGetLastError();
