@@ -610,6 +610,36 @@ __global__ __launch_bounds__(256, D <= 64 ? 3 : 2) void attn_mfma_kernel(AttnArg
     auto general_block = [&](int kb, const BlockClass& bc) {
       if (!bc.act()) return f32x16{};
       const int kb0 = k0 + 32 * kb;
+      if constexpr (CAND) {
+        // Candidate mode: each pair's whole bias, formed as the per-key path forms it
+        // (position term plus time term in fp32, split into a bf16 high and low part,
+        // whose sum is exact in fp32), starts the accumulator. A candidate's scores then
+        // round the same way whichever path its wavefront takes, so its output does not
+        // depend on which candidates share its wavefront.
+        f32x16 x;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = kb0 + 8 * (r >> 2) + 4 * hl + (r & 3);
+          float b = has_pos ? rp[max(0, min(qpos0 - j, P - 1))] : 0.f;
+          if (has_time) b += rt[bucket_of(tq - tk64[buf][j - k0], T)];
+          const bf16 bh = (bf16)b;
+          x[r] = (float)bh + (float)(bf16)(b - (float)bh);
+        }
+        bf16x8 kq[NKK];
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) kq[kk] = kfrag(Kt, kb, kk);
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk)
+          x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kq[kk], qf[kk], x, 0, 0, 0);
+        if (bc.mask()) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int keyoff = 8 * (r >> 2) + 4 * hl + (r & 3);
+            x[r] = kb0 + keyoff < kend ? x[r] : 0.f;
+          }
+        }
+        return x;
+      }
       f32x16 x = s_chain(kb, (bc.pos_c() ? pb : 0.f) + (bc.tmode() < 2 ? bc.tlo : 0.f), nullptr, false);
       // i - j = dbase - (8*(r/4) + r%4) for accumulator slot r
       const int dbase = qpos - kb0 - 4 * hl;
