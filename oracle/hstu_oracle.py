@@ -49,7 +49,8 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
-    "silu", "round_storage", "floor_log2", "pos_bucket", "time_bucket", "bias_matrix", "attention_one_head",
+    "silu", "round_storage", "floor_log2", "pos_bucket", "time_bucket", "bucket_indices",
+    "bias_from_buckets", "bias_matrix", "attention_one_head",
     "hstu_attention", "hstu_attention_rows", "layer_norm_rows", "hstu_layer", "hstu_layer_stack", "mfalcon_score",
     "mfalcon_by_definition", "candidate_attention", "attention_pairs", "attention_flops",
 ]
@@ -112,21 +113,36 @@ def time_bucket(dt, T):
     return np.minimum(floor_log2(np.maximum(dt, 0) + 1), T - 1)
 
 
+def bucket_indices(qpos, kpos, qts, kts, rab_pos, rab_time):
+    """The (position, time) bucket index matrices [nq, nk] of every query against every
+    key. They do not depend on the head. An index matrix is None where its table (or,
+    for time, the timestamps) is missing."""
+    qpos = np.asarray(qpos, dtype=np.int64)
+    kpos = np.asarray(kpos, dtype=np.int64)
+    bp = bt = None
+    if rab_pos is not None:
+        bp = pos_bucket(qpos[:, None] - kpos[None, :], rab_pos.shape[1])
+    if rab_time is not None and qts is not None and kts is not None:
+        bt = time_bucket(np.asarray(qts, np.int64)[:, None] - np.asarray(kts, np.int64)[None, :],
+                         rab_time.shape[1])
+    return bp, bt
+
+
+def bias_from_buckets(h, shape, bp, bt, rab_pos, rab_time):
+    """rab^{p,t} of head h: rab_pos[h][bp] + rab_time[h][bt], a missing term adding 0."""
+    bias = np.zeros(shape, dtype=np.float64)
+    if bp is not None:
+        bias += _f64(rab_pos)[h][bp]
+    if bt is not None:
+        bias += _f64(rab_time)[h][bt]
+    return bias
+
+
 def bias_matrix(h, qpos, kpos, qts, kts, rab_pos, rab_time):
     """rab^{p,t}[i, j] for head h, over query positions and timestamps against key
     positions and timestamps. Missing tables or timestamps add 0."""
-    qpos = np.asarray(qpos, dtype=np.int64)
-    kpos = np.asarray(kpos, dtype=np.int64)
-    bias = np.zeros((len(qpos), len(kpos)), dtype=np.float64)
-    if rab_pos is not None:
-        P = rab_pos.shape[1]
-        bp = pos_bucket(qpos[:, None] - kpos[None, :], P)
-        bias += _f64(rab_pos)[h][bp]
-    if rab_time is not None and qts is not None and kts is not None:
-        T = rab_time.shape[1]
-        bt = time_bucket(np.asarray(qts, np.int64)[:, None] - np.asarray(kts, np.int64)[None, :], T)
-        bias += _f64(rab_time)[h][bt]
-    return bias
+    bp, bt = bucket_indices(qpos, kpos, qts, kts, rab_pos, rab_time)
+    return bias_from_buckets(h, (len(qpos), len(kpos)), bp, bt, rab_pos, rab_time)
 
 
 # ---------------------------------------------------------------------------
@@ -159,8 +175,9 @@ def hstu_attention(offsets, ts, q, k, v, rab_pos, rab_time, N, u=None, gamma=Non
         pos = np.arange(n, dtype=np.int64)
         t = None if ts is None else np.asarray(ts, np.int64)[s:e]
         visible = pos[None, :] <= pos[:, None]
+        bp, bt = bucket_indices(pos, pos, t, t, rab_pos, rab_time)  # the same for every head
         for h in range(H):
-            bias = bias_matrix(h, pos, pos, t, t, rab_pos, rab_time)
+            bias = bias_from_buckets(h, (n, n), bp, bt, rab_pos, rab_time)
             out[s:e, h, :] = attention_one_head(q[s:e, h], k[s:e, h], v[s:e, h], visible, bias, N)
     if u is None:
         return out
@@ -273,9 +290,10 @@ def candidate_attention(Qc, Kc, Vc, Kh, Vh, cand_ts, hist_ts, rab_pos, rab_time,
     kpos = np.arange(nh, dtype=np.int64)
     have_t = cand_ts is not None and hist_ts is not None
     zero = np.zeros(1, np.int64)
+    bp, bt = bucket_indices(qpos, kpos, cand_ts if have_t else None, hist_ts if have_t else None,
+                            rab_pos, rab_time)  # the same for every head
     for h in range(H):
-        bias_h = bias_matrix(h, qpos, kpos, cand_ts if have_t else None,
-                             hist_ts if have_t else None, rab_pos, rab_time)
+        bias_h = bias_from_buckets(h, (nc, nh), bp, bt, rab_pos, rab_time)
         vis = np.ones((nc, nh), dtype=bool)
         o[:, h, :] = attention_one_head(Qc[:, h], Kh[:, h], Vh[:, h], vis, bias_h, N)
         self_bias = bias_matrix(h, zero, zero, zero if have_t else None,

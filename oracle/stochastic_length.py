@@ -4,10 +4,9 @@ TEST INFRASTRUCTURE ONLY: the test suite is the only user. The GPU library never
 imports, calls or falls back to it.
 
 Source: the HSTU chapter of chenhuiyu.github.io, "Three more scaling components",
-paragraph "Stochastic Length". It states that training usually samples a shorter
-subsequence from very long users and occasionally keeps the full history, and that
-with alpha = 1.6 a length of 4,096 becomes 776 most of the time. 776 is
-floor(4096 ** 0.8) = floor(4096 ** (alpha / 2)).
+paragraph "Stochastic Length". Long histories are cut to a random sub-sequence
+whose length is set by alpha, and a few are left whole; the page's worked number is
+4,096 -> 776 at alpha = 1.6, which is floor(4096 ** 0.8) = floor(4096 ** (alpha / 2)).
 
 Readings taken where the page is silent:
 
