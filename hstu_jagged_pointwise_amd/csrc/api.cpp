@@ -977,6 +977,89 @@ hstu_status layer_bwd_once(const hstu_layer_desc* d, const LayerBwdPlan& p, cons
   return HSTU_OK;
 }
 
+// ---------------------------------------------------------------- attention entry
+// Host-only checks of an hstu_attn_fwd call (nothing is launched), then the launches.
+hstu_status check_attn_fwd(const hstu_attn_desc* desc, const int64_t* off_host,
+                           const int64_t* seq_offsets, const void* q, const void* k,
+                           const void* v, const void* u, const void* out, AttnPlan* p) {
+  hstu_status st = plan_attn(desc, off_host, u != nullptr, p);
+  if (st) return st;
+  if (u && (st = check_eps(desc->ln_eps))) return st;
+  if (p->j.total == 0) return HSTU_OK;
+  if (!seq_offsets) return fail(HSTU_INVALID_ARGUMENT, "device seq_offsets is NULL");
+  if (!q || !k || !v || !out) return fail(HSTU_INVALID_ARGUMENT, "q, k, v and out are required");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || (u && !aligned16(u)))
+    return fail(HSTU_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
+  return HSTU_OK;
+}
+
+hstu_status enqueue_attn_fwd(const hstu_attn_desc* desc, const AttnPlan& p,
+                             const int64_t* seq_offsets, const int64_t* timestamps, const void* q,
+                             const void* k, const void* v, const float* rab_pos,
+                             const float* rab_time, const void* u, const float* ln_gamma,
+                             const float* ln_beta, void* out, void* workspace, hipStream_t s) {
+  Carver c{(char*)workspace};
+  int2* items = (int2*)c.take((size_t)p.j.items * sizeof(int2));
+  KeyRange* kr = (KeyRange*)c.take(key_range_bytes(desc, p.j.total));
+  float* o32 = u ? (float*)c.take((size_t)p.j.total * desc->num_heads * desc->d_v * 4) : nullptr;
+  const bool timed = rab_time && timestamps && kr;
+  HSTU_TRY(launch_plan(seq_offsets, desc->batch, attn_tile_rows(desc), p.j.max_tiles, items,
+                       (int)p.j.items, timed ? timestamps : nullptr, p.j.max_len, kr, s),
+           "tile planner and key ranges");
+  AttnArgs a = base_args(desc);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.ld_q = a.ld_k = (int64_t)desc->num_heads * desc->d_qk;
+  a.ld_v = (int64_t)desc->num_heads * desc->d_v;
+  a.out = u ? (void*)o32 : out;
+  a.ld_o = (int64_t)desc->num_heads * desc->d_v;
+  a.out_f32 = u ? 1 : (desc->dtype == HSTU_F32);
+  a.q_offsets = a.k_offsets = seq_offsets;
+  a.ts_q = a.ts_k = timestamps;
+  a.rab_pos = rab_pos;
+  a.rab_time = rab_time;
+  a.key_ranges = timed ? kr : nullptr;
+  a.items = items;
+  a.n_items = (int)p.j.items;
+  HSTU_TRY(run_attention(desc, a, false, s), "attention");
+  if (u) {
+    const int hv = desc->num_heads * desc->d_v;
+    HSTU_TRY(launch_ln_gate(o32, hv, 1, 0, u, hv, ln_gamma, ln_beta, desc->ln_eps, out, hv,
+                            p.j.total, hv, desc->dtype == HSTU_BF16, s),
+             "layer norm gate");
+  }
+  return HSTU_OK;
+}
+
+// ---------------------------------------------------------------- allocation-free scratch
+// The scratch of hstu_attn_fwd_noalloc: a file-scope device array. Every device the
+// library runs on holds its own copy until the process ends. Host code never passes the
+// array's name to a kernel or a copy (on the host that name is a stand-in, not a device
+// address): the device address comes from hipGetSymbolAddress, taken once per device
+// with that device current, and kept below.
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+hstu_status noalloc_scratch(void** out) {
+  int dev = 0;
+  HSTU_TRY(hipGetDevice(&dev), "current device");
+  if (dev < 0 || dev >= kMaxDevices) return fail(HSTU_UNSUPPORTED, "device index %d", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    HSTU_TRY(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)), "scratch address");
+    if (!ptr || ((uintptr_t)ptr & (kAlign - 1)) != 0)
+      return fail(HSTU_DEVICE_ERROR, "scratch address is NULL or not 256-byte aligned");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return HSTU_OK;
+}
+
 }  // namespace
 
 // =========================================================================
@@ -1014,52 +1097,37 @@ hstu_status hstu_attn_fwd(const hstu_attn_desc* desc, const int64_t* seq_offsets
                           const float* ln_beta, void* out, void* workspace,
                           size_t workspace_bytes, void* stream) {
   AttnPlan p;
-  hstu_status st = plan_attn(desc, seq_offsets_host, u != nullptr, &p);
-  if (st) return st;
-  if (u && (st = check_eps(desc->ln_eps))) return st;
-  if (p.j.total == 0) return HSTU_OK;
-  if (!seq_offsets) return fail(HSTU_INVALID_ARGUMENT, "device seq_offsets is NULL");
-  if (!q || !k || !v || !out) return fail(HSTU_INVALID_ARGUMENT, "q, k, v and out are required");
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || (u && !aligned16(u)))
-    return fail(HSTU_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
+  hstu_status st = check_attn_fwd(desc, seq_offsets_host, seq_offsets, q, k, v, u, out, &p);
+  if (st || p.j.total == 0) return st;
   if (workspace_bytes < p.ws || (!workspace && p.ws))
     return fail(HSTU_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes (got %zu)", p.ws,
                 workspace_bytes);
   if (((uintptr_t)workspace & (kAlign - 1)) != 0)
     return fail(HSTU_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
-  hipStream_t s = (hipStream_t)stream;
-  Carver c{(char*)workspace};
-  int2* items = (int2*)c.take((size_t)p.j.items * sizeof(int2));
-  KeyRange* kr = (KeyRange*)c.take(key_range_bytes(desc, p.j.total));
-  float* o32 = u ? (float*)c.take((size_t)p.j.total * desc->num_heads * desc->d_v * 4) : nullptr;
-  const bool timed = rab_time && timestamps && kr;
-  HSTU_TRY(launch_plan(seq_offsets, desc->batch, attn_tile_rows(desc), p.j.max_tiles, items,
-                       (int)p.j.items, timed ? timestamps : nullptr, p.j.max_len, kr, s),
-           "tile planner and key ranges");
-  AttnArgs a = base_args(desc);
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.ld_q = a.ld_k = (int64_t)desc->num_heads * desc->d_qk;
-  a.ld_v = (int64_t)desc->num_heads * desc->d_v;
-  a.out = u ? (void*)o32 : out;
-  a.ld_o = (int64_t)desc->num_heads * desc->d_v;
-  a.out_f32 = u ? 1 : (desc->dtype == HSTU_F32);
-  a.q_offsets = a.k_offsets = seq_offsets;
-  a.ts_q = a.ts_k = timestamps;
-  a.rab_pos = rab_pos;
-  a.rab_time = rab_time;
-  a.key_ranges = timed ? kr : nullptr;
-  a.items = items;
-  a.n_items = (int)p.j.items;
-  HSTU_TRY(run_attention(desc, a, false, s), "attention");
-  if (u) {
-    const int hv = desc->num_heads * desc->d_v;
-    HSTU_TRY(launch_ln_gate(o32, hv, 1, 0, u, hv, ln_gamma, ln_beta, desc->ln_eps, out, hv,
-                            p.j.total, hv, desc->dtype == HSTU_BF16, s),
-             "layer norm gate");
-  }
-  return HSTU_OK;
+  return enqueue_attn_fwd(desc, p, seq_offsets, timestamps, q, k, v, rab_pos, rab_time, u,
+                          ln_gamma, ln_beta, out, workspace, (hipStream_t)stream);
+}
+
+size_t hstu_attn_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
+
+hstu_status hstu_attn_fwd_noalloc(const hstu_attn_desc* desc, const int64_t* seq_offsets_host,
+                                  const int64_t* seq_offsets, const int64_t* timestamps,
+                                  const void* q, const void* k, const void* v,
+                                  const float* rab_pos, const float* rab_time, const void* u,
+                                  const float* ln_gamma, const float* ln_beta, void* out,
+                                  void* stream) {
+  AttnPlan p;
+  hstu_status st = check_attn_fwd(desc, seq_offsets_host, seq_offsets, q, k, v, u, out, &p);
+  if (st || p.j.total == 0) return st;
+  if (p.ws > kNoAllocScratchBytes)
+    return fail(HSTU_UNSUPPORTED,
+                "this call needs %zu bytes of scratch; the allocation-free entry point has %zu "
+                "(use hstu_attn_fwd with a workspace)",
+                p.ws, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  if ((st = noalloc_scratch(&ws))) return st;
+  return enqueue_attn_fwd(desc, p, seq_offsets, timestamps, q, k, v, rab_pos, rab_time, u,
+                          ln_gamma, ln_beta, out, ws, (hipStream_t)stream);
 }
 
 hstu_status hstu_layer_workspace_size(const hstu_layer_desc* desc,

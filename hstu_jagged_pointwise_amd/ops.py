@@ -72,6 +72,9 @@ _sig = {
     "hstu_attn_workspace_size": ([ctypes.POINTER(hstu_attn_desc), _I64P, _SZP], ctypes.c_int),
     "hstu_attn_fwd": ([ctypes.POINTER(hstu_attn_desc), _I64P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                        _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "hstu_attn_noalloc_scratch_bytes": ([], ctypes.c_size_t),
+    "hstu_attn_fwd_noalloc": ([ctypes.POINTER(hstu_attn_desc), _I64P, _P, _P, _P, _P, _P, _P, _P,
+                               _P, _P, _P, _P, _P], ctypes.c_int),
     "hstu_layer_workspace_size": ([ctypes.POINTER(hstu_layer_desc), _I64P, _SZP], ctypes.c_int),
     "hstu_layer_fwd": ([ctypes.POINTER(hstu_layer_desc), _I64P, _P, _P, _P,
                         ctypes.POINTER(hstu_layer_weights), _P, _P, ctypes.c_size_t, _P],
@@ -210,6 +213,28 @@ def hstu_attn_fwd(seq_offsets: torch.Tensor, timestamps: Optional[torch.Tensor],
                              _ptr(q), _ptr(k), _ptr(v), _ptr(rab_pos), _ptr(rab_time), _ptr(u),
                              _ptr(ln_gamma), _ptr(ln_beta), _ptr(out), _ptr(ws), nbytes,
                              _stream(stream)))
+    return out
+
+
+def hstu_attn_fwd_noalloc(seq_offsets: torch.Tensor, timestamps: Optional[torch.Tensor], q, k,
+                          v, rab_pos=None, rab_time=None, *, max_seq_len: int,
+                          num_pos_buckets=None, num_time_buckets=None, u=None, ln_gamma=None,
+                          ln_beta=None, ln_eps=1e-5, out=None, seq_offsets_host=None,
+                          stream=None) -> torch.Tensor:
+    """hstu_attn_fwd with the library's own device scratch instead of a workspace (nothing
+    is allocated by the call; `out` may be passed in to allocate nothing here either)."""
+    host = _host_offsets(seq_offsets, seq_offsets_host)
+    T_tot, H, d_qk = q.shape
+    d_v = v.shape[2]
+    P = rab_pos.shape[1] if rab_pos is not None else (num_pos_buckets or 1)
+    T = rab_time.shape[1] if rab_time is not None else (num_time_buckets or 1)
+    desc = attn_desc(len(host) - 1, H, d_qk, d_v, max_seq_len, P, T, _dtype_code(q), ln_eps)
+    if out is None:
+        out = torch.empty((T_tot, H, d_v), dtype=q.dtype, device=q.device)
+    _check(lib.hstu_attn_fwd_noalloc(ctypes.byref(desc), _i64p(host), _ptr(seq_offsets),
+                                     _ptr(timestamps), _ptr(q), _ptr(k), _ptr(v), _ptr(rab_pos),
+                                     _ptr(rab_time), _ptr(u), _ptr(ln_gamma), _ptr(ln_beta),
+                                     _ptr(out), _stream(stream)))
     return out
 
 

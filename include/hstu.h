@@ -22,7 +22,9 @@
  *   pointer after it returns. It needs scratch device memory only through the
  *   caller's `workspace` (256-byte aligned, at least the size that the
  *   matching *_workspace_size call reports). The caller keeps the workspace
- *   alive until the stream has passed the call.
+ *   alive until the stream has passed the call. The one exception is
+ *   hstu_attn_fwd_noalloc, whose scratch is a fixed device array inside the
+ *   library.
  * Streams.  `stream` is a hipStream_t (NULL for the null stream). Every call
  *   only enqueues work on it and never synchronises the device. HSTU_OK means
  *   "validated and enqueued".
@@ -143,6 +145,31 @@ hstu_status hstu_attn_fwd(const hstu_attn_desc* desc, const int64_t* seq_offsets
                           const float* rab_time, const void* u, const float* ln_gamma,
                           const float* ln_beta, void* out, void* workspace,
                           size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * hstu_attn_fwd_noalloc: hstu_attn_fwd without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation). It runs the same
+ * kernels and returns the same results bit for bit. Arguments are those of
+ * hstu_attn_fwd minus workspace and workspace_bytes.
+ * Its scratch is a device array inside the library, of
+ * hstu_attn_noalloc_scratch_bytes() bytes (64 MiB): every device that the
+ * library runs on holds one copy until the process ends. The call allocates
+ * nothing (no hipMalloc, no hipFree, no allocating library routine); its first
+ * call on a device looks up that device's copy once. A call whose scratch need
+ * (hstu_attn_workspace_size) exceeds the array returns HSTU_UNSUPPORTED before
+ * anything is launched. All calls on one device share its array, so calls
+ * that overlap on one device (several streams or host threads) race: order
+ * them on one stream. Nothing in the scratch needs to start at zero; each call
+ * rewrites what it reads.
+ * ---------------------------------------------------------------------- */
+size_t hstu_attn_noalloc_scratch_bytes(void);
+hstu_status hstu_attn_fwd_noalloc(const hstu_attn_desc* desc, const int64_t* seq_offsets_host,
+                                  const int64_t* seq_offsets, const int64_t* timestamps,
+                                  const void* q, const void* k, const void* v,
+                                  const float* rab_pos, const float* rab_time, const void* u,
+                                  const float* ln_gamma, const float* ln_beta, void* out,
+                                  void* stream);
 
 /* ------------------------------------------------------------------------
  * hstu_layer_fwd: num_layers HSTU layers over a jagged batch (eqs. 1-3):

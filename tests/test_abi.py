@@ -96,6 +96,44 @@ def test_empty_batches_are_noops(ops):
     assert _attn(ops, _desc(ops), np.zeros(3, np.int64), q=None, k=None, v=None, out=None) == 0
 
 
+def _attn_noalloc(ops, desc, off, q=FAKE, k=FAKE, v=FAKE, u=None, out=FAKE):
+    return ops.lib.hstu_attn_fwd_noalloc(ctypes.byref(desc) if desc is not None else None,
+                                         off.ctypes.data_as(ops._I64P) if off is not None else None,
+                                         FAKE, None, q, k, v, None, None, u, None, None, out, None)
+
+
+def test_noalloc_rejections(ops):
+    """The allocation-free attention call validates like hstu_attn_fwd and rejects a call
+    whose scratch need exceeds its fixed device array, all before any HIP call."""
+    cap = ops.lib.hstu_attn_noalloc_scratch_bytes()
+    assert cap == 64 << 20
+    d = _desc(ops)
+    assert _attn_noalloc(ops, None, GOOD_OFF) == 1
+    assert _attn_noalloc(ops, d, None) == 1
+    assert _attn_noalloc(ops, d, GOOD_OFF, q=None) == 1
+    assert _attn_noalloc(ops, d, GOOD_OFF, out=ctypes.c_void_p(0x10008)) == 1
+    assert _attn_noalloc(ops, _desc(ops, ln_eps=0.0), GOOD_OFF, u=FAKE) == 1
+    assert _attn_noalloc(ops, _desc(ops, batch=0), np.zeros(1, np.int64), q=None, k=None,
+                         v=None, out=None) == 0
+    # a gated call needs 4 * H * d_v bytes of fp32 rows per token: find the first batch
+    # that does not fit (one sequence per 4096 rows) and check both sides of the limit
+    dd = dict(num_heads=8, d_qk=64, d_v=64, max_seq_len=4096)
+    def need(rows):
+        off = np.arange(0, rows + 1, 4096, dtype=np.int64)
+        if off[-1] != rows:
+            off = np.append(off, rows)
+        return off, ops.hstu_attn_workspace_size(_desc(ops, batch=len(off) - 1, **dd), off)
+    lo, hi = 4096, 1 << 20
+    while hi - lo > 1:
+        mid = (lo + hi) // 2
+        lo, hi = (mid, hi) if need(mid)[1] <= cap else (lo, mid)
+    off_ok, n_ok = need(lo)
+    off_big, n_big = need(hi)
+    assert n_ok <= cap < n_big
+    assert _attn_noalloc(ops, _desc(ops, batch=len(off_big) - 1, **dd), off_big, u=FAKE) == 2
+    assert "scratch" in ops.lib.hstu_last_error().decode()
+
+
 def test_workspace_sizes(ops):
     d = _desc(ops, batch=4, max_seq_len=300)  # bf16, d=64: 128-row tiles
     off = np.array([0, 300, 301, 301, 500], np.int64)
