@@ -10,6 +10,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstring>
 #include <mutex>
 #include <string>
 #include <utility>
@@ -104,8 +105,13 @@ hstu_status check_attn_desc(const hstu_attn_desc* d) {
   if (d->max_seq_len < 1) return fail(HSTU_INVALID_ARGUMENT, "max_seq_len (N) must be >= 1");
   if (d->num_pos_buckets < 1 || d->num_time_buckets < 1)
     return fail(HSTU_INVALID_ARGUMENT, "bucket counts must be >= 1");
-  if (d->dtype != HSTU_F32 && d->dtype != HSTU_BF16)
-    return fail(HSTU_UNSUPPORTED, "dtype must be HSTU_F32 or HSTU_BF16");
+  // a C caller may store any int in the enum field; read it as its bytes, since loading an
+  // out-of-range value as the enum type is undefined in C++
+  int32_t dtype_raw;
+  static_assert(sizeof(dtype_raw) == sizeof(d->dtype), "hstu_dtype is a 32-bit field");
+  std::memcpy(&dtype_raw, &d->dtype, sizeof(dtype_raw));
+  if (dtype_raw != HSTU_F32 && dtype_raw != HSTU_BF16)
+    return fail(HSTU_UNSUPPORTED, "dtype must be HSTU_F32 or HSTU_BF16 (got %d)", dtype_raw);
   return HSTU_OK;
 }
 

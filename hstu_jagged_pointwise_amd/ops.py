@@ -17,7 +17,9 @@ import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libhstu.so")
+# HSTU_LIB selects another build of the same library (the host-sanitizer build that the
+# CPU tests use); by default the in-tree libhstu.so
+LIB_PATH = os.environ.get("HSTU_LIB") or os.path.join(_HERE, "libhstu.so")
 
 HSTU_OK, HSTU_INVALID_ARGUMENT, HSTU_UNSUPPORTED, HSTU_WORKSPACE_TOO_SMALL, HSTU_DEVICE_ERROR = range(5)
 HSTU_F32, HSTU_BF16 = 0, 1
