@@ -38,18 +38,46 @@ def row_errors(g, o):
     return num, den
 
 
+def record(what, msg):
+    """One line per checked output for the run's log: what was compared and how closely."""
+    print(f"[parity] {what}: {msg}", flush=True)
+
+
 def assert_rows_close(g, o, tol, what=""):
-    """Relative error per row (infinity norm) <= tol. Where the oracle row is exactly zero,
-    the GPU row must be exactly zero too."""
+    """Relative error per row (infinity norm) <= tol on every row. Where the oracle row is
+    exactly zero, the GPU row must be exactly zero too."""
     assert np.all(np.isfinite(g)), f"{what}: non-finite output"
     num, den = row_errors(g, o)
     zero = den == 0
     assert np.all(num[zero] == 0), f"{what}: rows that must be zero are not"
     rel = num[~zero] / den[~zero]
     worst = float(rel.max()) if rel.size else 0.0
-    assert worst <= tol, f"{what}: worst row error {worst:.3e} > {tol:.1e} (p99 " \
-                         f"{float(np.quantile(rel, 0.99)) if rel.size else 0:.3e})"
+    p99 = float(np.quantile(rel, 0.99)) if rel.size else 0.0
+    record(what, f"{len(num)} rows, flat tol {tol:.0e}: worst {worst:.3e}, p99 {p99:.3e}")
+    assert worst <= tol, f"{what}: worst row error {worst:.3e} > {tol:.1e} (p99 {p99:.3e})"
     return worst
+
+
+RANGE_FLOOR = 2.0 ** -100  # below this, a layer's fp32 products fall under fp32's normal range
+
+
+def assert_rows_close_in_range(g, o, tol, what=""):
+    """assert_rows_close on every row whose oracle values lie inside fp32's working range.
+    A row whose largest oracle value is below RANGE_FLOOR (~7.9e-31) comes out of sums of
+    products below 2^-126, which fp32 arithmetic flushes to zero or resolves only
+    coarsely: such rows are counted and reported, and must be finite and no larger than
+    RANGE_FLOOR on the GPU as well."""
+    assert np.all(np.isfinite(g)), f"{what}: non-finite output"
+    g = np.asarray(g, np.float64).reshape(len(g), -1)
+    o = np.asarray(o, np.float64).reshape(len(o), -1)
+    tiny = np.abs(o).max(axis=1) < RANGE_FLOOR
+    if tiny.any():
+        record(what, f"{int(tiny.sum())} of {len(o)} rows below fp32 working range "
+                     f"(oracle row max < 2^-100); GPU max there {np.abs(g[tiny]).max():.3e}")
+        assert np.abs(g[tiny]).max() <= RANGE_FLOOR, f"{what}: out-of-range rows are not tiny"
+    if (~tiny).any():
+        return assert_rows_close(g[~tiny], o[~tiny], tol, what)
+    return 0.0
 
 
 def attn_on_gpu(x, with_u=False, out_dtype=None, rab_pos="x", rab_time="x", ts="x", q=None):
@@ -100,6 +128,9 @@ def assert_sums_close(g, o, o_storage, terms, tol, k=4.0, what=""):
     row = np.maximum(tol * np.abs(o).max(axis=1), k * np.abs(s - o).max(axis=1))[:, None]
     bound = np.maximum(np.maximum(row, tol * t), FP32_TINY)
     bad = err > bound
+    flat_ok = err <= tol * np.abs(o).max(axis=1)[:, None]
+    record(what, f"{err.size} entries: {int((~flat_ok).sum())} above the flat row bound, decided "
+                 f"by the storage, sum-of-terms or fp32-range terms")
     assert not bad.any(), f"{what}: {int(bad.sum())} entries outside the bound; worst excess " \
                           f"{float((err / np.maximum(bound, 1e-300)).max()):.3f}"
     return float((err / np.maximum(np.maximum(np.abs(o).max(axis=1)[:, None], t), 1e-300)).max())
@@ -120,9 +151,19 @@ def assert_rows_close_storage(g, o, o_storage, tol, k=4.0, what=""):
     sens = np.abs(s - o).max(axis=1)
     bound = np.maximum(tol * den, k * sens)
     bad = num > bound
+    live = den > 0
+    flat = num[live] / den[live]
+    over = flat > tol  # rows that the flat tolerance alone would fail: decided by the storage term
+    msg = f"{int(live.sum())} rows: flat worst {float(flat.max()) if flat.size else 0:.3e}, " \
+          f"{int(over.sum())} rows above flat {tol:.0e}"
+    if over.any():
+        idx = np.flatnonzero(live)[over]
+        msg += f" (rows {idx[:8].tolist()}{'...' if len(idx) > 8 else ''}), each within " \
+               f"{k:g}x its storage-only deviation (which is >= " \
+               f"{float((sens[live][over] / den[live][over]).min()):.3e} on those rows)"
+    record(what, msg)
     assert not bad.any(), f"{what}: {int(bad.sum())} rows outside the bound; worst excess " \
                           f"{float((num / np.maximum(bound, 1e-300)).max()):.3f}"
-    live = den > 0
     med = float(np.median(num[live] / den[live])) if live.any() else 0.0
     assert med <= tol, f"{what}: median row error {med:.3e} > {tol}"
     return float((num[live] / den[live]).max()) if live.any() else 0.0

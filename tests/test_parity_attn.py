@@ -111,21 +111,12 @@ def test_large_position_table_falls_back_to_vector_kernel():
     assert_rows_close(to_np(attn_on_gpu(x)), _oracle(x), TOL["bf16"], "P=2048")
 
 
-def test_long_sequence_workload_sampled_rows():
-    """The length-8192 workload (B=8, H=4, d=128) in the launch configuration the benchmark
-    times, checked on sampled rows that the oracle computes one by one."""
+def test_long_sequence_workload_every_row():
+    """The length-8192 workload (B=8, H=4, d=128, 46,858 rows) in the launch configuration
+    the benchmark times: every row of every head within a flat 2e-2 of the fp64 oracle."""
     x = synth.workload_long_attention()
     announce(f"long attention, T_tot={int(x.offsets[-1])}")
-    g = attn_on_gpu(x)
-    gn = g.float()
-    assert bool(gn.isfinite().all())
-    rng = np.random.default_rng(0)
-    rows = set()
-    for b in range(len(x.offsets) - 1):
-        s, e = int(x.offsets[b]), int(x.offsets[b + 1])
-        rows |= {s, s + 1, s + 127, s + 128, e - 1, e - 2}
-        rows |= set(int(r) for r in rng.integers(s, e, size=3))
-    rows = np.array(sorted(rows))
-    want = O.hstu_attention_rows(x.offsets, x.ts, x.q, x.k, x.v, x.rab_pos, x.rab_time,
-                                 x.max_seq_len, rows)
-    assert_rows_close(to_np(gn[rows]), want, TOL["bf16"], "length 8192 sampled rows")
+    g = to_np(attn_on_gpu(x))
+    d = x.d_v
+    assert_rows_close(g.reshape(-1, d), _oracle(x).reshape(-1, d), TOL["bf16"],
+                      "length 8192, every (row, head)")

@@ -1,18 +1,29 @@
 """GPU parity of hstu_layer_fwd (eqs. 1-3, one layer or a stack) against the fp64 oracle.
 
-fp32: every row within 1e-5 (infinity norm, relative). bf16 with fp32 accumulation:
-every row within max(2e-2 |o|, 4 |o_s - o|), where o_s is the oracle with bf16
-storage of U, V, Q, K, G and Y. Deep random-init stacks without a residual are
-ill-conditioned: bf16 storage alone moves some rows by up to 100%. The median
-row must still be within 2e-2."""
+fp32: every row of the stack's output within 1e-5 (infinity norm, relative).
+
+bf16 with fp32 accumulation (bf16 inputs, weights and stored activations):
+* Each layer on its own: the GPU runs the stack one layer per call, each layer fed the
+  GPU's own bf16 output of the layer before, and every row of every layer must be within
+  a flat 2e-2 of the oracle applied to that same bf16 input. The one-call stack must equal
+  that chain bit for bit, so the check covers the stack call itself.
+* The whole stack against the fp64 oracle from the original input: a flat 2e-2 on every
+  row for one layer and for stacks with a residual. Deep random-init stacks without a
+  residual amplify every rounding layer after layer (storing the activations in bf16 moves
+  the oracle's own output of a 3-layer stack by up to 3.9e-2), so there the bound is
+  max(2e-2 |o|, 4 |o_s - o|) with o_s the oracle with bf16 storage, and the rows that the
+  second term decides are counted in the run's log.
+"""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
 
 from oracle import hstu_oracle as O
 from hstu_jagged_pointwise_amd import synth
-from gpu_util import (announce, assert_rows_close, assert_rows_close_storage, dev, act_dtype,
-                      layer_weights_on_gpu, to_np)
+from gpu_util import (announce, assert_rows_close, assert_rows_close_in_range,
+                      assert_rows_close_storage, dev, act_dtype, layer_weights_on_gpu, to_np)
 
 pytestmark = pytest.mark.gpu
 TOL = {"f32": 1e-5, "bf16": 2e-2}
@@ -34,12 +45,39 @@ def layer_oracle(x, storage=None):
                               x.max_seq_len, x.eps, x.residual, storage)
 
 
-def check_layer(x, what):
+def layer_chain_on_gpu(x):
+    """The stack one layer per call: returns each layer's (bf16) input and output."""
+    ins, outs = [], []
+    cur = np.asarray(x.x, np.float32)
+    for w in x.layers:
+        y = layer_on_gpu(dataclasses.replace(x, x=cur, layers=[w]))
+        ins.append(cur)
+        outs.append(y)
+        cur = y.astype(np.float32)  # bf16 values, exact in fp32
+    return ins, outs
+
+
+def check_each_layer(x, g_stack, what):
+    """Every layer against the oracle on the GPU's own bf16 input of that layer."""
+    ins, outs = layer_chain_on_gpu(x)
+    assert np.array_equal(outs[-1], g_stack), f"{what}: stack call != one-layer chain"
+    for l, w in enumerate(x.layers):
+        o = O.hstu_layer(x.offsets, x.ts, ins[l], w, x.num_heads, x.d_qk, x.d_v, x.max_seq_len,
+                         x.eps, x.residual)
+        assert_rows_close_in_range(outs[l], o, TOL["bf16"], f"{what} layer {l} (own input)")
+
+
+def check_layer(x, what, end_to_end=True):
     g = layer_on_gpu(x)
     if x.dtype == "f32":
         return assert_rows_close(g, layer_oracle(x), TOL["f32"], what)
+    check_each_layer(x, g, what)
+    if not end_to_end:
+        return None
+    if len(x.layers) == 1 or x.residual:
+        return assert_rows_close(g, layer_oracle(x), TOL["bf16"], f"{what} end to end")
     return assert_rows_close_storage(g, layer_oracle(x), layer_oracle(x, "bf16"), TOL["bf16"],
-                                     what=what)
+                                     what=f"{what} end to end")
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
@@ -50,7 +88,7 @@ def test_small_layer_stack(dt, residual, num_layers):
                          96, 32, 16, dt, num_layers=num_layers, w_std=0.1, random_bias=True,
                          with_ln_affine=True, residual=residual)
     announce(f"layer stack {dt} L={num_layers} residual={residual}")
-    check_layer(x, f"layer {dt} L={num_layers}")
+    check_layer(x, f"layer {dt} L={num_layers} res={residual}")
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
@@ -62,14 +100,30 @@ def test_layer_other_widths(dt):
 
 
 def test_short_history_workload_full():
-    """B=256 short histories (lengths 20..200), H=2, d=64, d_model=128, bf16: every row."""
+    """B=256 short histories (lengths 20..200), H=2, d=64, d_model=128, bf16: every row
+    within a flat 2e-2 of the fp64 oracle."""
     x = synth.workload_short_history_layer()
     announce(f"short-history layer, T_tot={int(x.offsets[-1])}")
     check_layer(x, "short-history layer")
 
 
 def test_heavy_tail_four_layer_stack_full():
-    """B=32 power-law lengths (64..4096), d_model 512, H=8, d=64, 4 layers, bf16: every row."""
+    """B=32 power-law lengths (64..4096), d_model 512, H=8, d=64, 4 layers, bf16, no
+    residual: every row of every layer within a flat 2e-2 of the oracle on the GPU's own
+    input. The random-init stack shrinks its activations layer after layer (row maxima
+    about 1e-1, 1e-6, 1e-16, then 1e-36); the last layer's rows lie below fp32's working
+    range and are counted, not compared (see assert_rows_close_in_range). No end-to-end
+    comparison: from the original input, bf16 storage alone moves the oracle's last-layer
+    rows by 100%."""
     x = synth.workload_heavy_tail_stack()
     announce(f"heavy-tail 4-layer stack, T_tot={int(x.offsets[-1])}")
-    check_layer(x, "4-layer stack")
+    check_layer(x, "4-layer stack", end_to_end=False)
+
+
+def test_heavy_tail_four_layer_stack_residual_full():
+    """The heavy-tailed 4-layer stack with the residual on (well conditioned: activations
+    stay O(1)): every row of every layer on its own input, and every row of the stack's
+    output against the fp64 oracle from the original input, within a flat 2e-2."""
+    x = dataclasses.replace(synth.workload_heavy_tail_stack(), residual=1)
+    announce(f"heavy-tail 4-layer stack with residual, T_tot={int(x.offsets[-1])}")
+    check_layer(x, "4-layer stack, residual")
