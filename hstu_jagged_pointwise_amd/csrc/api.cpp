@@ -246,7 +246,13 @@ struct LayerBufs {
   float* o;
   void* g;
   void* tmp;
+  // bf16 MFMA path: the lo parts of the f1 output's Q and K columns (same layout as uvqk),
+  // so that the causal attention forms its scores from ~16-bit Q and K; NULL otherwise
+  void* qk_lo;
 };
+
+// Whether a layer's causal attention takes split (hi + lo) Q and K: the bf16 MFMA kernel.
+bool layer_splits_qk(const hstu_attn_desc& a) { return uses_mfma(&a); }
 
 void carve_layer(Carver& c, const hstu_layer_desc* d, int64_t rows, int64_t items, LayerBufs* b) {
   const hstu_attn_desc& a = d->attn;
@@ -259,6 +265,7 @@ void carve_layer(Carver& c, const hstu_layer_desc* d, int64_t rows, int64_t item
   b->o = (float*)c.take((size_t)rows * hv * sizeof(float));
   b->g = c.take((size_t)rows * hv * es);
   b->tmp = d->num_layers > 1 ? c.take((size_t)rows * d->d_model * es) : nullptr;
+  b->qk_lo = layer_splits_qk(a) ? c.take((size_t)rows * f1 * es) : nullptr;
 }
 
 hstu_status plan_layer(const hstu_layer_desc* d, const int64_t* off_host, LayerPlan* p) {
@@ -312,8 +319,9 @@ hstu_status layer_once(const hstu_layer_desc* d, const int64_t* off_dev, const i
   const int64_t rows = j.total;
   const int64_t f1 = 2LL * a.num_heads * (a.d_v + a.d_qk);
   const int hv = a.num_heads * a.d_v;
+  void* lo = f1_only ? nullptr : b.qk_lo;
   HSTU_TRY(launch_gemm(x, d->d_model, w.w1, d->d_model, w.b1, nullptr, 0, b.uvqk, f1, rows, (int)f1,
-                       d->d_model, 1, bf, s),
+                       d->d_model, 1, bf, s, lo, 2 * hv),
            "f1 projection");
   if (f1_only) return HSTU_OK;
   const UVQK vw = split_view(b.uvqk, a);
@@ -321,6 +329,11 @@ hstu_status layer_once(const hstu_layer_desc* d, const int64_t* off_dev, const i
   aa.q = vw.q;
   aa.k = vw.k;
   aa.v = vw.v;
+  if (lo) {
+    const UVQK lw = split_view(lo, a);
+    aa.q_lo = lw.q;
+    aa.k_lo = lw.k;
+  }
   aa.ld_q = aa.ld_k = aa.ld_v = vw.ld;
   aa.out = b.o;
   aa.ld_o = hv;
@@ -359,7 +372,7 @@ struct MfPlan {
   size_t cand_ws = 0;         // candidate-pass workspace
 };
 
-constexpr int64_t kKeysPerSplit = 1024;  // history keys per candidate-attention workgroup
+constexpr int64_t kKeysPerSplit = 2048;  // history keys per candidate-attention workgroup
 constexpr int kMaxSplits = 16;
 
 struct MfCache {
@@ -371,6 +384,7 @@ struct MfHistBufs {
   float* o;
   void* g;
   void* hx[2];
+  void* qk_lo;  // lo parts of Q and K for the history's full layers (0..L-2)
 };
 struct MfCandBufs {
   void* c_uvqk;
@@ -401,67 +415,36 @@ void carve_hist_ws(Carver& c, const mfalcon_desc* d, const MfPlan& p, MfHistBufs
   b->g = c.take((size_t)nh * hv * es);
   b->hx[0] = ld.num_layers > 1 ? c.take((size_t)nh * ld.d_model * es) : nullptr;
   b->hx[1] = ld.num_layers > 2 ? c.take((size_t)nh * ld.d_model * es) : nullptr;
+  const int64_t f1 = 2LL * a.num_heads * (a.d_v + a.d_qk);
+  b->qk_lo = ld.num_layers > 1 && layer_splits_qk(a) ? c.take((size_t)nh * f1 * es) : nullptr;
 }
 
-// Streams (and buffer sets) of the candidate pass: microbatches are dealt round robin
-// to kCandStreams streams when there is more than one microbatch, else one set runs on
-// the caller's stream. Four is the number of hardware queues HIP opens per device by
-// default, so the four streams run side by side.
-constexpr int kCandStreams = 4;
-int cand_sets(const mfalcon_desc* d, const MfPlan& p) {
-  const int64_t nmb = (p.cand_total + d->microbatch - 1) / d->microbatch;
-  return nmb > 1 ? kCandStreams : 1;
+// The candidate pass keeps up to kInFlight microbatches in flight: their work is
+// issued together, one launch per step for all of them (the rows of one group of up to
+// kInFlight microbatches, in global candidate order), on the caller's stream. Each
+// microbatch's candidates are computed exactly as they would be alone (every output
+// row has its own fixed reduction order), so the grouping only sets how much work one
+// launch holds: a group fills the device where one microbatch of ~1k candidates would
+// leave most of it idle. The working set is that of kInFlight microbatches.
+constexpr int kInFlight = 4;
+int64_t group_rows(const mfalcon_desc* d, const MfPlan& p) {
+  const int64_t g = (int64_t)d->microbatch * kInFlight;
+  return std::max<int64_t>(1, std::min<int64_t>(g, p.cand_total));
 }
 
-void carve_cand_ws(Carver& c, const mfalcon_desc* d, const MfPlan& p, MfCandBufs* bs) {
+void carve_cand_ws(Carver& c, const mfalcon_desc* d, const MfPlan& p, MfCandBufs* b) {
   const hstu_layer_desc& ld = d->layer;
   const hstu_attn_desc& a = ld.attn;
   const size_t es = elt_size(a.dtype);
   const int64_t f1 = 2LL * a.num_heads * (a.d_v + a.d_qk);
   const int64_t hv = (int64_t)a.num_heads * a.d_v;
-  const int64_t m = std::min<int64_t>(d->microbatch, std::max<int64_t>(p.cand_total, 1));
-  for (int i = 0; i < cand_sets(d, p); ++i) {
-    MfCandBufs* b = bs + i;
-    b->c_uvqk = c.take((size_t)m * f1 * es);
-    b->c_o = (float*)c.take((size_t)p.kv_splits * m * hv * sizeof(float));
-    b->c_self = uses_mfma(&a) ? (float*)c.take((size_t)m * a.num_heads * sizeof(float)) : nullptr;
-    b->c_g = c.take((size_t)m * hv * es);
-    b->cx[0] = ld.num_layers > 1 ? c.take((size_t)m * ld.d_model * es) : nullptr;
-    b->cx[1] = ld.num_layers > 2 ? c.take((size_t)m * ld.d_model * es) : nullptr;
-  }
-}
-
-// The streams of the candidate pass, with their fork and join events: one set per
-// device, created together at the first call that needs them and kept for the life of
-// the process (default priority). Streams are dealt to the device's hardware queues
-// round robin, so streams created one after the other do not share a queue (the
-// caller's stream may share one with any of them, which is why it only forks and
-// joins). The mutex makes the enqueue of one call's fork ... join sequence atomic with
-// respect to other host threads using the same device.
-struct AuxStream {
-  hipStream_t s[kCandStreams] = {};
-  hipEvent_t fork = nullptr, join[kCandStreams] = {};
-};
-constexpr int kMaxDevices = 64;
-std::mutex g_aux_mu[kMaxDevices];
-AuxStream g_aux[kMaxDevices];
-
-hstu_status aux_stream(int* dev, AuxStream** out) {
-  HSTU_TRY(hipGetDevice(dev), "current device");
-  if (*dev < 0 || *dev >= kMaxDevices) return fail(HSTU_UNSUPPORTED, "device index %d", *dev);
-  AuxStream& a = g_aux[*dev];
-  if (!a.join[kCandStreams - 1]) {
-    for (int i = 0; i < kCandStreams; ++i)
-      if (!a.s[i])
-        HSTU_TRY(hipStreamCreateWithFlags(&a.s[i], hipStreamNonBlocking), "candidate stream");
-    if (!a.fork)
-      HSTU_TRY(hipEventCreateWithFlags(&a.fork, hipEventDisableTiming), "candidate event");
-    for (int i = 0; i < kCandStreams; ++i)
-      if (!a.join[i])
-        HSTU_TRY(hipEventCreateWithFlags(&a.join[i], hipEventDisableTiming), "candidate event");
-  }
-  *out = &a;
-  return HSTU_OK;
+  const int64_t m = group_rows(d, p);
+  b->c_uvqk = c.take((size_t)m * f1 * es);
+  b->c_o = (float*)c.take((size_t)p.kv_splits * m * hv * sizeof(float));
+  b->c_self = uses_mfma(&a) ? (float*)c.take((size_t)m * a.num_heads * sizeof(float)) : nullptr;
+  b->c_g = c.take((size_t)m * hv * es);
+  b->cx[0] = ld.num_layers > 1 ? c.take((size_t)m * ld.d_model * es) : nullptr;
+  b->cx[1] = ld.num_layers > 2 ? c.take((size_t)m * ld.d_model * es) : nullptr;
 }
 
 // The history half of the plan (cand offsets may be NULL: then no candidate sizes).
@@ -506,8 +489,8 @@ hstu_status plan_mfalcon(const mfalcon_desc* d, const int64_t* hoff, const int64
   carve_hist_ws(h, d, *p, &hb);
   p->hist_ws = h.off;
   Carver k{nullptr};
-  MfCandBufs kb[kCandStreams];
-  carve_cand_ws(k, d, *p, kb);
+  MfCandBufs kb;
+  carve_cand_ws(k, d, *p, &kb);
   p->cand_ws = k.off;
   return HSTU_OK;
 }
@@ -534,6 +517,7 @@ hstu_status run_history(const mfalcon_desc* d, const MfPlan& p, const int64_t* h
   lb.kr = cache.kr;
   lb.o = hb.o;
   lb.g = hb.g;
+  lb.qk_lo = hb.qk_lo;
   // the history's work items (layers 0..L-2) and key ranges (every layer, candidates included)
   hstu_status st = plan_causal(ld.attn, hist_offsets, hist_ts, p.hist, lb, s);
   if (st) return st;
@@ -563,111 +547,79 @@ hstu_status run_candidates(const mfalcon_desc* d, const MfPlan& p, const int64_t
   const int hv = a.num_heads * a.d_v;
   const int dm = ld.d_model;
   const int B = a.batch;
-  const int64_t m = d->microbatch;
-  // With several microbatches, microbatch i runs on the library's stream i % 4 with
-  // buffer set i % 4, so that the projections and gates of some microbatches fill the
-  // gaps and tails of the others' attention. The streams are forked from the caller's
-  // stream after the work already queued there (the history pass) and joined back before
-  // the logits. Each microbatch's results are those of a serial run.
-  const int sets = cand_sets(d, p);
-  hipStream_t st[kCandStreams];
-  for (int i = 0; i < kCandStreams; ++i) st[i] = s0;
-  AuxStream* aux = nullptr;
-  std::unique_lock<std::mutex> lock;
-  if (sets > 1) {
-    int dev = 0;
-    hstu_status ast = aux_stream(&dev, &aux);
-    if (ast) return ast;
-    lock = std::unique_lock<std::mutex>(g_aux_mu[dev]);
-    HSTU_TRY(hipEventRecord(aux->fork, s0), "candidate fork");
-    for (int i = 0; i < kCandStreams; ++i) {
-      st[i] = aux->s[i];
-      HSTU_TRY(hipStreamWaitEvent(aux->s[i], aux->fork, 0), "candidate fork");
+  const int64_t gm = group_rows(d, p);
+  const hipStream_t s = s0;
+  const MfCandBufs& b = *bufs;
+  for (int64_t m0 = 0; m0 < p.cand_total; m0 += gm) {
+    const int64_t m1 = std::min(m0 + gm, p.cand_total);
+    const int64_t rows = m1 - m0;
+    // users whose candidate range overlaps [m0, m1)
+    int ub = (int)(std::upper_bound(cand_offsets_host, cand_offsets_host + B + 1, m0) -
+                   cand_offsets_host) - 1;
+    int ue = (int)(std::lower_bound(cand_offsets_host, cand_offsets_host + B + 1, m1) -
+                   cand_offsets_host);  // one past the last overlapping user
+    ub = std::max(ub, 0);
+    ue = std::min(ue, B);
+    int64_t max_rows = 0;
+    for (int u = ub; u < ue; ++u) {
+      const int64_t cs = std::max(cand_offsets_host[u], m0);
+      const int64_t ce = std::min(cand_offsets_host[u + 1], m1);
+      max_rows = std::max(max_rows, ce - cs);
+    }
+    const void* in = (const char*)cand_x + (size_t)m0 * dm * es;
+    for (int l = 0; l < L; ++l) {
+      const hstu_layer_weights& w = weights[l];
+      void* out = (l == L - 1) ? (void*)((char*)cand_out + (size_t)m0 * dm * es) : b.cx[l % 2];
+      const int64_t f1 = 2LL * a.num_heads * (a.d_v + a.d_qk);
+      HSTU_TRY(launch_gemm(in, dm, w.w1, dm, w.b1, nullptr, 0, b.c_uvqk, f1, rows, (int)f1, dm, 1,
+                           bf, s),
+               "candidate f1 projection");
+      const UVQK cv = split_view(b.c_uvqk, a);
+      const UVQK hvw = split_view(cache.uvqk[l], a);
+      AttnArgs aa = base_args(&a);
+      aa.q = cv.q;
+      aa.ld_q = cv.ld;
+      aa.kc = cv.k;
+      aa.vc = cv.v;
+      aa.ld_kc = aa.ld_vc = cv.ld;
+      aa.k = hvw.k;
+      aa.v = hvw.v;
+      aa.ld_k = aa.ld_v = hvw.ld;
+      aa.out = b.c_o;
+      aa.ld_o = hv;
+      aa.out_f32 = 1;
+      aa.q_offsets = cand_offsets;
+      aa.k_offsets = hist_offsets;
+      aa.ts_q = cand_ts;
+      aa.ts_k = hist_ts;
+      aa.rab_pos = w.rab_pos;
+      aa.rab_time = w.rab_time;
+      aa.key_ranges = (hist_ts && w.rab_time) ? cache.kr : nullptr;  // unread when no history
+      aa.row_begin = m0;
+      aa.row_end = m1;
+      aa.max_user_rows = max_rows;
+      // key-range splits of the history: fixed by the history lengths alone, so a
+      // candidate's reduction order never depends on the rows around it
+      aa.kv_splits = p.kv_splits;
+      aa.keys_per_split = p.keys_per_split;
+      aa.part_stride = rows * hv;
+      // the MFMA kernel leaves the candidates' own values to the layer norm
+      aa.self_w = b.c_self;
+      for (int u0 = ub; u0 < ue; u0 += 65535) {
+        aa.user_begin = u0;
+        aa.n_users = std::min(ue - u0, 65535);
+        HSTU_TRY(run_attention(&a, aa, true, s), "candidate attention");
+      }
+      HSTU_TRY(launch_ln_gate(b.c_o, hv, aa.kv_splits, aa.part_stride, cv.u, cv.ld, w.ln_gamma,
+                              w.ln_beta, a.ln_eps, b.c_g, hv, rows, hv, bf, s, aa.self_w, cv.v,
+                              cv.ld, a.d_v),
+               "candidate layer norm gate");
+      HSTU_TRY(launch_gemm(b.c_g, hv, w.w2, hv, w.b2, ld.residual ? in : nullptr, dm, out, dm,
+                           rows, dm, hv, 0, bf, s),
+               "candidate f2 projection");
+      in = out;
     }
   }
-  auto microbatches = [&]() -> hstu_status {
-    int64_t mb = 0;
-    for (int64_t m0 = 0; m0 < p.cand_total; m0 += m, ++mb) {
-      const hipStream_t s = st[mb % sets];
-      const MfCandBufs& b = bufs[mb % sets];
-      const int64_t m1 = std::min(m0 + m, p.cand_total);
-      const int64_t rows = m1 - m0;
-      // users whose candidate range overlaps [m0, m1)
-      int ub = (int)(std::upper_bound(cand_offsets_host, cand_offsets_host + B + 1, m0) -
-                     cand_offsets_host) - 1;
-      int ue = (int)(std::lower_bound(cand_offsets_host, cand_offsets_host + B + 1, m1) -
-                     cand_offsets_host);  // one past the last overlapping user
-      ub = std::max(ub, 0);
-      ue = std::min(ue, B);
-      int64_t max_rows = 0;
-      for (int u = ub; u < ue; ++u) {
-        const int64_t cs = std::max(cand_offsets_host[u], m0);
-        const int64_t ce = std::min(cand_offsets_host[u + 1], m1);
-        max_rows = std::max(max_rows, ce - cs);
-      }
-      const void* in = (const char*)cand_x + (size_t)m0 * dm * es;
-      for (int l = 0; l < L; ++l) {
-        const hstu_layer_weights& w = weights[l];
-        void* out = (l == L - 1) ? (void*)((char*)cand_out + (size_t)m0 * dm * es) : b.cx[l % 2];
-        const int64_t f1 = 2LL * a.num_heads * (a.d_v + a.d_qk);
-        HSTU_TRY(launch_gemm(in, dm, w.w1, dm, w.b1, nullptr, 0, b.c_uvqk, f1, rows, (int)f1, dm, 1,
-                             bf, s),
-                 "candidate f1 projection");
-        const UVQK cv = split_view(b.c_uvqk, a);
-        const UVQK hvw = split_view(cache.uvqk[l], a);
-        AttnArgs aa = base_args(&a);
-        aa.q = cv.q;
-        aa.ld_q = cv.ld;
-        aa.kc = cv.k;
-        aa.vc = cv.v;
-        aa.ld_kc = aa.ld_vc = cv.ld;
-        aa.k = hvw.k;
-        aa.v = hvw.v;
-        aa.ld_k = aa.ld_v = hvw.ld;
-        aa.out = b.c_o;
-        aa.ld_o = hv;
-        aa.out_f32 = 1;
-        aa.q_offsets = cand_offsets;
-        aa.k_offsets = hist_offsets;
-        aa.ts_q = cand_ts;
-        aa.ts_k = hist_ts;
-        aa.rab_pos = w.rab_pos;
-        aa.rab_time = w.rab_time;
-        aa.key_ranges = (hist_ts && w.rab_time) ? cache.kr : nullptr;  // unread when no history
-        aa.row_begin = m0;
-        aa.row_end = m1;
-        aa.max_user_rows = max_rows;
-        // key-range splits of the history: fixed by the history lengths alone, so a
-        // candidate's reduction order never depends on the microbatch around it
-        aa.kv_splits = p.kv_splits;
-        aa.keys_per_split = p.keys_per_split;
-        aa.part_stride = rows * hv;
-        // the MFMA kernel leaves the candidates' own values to the layer norm
-        aa.self_w = b.c_self;
-        for (int u0 = ub; u0 < ue; u0 += 65535) {
-          aa.user_begin = u0;
-          aa.n_users = std::min(ue - u0, 65535);
-          HSTU_TRY(run_attention(&a, aa, true, s), "candidate attention");
-        }
-        HSTU_TRY(launch_ln_gate(b.c_o, hv, aa.kv_splits, aa.part_stride, cv.u, cv.ld, w.ln_gamma,
-                                w.ln_beta, a.ln_eps, b.c_g, hv, rows, hv, bf, s, aa.self_w, cv.v,
-                                cv.ld, a.d_v),
-                 "candidate layer norm gate");
-        HSTU_TRY(launch_gemm(b.c_g, hv, w.w2, hv, w.b2, ld.residual ? in : nullptr, dm, out, dm,
-                             rows, dm, hv, 0, bf, s),
-                 "candidate f2 projection");
-        in = out;
-      }
-    }
-    return HSTU_OK;
-  };
-  const hstu_status rs = microbatches();
-  if (sets > 1)  // joined also after a failed launch, so that nothing runs past the call
-    for (int i = 0; i < kCandStreams; ++i) {
-      HSTU_TRY(hipEventRecord(aux->join[i], aux->s[i]), "candidate join");
-      HSTU_TRY(hipStreamWaitEvent(s0, aux->join[i], 0), "candidate join");
-    }
-  if (rs) return rs;
   // the logits of every candidate in one launch (each row's dot product is independent
   // of the microbatch it was scored in)
   if (cand_logit)
@@ -876,8 +828,11 @@ hstu_status layer_bwd_once(const hstu_layer_desc* d, const LayerBwdPlan& p, cons
   if (!g) g = &none;
   // forward pieces: z1, SiLU(z1), attention output, gate
   // (bf16: the GEMM writes SiLU(z1) too)
+  // as in the forward, the attention takes split Q and K (their lo parts borrow dact,
+  // which this layer's backward writes only after the attention has read them)
+  void* lo = layer_splits_qk(a) ? b.dact : nullptr;
   HSTU_TRY(launch_gemm_ex(xl, dm, w.w1, dm, w.b1, nullptr, 0, b.z1, F1, T, (int)F1, dm, 0, bf, 1, 1,
-                          dm, 0, bf ? b.uvqk : nullptr, s),
+                          dm, 0, bf ? b.uvqk : nullptr, s, lo, 2 * hv),
            "f1 pre-activation");
   if (!bf) HSTU_TRY(launch_silu_act(b.z1, F1, b.uvqk, F1, T, (int)F1, bf, s), "f1 activation");
   const UVQK vw = split_view(b.uvqk, a);
@@ -885,6 +840,11 @@ hstu_status layer_bwd_once(const hstu_layer_desc* d, const LayerBwdPlan& p, cons
   aa.q = vw.q;
   aa.k = vw.k;
   aa.v = vw.v;
+  if (lo) {
+    const UVQK lw = split_view(lo, a);
+    aa.q_lo = lw.q;
+    aa.k_lo = lw.k;
+  }
   aa.ld_q = aa.ld_k = aa.ld_v = vw.ld;
   aa.out = b.o;
   aa.ld_o = hv;
@@ -1045,6 +1005,7 @@ hstu_status enqueue_attn_fwd(const hstu_attn_desc* desc, const AttnPlan& p,
 // address): the device address comes from hipGetSymbolAddress, taken once per device
 // with that device current, and kept below.
 constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+constexpr int kMaxDevices = 64;
 static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
 
 std::mutex g_scratch_mu;
@@ -1223,7 +1184,9 @@ hstu_status hstu_layer_bwd(const hstu_layer_desc* desc, const int64_t* seq_offse
   const hstu_attn_desc& a = desc->attn;
   const size_t xbytes = (size_t)p.j.total * desc->d_model * elt_size(a.dtype);
   // forward: inputs of layers 1..L-1
-  LayerBufs lb{b.items, b.kr, b.uvqk, b.o, b.g, nullptr};
+  // the forward recompute borrows dact (not used until the backward part) for the lo parts
+  LayerBufs lb{b.items, b.kr, b.uvqk, b.o, b.g, nullptr,
+               layer_splits_qk(a) ? b.dact : nullptr};
   if ((st = plan_causal(a, seq_offsets, timestamps, p.j, lb, s))) return st;
   for (int l = 0; l + 1 < L; ++l) {
     const void* in = l == 0 ? x : (const void*)(b.xs + (l - 1) * xbytes);
@@ -1286,11 +1249,11 @@ hstu_status mfalcon_score(const mfalcon_desc* desc, const int64_t* hist_offsets_
   MfHistBufs hb;
   carve_hist_ws(c, desc, p, &hb);
   c.off = align_up(p.cache) + align_up(p.hist_ws);
-  MfCandBufs cb[kCandStreams];
-  carve_cand_ws(c, desc, p, cb);
+  MfCandBufs cb;
+  carve_cand_ws(c, desc, p, &cb);
   if ((st = run_history(desc, p, hist_offsets, hist_ts, hist_x, weights, cache, hb, s))) return st;
   return run_candidates(desc, p, hist_offsets, hist_ts, cache, cand_offsets_host, cand_offsets,
-                        cand_ts, cand_x, weights, w_head, cand_out, cand_logit, cb, s);
+                        cand_ts, cand_x, weights, w_head, cand_out, cand_logit, &cb, s);
 }
 
 hstu_status mfalcon_cache_size(const mfalcon_desc* desc, const int64_t* hist_offsets_host,
@@ -1370,10 +1333,10 @@ hstu_status mfalcon_score_cached(const mfalcon_desc* desc, const int64_t* hist_o
   MfCache cb;
   carve_cache(c, desc, p, &cb);
   Carver w{(char*)workspace};
-  MfCandBufs kb[kCandStreams];
-  carve_cand_ws(w, desc, p, kb);
+  MfCandBufs kb;
+  carve_cand_ws(w, desc, p, &kb);
   return run_candidates(desc, p, hist_offsets, hist_ts, cb, cand_offsets_host, cand_offsets,
-                        cand_ts, cand_x, weights, w_head, cand_out, cand_logit, kb,
+                        cand_ts, cand_x, weights, w_head, cand_out, cand_logit, &kb,
                         (hipStream_t)stream);
 }
 

@@ -154,8 +154,14 @@ bool attn_mfma_strides_ok(const AttnArgs& a) {
   return a.ld_k == a.ld_v && a.ld_k > 0 && (int64_t)(MBN + 1) * a.ld_k * 2 < (int64_t(1) << 32);
 }
 
-template <int D, bool CAND>
-__global__ __launch_bounds__(256, D <= 64 ? 3 : 2) void attn_mfma_kernel(AttnArgs a) {
+// SPLIT (causal mode only): queries and keys come as bf16 pairs hi + lo (a.q / a.q_lo,
+// a.k / a.k_lo, same strides) carrying about 16 significant bits, and each score is
+// hi.hi + lo.hi + hi.lo: three MFMAs per k-step, the lo.lo term (about 2^-16 relative)
+// left out. The layer path uses it for the Q and K it computes itself.
+template <int D, bool CAND, bool SPLIT>
+__global__ __launch_bounds__(256, SPLIT ? (D <= 64 ? 2 : 1) : (D <= 64 ? 3 : 2)) void
+attn_mfma_kernel(AttnArgs a) {
+  static_assert(!(CAND && SPLIT), "split scores are for causal mode");
   constexpr int NKK = D / 16;  // k-steps of the S^T contraction
   constexpr int NC = D / 32;   // 32-wide output column blocks
   constexpr int CPR = D / 8;   // 16-byte chunks per row
@@ -164,6 +170,8 @@ __global__ __launch_bounds__(256, D <= 64 ? 3 : 2) void attn_mfma_kernel(AttnArg
   // the in-flight DMA target from the buffer being read (no conservative waits)
   __shared__ __attribute__((aligned(16))) bf16 Ks0[TE];
   __shared__ __attribute__((aligned(16))) bf16 Ks1[TE];
+  __shared__ __attribute__((aligned(16))) bf16 Kl0[SPLIT ? TE : 8];  // K lo parts (SPLIT)
+  __shared__ __attribute__((aligned(16))) bf16 Kl1[SPLIT ? TE : 8];
   __shared__ __attribute__((aligned(16))) bf16 Vs0[MBN * D];
   __shared__ __attribute__((aligned(16))) bf16 Vs1[MBN * D];
   __shared__ __attribute__((aligned(16))) uint32_t tk_lo[2][MBN];
@@ -201,13 +209,19 @@ __global__ __launch_bounds__(256, D <= 64 ? 3 : 2) void attn_mfma_kernel(AttnArg
   const bool row_ok = wrow < t.rows;
   const bool wave_live = 32 * wu < t.rows;
   bf16x8 qf[NKK];
+  bf16x8 qlf[SPLIT ? NKK : 1];  // lo parts of the queries (SPLIT)
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) {
+    const int64_t qo = (t.q_local + wrow) * a.ld_q + (int64_t)h * D + 16 * kk + 8 * hl;
     if (row_ok) {
-      qf[kk] = load_bf16x8(q + (t.q_local + wrow) * a.ld_q + (int64_t)h * D + 16 * kk + 8 * hl);
+      qf[kk] = load_bf16x8(q + qo);
+      if constexpr (SPLIT) qlf[kk] = load_bf16x8((const bf16*)a.q_lo + qo);
     } else {
 #pragma unroll
       for (int i = 0; i < 8; ++i) qf[kk][i] = (bf16)0.f;
+      if constexpr (SPLIT)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qlf[kk][i] = (bf16)0.f;
     }
   }
   // candidate mode, first key range: the candidate's own key (relative position 0,
@@ -263,43 +277,54 @@ __global__ __launch_bounds__(256, D <= 64 ? 3 : 2) void attn_mfma_kernel(AttnArg
   // instruction fills 16-byte slot L of a contiguous 1 KiB span, so the LDS layout
   // comes from which source chunk each lane fetches. K rows are padded by one slot
   // (row-fragment reads, see tile_off); V rows are unpadded with their 16-byte chunks
-  // permuted by an XOR of the row (see vtile_off). Rows past the data repeat the
-  // last valid row: their scores are masked and multiply finite values.
+  // permuted by an XOR of the row (see vtile_off). Rows past the data fetch the last
+  // chunk of the last valid row instead: their scores are masked and multiply finite
+  // values.
   constexpr int SPR = CPR + 1;        // 16-byte slots per K row
   constexpr int NSLOT = MBN * SPR;    // slots per K tile
   constexpr int NINSTR = NSLOT / 64;  // wave-instructions per K tile
   constexpr int NIW = (NINSTR + 3) / 4;
   static_assert(NSLOT % 64 == 0, "every DMA instruction fills 64 slots");
   static_assert(MBN * CPR == 4 * 64 * (NIW - 1), "each wavefront issues NIW - 1 V instructions");
-  // Wavefront w issues instructions w, w+4, w+8, ... of each matrix tile. The
-  // (key row, byte column) source of each of its slots is packed into one word,
-  // computed once; K and V share the row stride. The address is a uniform base
-  // plus a 32-bit offset (the scalar-base form of the instruction).
+  // Wavefront w issues instructions w, w+4, w+8, ... of each matrix tile. The byte
+  // offset of each of its slots' source chunk from the tile's first row is computed
+  // once (K and V share the row stride). The address is a uniform base plus that
+  // 32-bit offset (the scalar-base form of the instruction). Offsets grow with the row
+  // (a row's chunks span less than the row stride), so one unsigned minimum against the
+  // offset of the last valid row's last chunk keeps every fetch inside the data.
   const uint32_t ldb = (uint32_t)(a.ld_k * 2);
-  uint32_t spk[NIW], spv[NIW - 1];
+  uint32_t offk[NIW], offv[NIW - 1];
 #pragma unroll
   for (int j = 0; j < NIW; ++j) {
     const int slot = 64 * (w + 4 * j) + lane;
     const int row = slot / SPR, pc = slot % SPR;
-    spk[j] = (uint32_t)row | ((uint32_t)(pc < CPR ? pc : 0) << 10);
+    offk[j] = (uint32_t)row * ldb + 16u * (uint32_t)(pc < CPR ? pc : 0);
   }
 #pragma unroll
   for (int j = 0; j < NIW - 1; ++j) {
     const int slot = 64 * (w + 4 * j) + lane;
     const int row = slot / CPR;
-    spv[j] = (uint32_t)row | ((uint32_t)((slot % CPR) ^ vswz<D>(row)) << 10);
+    offv[j] = (uint32_t)row * ldb + 16u * (uint32_t)((slot % CPR) ^ vswz<D>(row));
   }
   const char* kg = (const char*)a.k + (int64_t)h * D * 2;
   const char* vg = (const char*)a.v + (int64_t)h * D * 2;
   struct DmaSrc {
     const char* kb;
     const char* vb;
-    uint32_t lim;  // last key row of the data in the tile
+    const char* klb;  // K lo parts (SPLIT), same row stride as K
+    uint32_t lim;     // last key row of the data, counted from the tile's first row
+    uint32_t limoff;  // offset of that row's last chunk (rows past the tile: its last row's)
+  };
+  auto lim_off = [&](uint32_t lim) {
+    return (lim < (uint32_t)MBN - 1 ? lim : (uint32_t)MBN - 1) * ldb + 16u * (CPR - 1);
   };
   // the source of the tile being fetched: set for the first tile, then advanced by one
   // tile of rows per step (K and V share the row stride)
   DmaSrc nsrc{kg + (t.k_base + kbeg) * a.ld_k * 2, vg + (t.k_base + kbeg) * a.ld_v * 2,
-              (uint32_t)(nk - 1 - kbeg)};
+              SPLIT ? (const char*)a.k_lo + (int64_t)h * D * 2 + (t.k_base + kbeg) * a.ld_k * 2
+                    : nullptr,
+              (uint32_t)(nk - 1 - kbeg), 0u};
+  nsrc.limoff = lim_off(nsrc.lim);
   const int64_t tile_bytes = (int64_t)MBN * a.ld_k * 2;
   // this wavefront's instruction pair j (K and V; the last K instruction has no V
   // partner) for one tile
@@ -308,20 +333,17 @@ __global__ __launch_bounds__(256, D <= 64 ? 3 : 2) void attn_mfma_kernel(AttnArg
     bf16* Kd = buf ? Ks1 : Ks0;
     bf16* Vd = buf ? Vs1 : Vs0;
     const int i = wu + 4 * j;
-    {
-      const uint32_t row = min(spk[j] & 1023u, src.lim);
-      const uint32_t off = row * ldb + 16u * (spk[j] >> 10);
+    __builtin_amdgcn_global_load_lds(
+        (const __attribute__((address_space(1))) void*)(src.kb + min(offk[j], src.limoff)),
+        (__attribute__((address_space(3))) void*)(&Kd[512 * i]), 16, 0, 0);
+    if constexpr (SPLIT)
       __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(src.kb + off),
-          (__attribute__((address_space(3))) void*)(&Kd[512 * i]), 16, 0, 0);
-    }
-    if (j < NIW - 1) {
-      const uint32_t row = min(spv[j] & 1023u, src.lim);
-      const uint32_t off = row * ldb + 16u * (spv[j] >> 10);
+          (const __attribute__((address_space(1))) void*)(src.klb + min(offk[j], src.limoff)),
+          (__attribute__((address_space(3))) void*)(&(buf ? Kl1 : Kl0)[512 * i]), 16, 0, 0);
+    if (j < NIW - 1)
       __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(src.vb + off),
+          (const __attribute__((address_space(1))) void*)(src.vb + min(offv[j], src.limoff)),
           (__attribute__((address_space(3))) void*)(&Vd[512 * i]), 16, 0, 0);
-    }
   };
   static_assert(NINSTR == 4 * (NIW - 1) + 1, "only wavefront 0 issues a last K instruction");
   auto dma_tile = [&](auto bufc, const DmaSrc& src) {
@@ -461,7 +483,9 @@ __global__ __launch_bounds__(256, D <= 64 ? 3 : 2) void attn_mfma_kernel(AttnArg
     if (more) {
       nsrc.kb += tile_bytes;
       nsrc.vb += tile_bytes;
+      if constexpr (SPLIT) nsrc.klb += tile_bytes;
       nsrc.lim -= MBN;
+      nsrc.limoff = lim_off(nsrc.lim);
     }
     auto dma = [&](int j) { dma_pair(BN_{}, nsrc, j); };
     if (wu == 0) dma(NIW - 1);
@@ -474,6 +498,7 @@ __global__ __launch_bounds__(256, D <= 64 ? 3 : 2) void attn_mfma_kernel(AttnArg
     const BlockClass c0 = block_class(cls, 0);
     const BlockClass c1 = block_class(cls, 1);
     const bf16* Kt = buf ? Ks1 : Ks0;
+    const bf16* Klt = buf ? Kl1 : Kl0;
     const bf16* Vt = buf ? Vs1 : Vs0;
     // both blocks active, unmasked, one position bucket, one time bucket
     const bool fast = (cls.f & 0x1f1fu) == 0x0505u;
@@ -513,15 +538,27 @@ __global__ __launch_bounds__(256, D <= 64 ? 3 : 2) void attn_mfma_kernel(AttnArg
       return xb;
     };
     // S^T of one block, starting from the constant part of its bias
+    // one k-step of a block's S^T: hi.hi, then (SPLIT) lo.hi and hi.lo
+    auto s_step = [&](f32x16 x, const bf16x8& kh, const bf16x8& kl, int kk) {
+      x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, qf[kk], x, 0, 0, 0);
+      if constexpr (SPLIT) {
+        x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kl, qf[kk], x, 0, 0, 0);
+        x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, qlf[kk], x, 0, 0, 0);
+      }
+      return x;
+    };
     auto s_chain = [&](int kb, float bias, const bf16x8* keyA, bool with_dma) {
-      bf16x8 kq[NKK];
+      bf16x8 kq[NKK], kql[SPLIT ? NKK : 1];
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) kq[kk] = kfrag(Kt, kb, kk);
+      for (int kk = 0; kk < NKK; ++kk) {
+        kq[kk] = kfrag(Kt, kb, kk);
+        if constexpr (SPLIT) kql[kk] = kfrag(Klt, kb, kk);
+      }
       f32x16 x = bias_step(bias, keyA);
       if (with_dma) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
-        x = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kq[kk], qf[kk], x, 0, 0, 0);
+        x = s_step(x, kq[kk], kql[SPLIT ? kk : 0], kk);
         if (with_dma) {  // the dependent chain has room for the next tile's DMA
           if (kk < NIW - 1) dma(kk);
           __builtin_amdgcn_sched_barrier(0);
@@ -555,14 +592,17 @@ __global__ __launch_bounds__(256, D <= 64 ? 3 : 2) void attn_mfma_kernel(AttnArg
         kA[1] = bias_frag(key_bias(k0 + 32));
       }
       const f32x16 s0 = s_chain(0, pb + c0.tlo, CAND && keyb ? &kA[0] : nullptr, true);
-      bf16x8 k1[NKK];
+      bf16x8 k1[NKK], k1l[SPLIT ? NKK : 1];
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) k1[kk] = kfrag(Kt, 1, kk);
+      for (int kk = 0; kk < NKK; ++kk) {
+        k1[kk] = kfrag(Kt, 1, kk);
+        if constexpr (SPLIT) k1l[kk] = kfrag(Klt, 1, kk);
+      }
       f32x16 s1 = bias_step(pb + c1.tlo, CAND && keyb ? &kA[1] : nullptr);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
-        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1[kk], qf[kk], s1, 0, 0, 0);
+        s1 = s_step(s1, k1[kk], k1l[SPLIT ? kk : 0], kk);
         act_step(s0, pa0, kk);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -592,14 +632,17 @@ __global__ __launch_bounds__(256, D <= 64 ? 3 : 2) void attn_mfma_kernel(AttnArg
     auto fast2_path = [&]() {
       f32x16 s0 = s_chain(0, pb + c0.tlo, nullptr, true);
       if (c0.tmode() == 1) two_bucket(s0, 0, c0);
-      bf16x8 k1[NKK];
+      bf16x8 k1[NKK], k1l[SPLIT ? NKK : 1];
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) k1[kk] = kfrag(Kt, 1, kk);
+      for (int kk = 0; kk < NKK; ++kk) {
+        k1[kk] = kfrag(Kt, 1, kk);
+        if constexpr (SPLIT) k1l[kk] = kfrag(Klt, 1, kk);
+      }
       f32x16 s1 = bias_step(pb + c1.tlo, nullptr);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
-        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1[kk], qf[kk], s1, 0, 0, 0);
+        s1 = s_step(s1, k1[kk], k1l[SPLIT ? kk : 0], kk);
         act_step(s0, pa0, kk);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -767,12 +810,16 @@ hipError_t launch_attn_mfma(const AttnArgs& a, bool cand, hipStream_t s) {
     grid = dim3((unsigned)((a.max_user_rows + MBM - 1) / MBM) * (unsigned)a.H, (unsigned)a.n_users,
                 (unsigned)(a.kv_splits > 1 ? a.kv_splits : 1));
   if (grid.x == 0 || grid.y == 0) return hipSuccess;
+  const bool split = a.q_lo != nullptr;
+  if (split && (cand || !a.k_lo)) return hipErrorInvalidValue;
 #define HSTU_MFMA_CASE(DD)                                                                  \
   if (a.d_qk == DD) {                                                                       \
     if (cand)                                                                               \
-      hipLaunchKernelGGL((attn_mfma_kernel<DD, true>), grid, dim3(256), 0, s, a);           \
+      hipLaunchKernelGGL((attn_mfma_kernel<DD, true, false>), grid, dim3(256), 0, s, a);    \
+    else if (split)                                                                         \
+      hipLaunchKernelGGL((attn_mfma_kernel<DD, false, true>), grid, dim3(256), 0, s, a);    \
     else                                                                                    \
-      hipLaunchKernelGGL((attn_mfma_kernel<DD, false>), grid, dim3(256), 0, s, a);          \
+      hipLaunchKernelGGL((attn_mfma_kernel<DD, false, false>), grid, dim3(256), 0, s, a);   \
     return hipGetLastError();                                                               \
   }
   HSTU_MFMA_CASE(32) HSTU_MFMA_CASE(64) HSTU_MFMA_CASE(128)

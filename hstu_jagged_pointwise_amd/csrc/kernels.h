@@ -53,6 +53,10 @@ struct AttnArgs {
   int kv_splits;
   int64_t keys_per_split;
   int64_t part_stride;
+  // causal mode, MFMA kernel, optional: the lo parts of q and k (same strides as q and k),
+  // so that each score is formed from ~16-bit queries and keys (hi.hi + lo.hi + hi.lo)
+  const void* q_lo;
+  const void* k_lo;
   // candidate mode, MFMA kernel: where split 0 writes each candidate's self weight
   // SiLU(q_c.k_c + rab_pos[0] + rab_time[0]) / N, [microbatch rows][H], for the LN gate to
   // add self_w * v_c (the vector-ALU kernel adds the self term itself and ignores this)
@@ -125,19 +129,25 @@ hipError_t launch_ln_gate(const float* o, int64_t ld_o, int nsplit, int64_t spli
                           const void* vself = nullptr, int64_t ld_vself = 0, int dv = 0);
 
 // C[M,N] = epi(A[M,K] W[N,K]^T + bias[N]); epi = SiLU when silu, + R[M,N] when R.
+// lo (bf16 output only): for columns n >= lo_c0 (a multiple of 8) also writes
+// lo[m, n] = bf16(y - bf16(y)), the part of the fp32 result y that the bf16 C drops, with
+// C's leading dimension; C + lo then carries y to about 16 significant bits.
 hipError_t launch_gemm(const void* A, int64_t lda, const void* W, int64_t ldw,
                        const float* bias, const void* R, int64_t ldr, void* C, int64_t ldc,
-                       int64_t M, int N, int K, int silu, int use_bf16, hipStream_t s);
+                       int64_t M, int N, int K, int silu, int use_bf16, hipStream_t s,
+                       void* lo = nullptr, int lo_c0 = 0);
 
 // launch_gemm with an fp32 output (bf16 inputs; fp32 inputs always write fp32) and
 // split-K: grid dimension y = splits, split y covers K range [y*ksplit, (y+1)*ksplit)
 // (ksplit a multiple of 64) and writes C + y*c_split; splits > 1 takes no bias,
 // residual or SiLU. act (bf16 inputs, fp32 output, one split, no SiLU, else NULL) also
 // receives SiLU(C) in bf16, same leading dimension, rounded as launch_silu_act rounds.
+// lo as for launch_gemm: the bf16 remainder of C (bf16 output) or, with act, of SiLU(C).
 hipError_t launch_gemm_ex(const void* A, int64_t lda, const void* W, int64_t ldw, const float* bias,
                           const void* R, int64_t ldr, void* C, int64_t ldc, int64_t M, int N, int K,
                           int silu, int use_bf16, int out_f32, int splits, int64_t ksplit,
-                          int64_t c_split, void* act, hipStream_t s);
+                          int64_t c_split, void* act, hipStream_t s, void* lo = nullptr,
+                          int lo_c0 = 0);
 
 // C[M,N] = sum_k A[k,m] B[k,n] (bf16 A [K, lda] and B [K, ldb] row-major, fp32 C): the
 // weight-gradient form, contraction over rows. M, N and both leading dimensions multiples

@@ -198,18 +198,15 @@ hstu_status hstu_layer_fwd(const hstu_layer_desc* desc, const int64_t* seq_offse
  * therefore equals the last row of hstu_layer_fwd run on
  * (history, candidate). The history pass runs once per call. The candidates
  * are then processed desc->microbatch at a time (in global candidate order)
- * through all layers, reusing the cached history keys and values.
+ * through all layers, reusing the cached history keys and values. Up to four
+ * microbatches are in flight at once: their work is issued together, one
+ * launch per step for the group, which is what the workspace is sized for.
+ * A candidate's result does not depend on the microbatch size or on the
+ * other candidates, bit for bit.
  * hist_x [n_hist_tot, d_model], cand_x and cand_out [C_tot, d_model] (dtype).
  * hist_ts and cand_ts are both NULL or both set.
  * w_head [d_model] fp32 or NULL; cand_logit [C_tot] fp32 = cand_out . w_head,
  * or NULL.
- * Streams: with more than one microbatch, the microbatches run on four streams
- * the library creates per device at first use (default priority, kept until
- * the process ends). They are forked from `stream` after the work already
- * queued on it and joined back into it before the call returns, so the call
- * behaves as if every launch were on `stream`: later work on `stream` sees all
- * of its results. Results equal those of a serial run bit for bit. Calls from
- * several host threads on one device are serialized while they queue work.
  * ---------------------------------------------------------------------- */
 hstu_status mfalcon_workspace_size(const mfalcon_desc* desc, const int64_t* hist_offsets_host,
                                    const int64_t* cand_offsets_host, size_t* bytes);
