@@ -319,9 +319,12 @@ hstu_status layer_once(const hstu_layer_desc* d, const int64_t* off_dev, const i
   const int64_t rows = j.total;
   const int64_t f1 = 2LL * a.num_heads * (a.d_v + a.d_qk);
   const int hv = a.num_heads * a.d_v;
+  const int hq = a.num_heads * a.d_qk;
   void* lo = f1_only ? nullptr : b.qk_lo;
+  // with split scores the attention takes its queries pre-scaled (kQueryPrescale)
+  const int q_c1 = lo ? 2 * hv + hq : 0;
   HSTU_TRY(launch_gemm(x, d->d_model, w.w1, d->d_model, w.b1, nullptr, 0, b.uvqk, f1, rows, (int)f1,
-                       d->d_model, 1, bf, s, lo, 2 * hv),
+                       d->d_model, 1, bf, s, lo, 2 * hv, 2 * hv, q_c1, kQueryPrescale),
            "f1 projection");
   if (f1_only) return HSTU_OK;
   const UVQK vw = split_view(b.uvqk, a);
@@ -571,8 +574,10 @@ hstu_status run_candidates(const mfalcon_desc* d, const MfPlan& p, const int64_t
       const hstu_layer_weights& w = weights[l];
       void* out = (l == L - 1) ? (void*)((char*)cand_out + (size_t)m0 * dm * es) : b.cx[l % 2];
       const int64_t f1 = 2LL * a.num_heads * (a.d_v + a.d_qk);
+      // the MFMA kernel's candidate mode takes its queries pre-scaled (kQueryPrescale)
+      const int q_c1 = uses_mfma(&a) ? 2 * hv + a.num_heads * a.d_qk : 0;
       HSTU_TRY(launch_gemm(in, dm, w.w1, dm, w.b1, nullptr, 0, b.c_uvqk, f1, rows, (int)f1, dm, 1,
-                           bf, s),
+                           bf, s, nullptr, 0, 2 * hv, q_c1, kQueryPrescale),
                "candidate f1 projection");
       const UVQK cv = split_view(b.c_uvqk, a);
       const UVQK hvw = split_view(cache.uvqk[l], a);
@@ -828,11 +833,9 @@ hstu_status layer_bwd_once(const hstu_layer_desc* d, const LayerBwdPlan& p, cons
   if (!g) g = &none;
   // forward pieces: z1, SiLU(z1), attention output, gate
   // (bf16: the GEMM writes SiLU(z1) too)
-  // as in the forward, the attention takes split Q and K (their lo parts borrow dact,
-  // which this layer's backward writes only after the attention has read them)
-  void* lo = layer_splits_qk(a) ? b.dact : nullptr;
+  // (the attention here takes bf16 scores: the attention backward reads the same Q and K)
   HSTU_TRY(launch_gemm_ex(xl, dm, w.w1, dm, w.b1, nullptr, 0, b.z1, F1, T, (int)F1, dm, 0, bf, 1, 1,
-                          dm, 0, bf ? b.uvqk : nullptr, s, lo, 2 * hv),
+                          dm, 0, bf ? b.uvqk : nullptr, s),
            "f1 pre-activation");
   if (!bf) HSTU_TRY(launch_silu_act(b.z1, F1, b.uvqk, F1, T, (int)F1, bf, s), "f1 activation");
   const UVQK vw = split_view(b.uvqk, a);
@@ -840,11 +843,6 @@ hstu_status layer_bwd_once(const hstu_layer_desc* d, const LayerBwdPlan& p, cons
   aa.q = vw.q;
   aa.k = vw.k;
   aa.v = vw.v;
-  if (lo) {
-    const UVQK lw = split_view(lo, a);
-    aa.q_lo = lw.q;
-    aa.k_lo = lw.k;
-  }
   aa.ld_q = aa.ld_k = aa.ld_v = vw.ld;
   aa.out = b.o;
   aa.ld_o = hv;

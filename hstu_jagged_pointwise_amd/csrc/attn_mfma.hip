@@ -158,10 +158,21 @@ bool attn_mfma_strides_ok(const AttnArgs& a) {
 // a.k / a.k_lo, same strides) carrying about 16 significant bits, and each score is
 // hi.hi + lo.hi + hi.lo: three MFMAs per k-step, the lo.lo term (about 2^-16 relative)
 // left out. The layer path uses it for the Q and K it computes itself.
+//
+// Pre-scaled queries (candidate mode and SPLIT, i.e. the queries the library computes
+// itself in its f1 projection): q arrives multiplied by -log2(e) (the projection stores
+// it so, rounded to bf16 from fp32 like any stored query), and the bias tables are
+// scaled the same way when they are copied to LDS. A score then comes out of the MFMA
+// as x' = -log2(e) x, so that SiLU needs no multiply before the exponential:
+// SiLU(x) = x' * rcp(1 + exp2(x')) / -log2(e), and the 1/-log2(e) joins the 1/N of the
+// output scale.
 template <int D, bool CAND, bool SPLIT>
 __global__ __launch_bounds__(256, SPLIT ? (D <= 64 ? 2 : 1) : (D <= 64 ? 3 : 2)) void
 attn_mfma_kernel(AttnArgs a) {
   static_assert(!(CAND && SPLIT), "split scores are for causal mode");
+  constexpr bool PRE = CAND || SPLIT;
+  constexpr float kPre = -kLog2e;     // the scale of pre-scaled queries and tables
+  const float tscale = PRE ? kPre : 1.f;
   constexpr int NKK = D / 16;  // k-steps of the S^T contraction
   constexpr int NC = D / 32;   // 32-wide output column blocks
   constexpr int CPR = D / 8;   // 16-byte chunks per row
@@ -194,15 +205,16 @@ attn_mfma_kernel(AttnArgs a) {
   const int P = a.P, T = a.T;
 
   if (has_pos)
-    for (int i = tid; i < P; i += 256) rp[i] = a.rab_pos[(int64_t)h * P + i];
+    for (int i = tid; i < P; i += 256) rp[i] = tscale * a.rab_pos[(int64_t)h * P + i];
   if (has_time) {
-    if (tid < kTimeTab) rt[tid] = a.rab_time[(int64_t)h * T + (tid < T - 1 ? tid : T - 1)];
+    if (tid < kTimeTab)
+      rt[tid] = tscale * a.rab_time[(int64_t)h * T + (tid < T - 1 ? tid : T - 1)];
     if (tid < 32) {
       const int bt = 31 - tid;
-      rtc[tid] = a.rab_time[(int64_t)h * T + (bt < T - 1 ? bt : T - 1)];
+      rtc[tid] = tscale * a.rab_time[(int64_t)h * T + (bt < T - 1 ? bt : T - 1)];
     }
   }
-  const float pb = has_pos ? sload(a.rab_pos + (int64_t)h * P + P - 1) : 0.f;  // bucket P-1
+  const float pb = has_pos ? tscale * sload(a.rab_pos + (int64_t)h * P + P - 1) : 0.f;  // P-1
 
   // this lane's query row (the S^T column it holds) and its Q fragment
   const int wrow = 32 * w + l32;
@@ -241,10 +253,11 @@ attn_mfma_kernel(AttnArgs a) {
         for (int i = 0; i < 8; ++i) part = fmaf((float)qf[kk][i], (float)kf[kk][i], part);
     }
     part += __shfl_xor(part, 32, 64);
-    float xs = part;
-    if (has_pos) xs += sload(a.rab_pos + (int64_t)h * P);
-    if (has_time) xs += sload(a.rab_time + (int64_t)h * T);
-    if (hl == 0 && row_ok) a.self_w[(t.q_local + wrow) * a.H + h] = silu_fast(xs) * a.inv_n;
+    float xs = part;  // pre-scaled like the queries
+    if (has_pos) xs += kPre * sload(a.rab_pos + (int64_t)h * P);
+    if (has_time) xs += kPre * sload(a.rab_time + (int64_t)h * T);
+    if (hl == 0 && row_ok)
+      a.self_w[(t.q_local + wrow) * a.H + h] = silu_prescaled(xs) * (a.inv_n / kPre);
   }
   const int64_t tq = (has_time && row_ok) ? a.ts_q[t.q_base + wrow] : 0;
   const uint32_t tq1 = (uint32_t)tq + 1u;
@@ -507,20 +520,13 @@ attn_mfma_kernel(AttnArgs a) {
     // causal mode: both blocks live, unmasked, one position bucket, one or two time
     // buckets each (the fast path's schedule plus a per-element two-bucket select)
     const bool fast2 = !CAND && (cls.f & 0x1717u) == 0x0505u;
-    // this lane's key's whole bias (candidate mode): position n_h - j, elapsed time t_c - t_j
-    auto key_bias = [&](int kb0) {
-      const int j = kb0 + l32;
-      float b = has_pos ? rp[min(qpos0 - j, P - 1)] : 0.f;
-      if (has_time) b += rt[bucket_of(qmin - tk64[buf][j - k0], T)];
-      return b;
-    };
     constexpr int E = 16 / NKK;  // scores activated per interleaved step
     // SiLU of accumulator slots st*E .. st*E+E-1 into bf16 A fragments
     auto act_step = [&](const f32x16& x, bf16x8* pa, int st) {
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         const int r = st * E + e;
-        pa[r >> 3][r & 7] = (bf16)silu_fast(x[r]);
+        pa[r >> 3][r & 7] = (bf16)(PRE ? silu_prescaled(x[r]) : silu_fast(x[r]));
       }
     };
     // the start of a block's S^T accumulator: the block's constant bias, or, given keyA,
@@ -588,8 +594,22 @@ attn_mfma_kernel(AttnArgs a) {
     auto fast_path = [&](bool keyb) {
       bf16x8 kA[2];
       if constexpr (CAND) {
-        kA[0] = bias_frag(key_bias(k0));
-        kA[1] = bias_frag(key_bias(k0 + 32));
+        // the whole bias of a key (position n_h - j, elapsed time t_c - t_j), one key per
+        // lane: lane L takes key k0 + L (block 0 in the low half-wavefront, block 1 in the
+        // high one), split into bf16 high and low parts packed in one word; the k-step
+        // fragments carry the word in the low half-wavefront only
+        const int j = k0 + lane;
+        float b = has_pos ? rp[min(qpos0 - j, P - 1)] : 0.f;
+        if (has_time) b += rt[bucket_of(qmin - tk64[buf][lane], T)];
+        const bf16 bh = (bf16)b;
+        const bf16 bl = (bf16)(b - (float)bh);
+        const uint32_t word = (uint32_t)__builtin_bit_cast(uint16_t, bh) |
+                              ((uint32_t)__builtin_bit_cast(uint16_t, bl) << 16);
+        const uint32_t word1 = (uint32_t)__shfl_xor((int)word, 32, 64);  // block 1's key
+        const u32x4 f0 = {hl == 0 ? word : 0u, 0u, 0u, 0u};
+        const u32x4 f1 = {hl == 0 ? word1 : 0u, 0u, 0u, 0u};
+        kA[0] = __builtin_bit_cast(bf16x8, f0);
+        kA[1] = __builtin_bit_cast(bf16x8, f1);
       }
       const f32x16 s0 = s_chain(0, pb + c0.tlo, CAND && keyb ? &kA[0] : nullptr, true);
       bf16x8 k1[NKK], k1l[SPLIT ? NKK : 1];
@@ -783,6 +803,7 @@ attn_mfma_kernel(AttnArgs a) {
   __syncthreads();
   if (!wave_live) return;
 
+  const float oscale = PRE ? a.inv_n / kPre : a.inv_n;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int rw = 8 * (r >> 2) + 4 * hl + (r & 3);  // row within the wavefront
@@ -793,7 +814,7 @@ attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const int col = c * 32 + l32;
-      const float val = o[c][r] * a.inv_n;
+      const float val = o[c][r] * oscale;
       if (a.out_f32)
         ((float*)a.out)[orow + col] = val;
       else

@@ -72,7 +72,8 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const bf16* __restric
                                                          int N, int K, int silu, int tiles_n,
                                                          int tiles_total, int64_t ksplit,
                                                          int64_t c_split, bf16* __restrict__ act,
-                                                         bf16* __restrict__ rem, int rem_c0) {
+                                                         bf16* __restrict__ rem, int rem_c0,
+                                                         int sc_c0, int sc_c1, float sc) {
   using G = GemmShape<BM, BN>;
   constexpr int GBK = G::GBK;
   constexpr int FM = G::FM, FN = G::FN, PERW = G::PERW, STAGE = G::STAGE;
@@ -268,6 +269,9 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const bf16* __restric
         }
       }
     } else {
+      if (n >= sc_c0 && n < sc_c1)  // a column block stored scaled (8-column segments never straddle)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) y[q] *= sc;
       bf16x8 o;
 #pragma unroll
       for (int q = 0; q < 8; ++q) o[q] = (bf16)y[q];
@@ -512,10 +516,13 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__
 hipError_t launch_gemm_ex(const void* A, int64_t lda, const void* W, int64_t ldw, const float* bias,
                           const void* R, int64_t ldr, void* C, int64_t ldc, int64_t M, int N, int K,
                           int silu, int bf16flag, int out_f32, int splits, int64_t ksplit,
-                          int64_t c_split, void* act, hipStream_t s, void* lo, int lo_c0) {
+                          int64_t c_split, void* act, hipStream_t s, void* lo, int lo_c0,
+                          int sc_c0, int sc_c1, float sc) {
   if (M <= 0 || N <= 0) return hipSuccess;
   if (act && (!bf16flag || !out_f32 || splits > 1 || silu)) return hipErrorInvalidValue;
   if (lo && (!bf16flag || (out_f32 && !act) || splits > 1 || lo_c0 % 8 != 0))
+    return hipErrorInvalidValue;
+  if (sc_c1 > sc_c0 && (!bf16flag || out_f32 || sc_c0 % 8 != 0 || sc_c1 % 8 != 0))
     return hipErrorInvalidValue;
   if (bf16flag) {
     // the DMA and the epilogue move 16-byte rows segments
@@ -537,7 +544,7 @@ hipError_t launch_gemm_ex(const void* A, int64_t lda, const void* W, int64_t ldw
       hipLaunchKernelGGL((gemm_bf16_kernel<T, T, O>), dim3(tn * tm, splits), dim3(256), 0, s,
                          (const bf16*)A, lda, (const bf16*)W, ldw, bias, (const bf16*)R, ldr, (O*)C,
                          ldc, M, N, K, silu, tn, tn * tm, ksplit, c_split, (bf16*)act,
-                         (bf16*)lo, lo_c0);
+                         (bf16*)lo, lo_c0, sc_c0, sc_c1, sc);
     };
     using I128 = std::integral_constant<int, 128>;
     using I64 = std::integral_constant<int, 64>;
@@ -586,9 +593,10 @@ hipError_t launch_gemm_tn(const void* A, int64_t lda, const void* B, int64_t ldb
 
 hipError_t launch_gemm(const void* A, int64_t lda, const void* W, int64_t ldw, const float* bias,
                        const void* R, int64_t ldr, void* C, int64_t ldc, int64_t M, int N, int K,
-                       int silu, int bf16flag, hipStream_t s, void* lo, int lo_c0) {
+                       int silu, int bf16flag, hipStream_t s, void* lo, int lo_c0, int sc_c0,
+                       int sc_c1, float sc) {
   return launch_gemm_ex(A, lda, W, ldw, bias, R, ldr, C, ldc, M, N, K, silu, bf16flag, 0, 1, K, 0,
-                        nullptr, s, lo, lo_c0);
+                        nullptr, s, lo, lo_c0, sc_c0, sc_c1, sc);
 }
 
 }  // namespace hstu

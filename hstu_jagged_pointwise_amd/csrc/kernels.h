@@ -19,6 +19,10 @@ inline int64_t key_range_slots(int64_t total, int batch) { return total / 32 + b
 
 // One attention launch. Row strides (ld_*) are in elements. Tensor bases point
 // at head 0 of row 0; head h sits at column h * d within each row.
+// -log2(e): the factor the library's f1 projection applies to the queries it stores for
+// the MFMA attention in candidate mode and in layers (split scores)
+constexpr float kQueryPrescale = -1.4426950408889634f;
+
 struct AttnArgs {
   const void* q;
   const void* k;
@@ -54,7 +58,9 @@ struct AttnArgs {
   int64_t keys_per_split;
   int64_t part_stride;
   // causal mode, MFMA kernel, optional: the lo parts of q and k (same strides as q and k),
-  // so that each score is formed from ~16-bit queries and keys (hi.hi + lo.hi + hi.lo)
+  // so that each score is formed from ~16-bit queries and keys (hi.hi + lo.hi + hi.lo).
+  // The MFMA kernel in candidate mode and with these lo parts takes queries pre-scaled by
+  // kQueryPrescale (see attn_mfma.hip); the f1 projection stores them so.
   const void* q_lo;
   const void* k_lo;
   // candidate mode, MFMA kernel: where split 0 writes each candidate's self weight
@@ -132,10 +138,13 @@ hipError_t launch_ln_gate(const float* o, int64_t ld_o, int nsplit, int64_t spli
 // lo (bf16 output only): for columns n >= lo_c0 (a multiple of 8) also writes
 // lo[m, n] = bf16(y - bf16(y)), the part of the fp32 result y that the bf16 C drops, with
 // C's leading dimension; C + lo then carries y to about 16 significant bits.
+// Columns [sc_c0, sc_c1) (multiples of 8; bf16 output only) are stored as sc * y (the
+// remainder then belongs to the scaled value).
 hipError_t launch_gemm(const void* A, int64_t lda, const void* W, int64_t ldw,
                        const float* bias, const void* R, int64_t ldr, void* C, int64_t ldc,
                        int64_t M, int N, int K, int silu, int use_bf16, hipStream_t s,
-                       void* lo = nullptr, int lo_c0 = 0);
+                       void* lo = nullptr, int lo_c0 = 0, int sc_c0 = 0, int sc_c1 = 0,
+                       float sc = 1.f);
 
 // launch_gemm with an fp32 output (bf16 inputs; fp32 inputs always write fp32) and
 // split-K: grid dimension y = splits, split y covers K range [y*ksplit, (y+1)*ksplit)
@@ -147,7 +156,7 @@ hipError_t launch_gemm_ex(const void* A, int64_t lda, const void* W, int64_t ldw
                           const void* R, int64_t ldr, void* C, int64_t ldc, int64_t M, int N, int K,
                           int silu, int use_bf16, int out_f32, int splits, int64_t ksplit,
                           int64_t c_split, void* act, hipStream_t s, void* lo = nullptr,
-                          int lo_c0 = 0);
+                          int lo_c0 = 0, int sc_c0 = 0, int sc_c1 = 0, float sc = 1.f);
 
 // C[M,N] = sum_k A[k,m] B[k,n] (bf16 A [K, lda] and B [K, ldb] row-major, fp32 C): the
 // weight-gradient form, contraction over rows. M, N and both leading dimensions multiples
