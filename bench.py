@@ -103,6 +103,46 @@ def time_calls(fn, stream, steps, warmup, warm_s=0.0):
     return np.array([s.elapsed_time(e) for s, e in zip(starts, ends)]), wall
 
 
+MALL_FLUSH_BYTES = 512 << 20  # twice the 256 MB last-level cache (MALL)
+
+
+def time_calls_cold(fn, stream, steps):
+    """Per-call durations (ms) with the last-level cache flushed before each call: a 512 MB
+    buffer is written on the same stream between calls, outside the timed events, so that
+    every call reads its inputs from HBM."""
+    import torch
+    flush = torch.empty(MALL_FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    fn()
+    torch.cuda.synchronize()
+    for i in range(steps):
+        flush.fill_(i & 0xff)
+        starts[i].record(stream)
+        fn()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    return np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
+
+
+def layer_bytes(x, split_qk=True):
+    """Algorithmic HBM bytes of one layer as its four steps run here, each step reading its
+    inputs once and writing its outputs once (bf16 activations and weights, fp32 attention
+    rows for the gate, int64 timestamps): f1 reads X and W1 and writes U|V|Q|K (plus the
+    bf16 remainder of Q and K that the split-precision scores read); the attention reads
+    Q, K, V (and the remainders) and the timestamps and writes fp32 O; the gate reads O
+    and U and writes G; f2 reads G and W2 and writes Y."""
+    T, dm, H, dqk, dv = int(x.offsets[-1]), x.d_model, x.num_heads, x.d_qk, x.d_v
+    f1c = 2 * H * (dqk + dv)
+    lo = 2 * H * dqk if split_qk else 0
+    f1 = T * dm * 2 + f1c * dm * 2 + T * (f1c + lo) * 2
+    attn = T * (2 * H * dqk + lo + H * dv) * 2 + T * 8 + T * H * dv * 4
+    gate = T * H * dv * 4 + T * H * dv * 2 * 2
+    f2 = T * H * dv * 2 + dm * H * dv * 2 + T * dm * 2
+    return {"f1": f1, "attention": attn, "ln_gate": gate, "f2": f2,
+            "total": f1 + attn + gate + f2}
+
+
 def leg_attention(steps, warmup, warm_s=0.0):
     import torch
     from hstu_jagged_pointwise_amd import ops, synth
@@ -131,34 +171,80 @@ def leg_attention(steps, warmup, warm_s=0.0):
 
 
 # Vector-ALU side of the attention's roofline. Every score goes through SiLU on the vector
-# ALU: in the kernel's fast path, per score, one exp2 and one reciprocal (transcendental)
-# plus a multiply, an add, a multiply and half of a two-value bf16 convert (ordinary fp32
-# ops, packed fp32 disabled). Rates from the chip's unit counts: 256 CUs x 4 SIMDs x 16
-# lanes x 2.4 GHz ordinary lane-ops/s; transcendentals at half that (measured on the
-# device: a wave64 exp2 or reciprocal takes twice the cycles of an fp32 FMA).
+# ALU. The instruction counts per score come from the committed hardware-counter record of
+# the attention kernel (profiles/attn_long_counters.json: SQ_INSTS_VALU, SQ_INSTS_MFMA and
+# SQ_INSTS_VALU_TRANS_F32 per dispatch, wave instructions of 64 lanes) when it was taken on
+# the current kernel source; otherwise from the kernel's fast path as written (2
+# transcendentals and 3.5 ordinary ops per score, plus one accumulator-start move). Rates
+# from the chip's unit counts: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz ordinary lane-ops/s
+# (packed fp32 disabled); transcendentals at half that (measured on the device: a wave64
+# exp2 or reciprocal takes twice the cycles of an fp32 FMA).
 VALU_PLAIN_PER_S = 256 * 4 * 16 * 2.4e9
 VALU_TRANS_PER_S = VALU_PLAIN_PER_S / 2
-SILU_OPS = {"transcendental": 2.0, "plain": 3.5}
+FAST_PATH_OPS = {"transcendental": 2.0, "plain": 4.5}
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "attn_long_counters.json")
+
+
+def counter_record():
+    """The committed counter record, if it was taken on the current attention source."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    rec = json.load(open(COUNTERS_FILE))
+    return rec if rec.get("source_hash") == source_hash() else None
 
 
 def valu_ceiling(attn):
     scores = attn["pairs"] * attn["x"].num_heads
-    t_valu = scores * (SILU_OPS["plain"] / VALU_PLAIN_PER_S +
-                       SILU_OPS["transcendental"] / VALU_TRANS_PER_S)
+    rec = counter_record()
+    if rec:
+        c = rec["counters_per_dispatch"]
+        trans = c["SQ_INSTS_VALU_TRANS_F32"] * 64 / scores
+        plain = (c["SQ_INSTS_VALU"] - c["SQ_INSTS_MFMA"] - c["SQ_INSTS_VALU_TRANS_F32"]) * 64 / scores
+        ops = {"transcendental": round(trans, 3), "plain": round(plain, 3),
+               "source": "hardware counters of this kernel source (profiles/attn_long_counters.json)"}
+        cyc = c["SQ_CYCLES"] / rec["shader_engines"]  # per SIMD (the counter sums the engines)
+        busy = {"mfma_busy": round(c["SQ_VALU_MFMA_BUSY_CYCLES"] / rec["simds"] / cyc, 4),
+                "valu_busy": round(4 * c["SQ_ACTIVE_INST_VALU"] / rec["simds"] / cyc, 4),
+                "mfma_and_valu": round(c["SQ_VALU_MFMA_COEXEC_CYCLES"] / rec["simds"] / cyc, 4),
+                "note": "fractions of each SIMD's cycles over the dispatch, from the counters"}
+    else:
+        ops = dict(FAST_PATH_OPS, source="the kernel's fast path as written (no counter record "
+                                         "for this kernel source)")
+        busy = None
+    t_valu = scores * (ops["plain"] / VALU_PLAIN_PER_S + ops["transcendental"] / VALU_TRANS_PER_S)
     valu_tf = attn["flops"] / t_valu / 1e12
     both_tf = 1.0 / (1.0 / PEAK_BF16_TFLOPS + 1.0 / valu_tf)
-    return {"scores": int(scores), "ops_per_score": SILU_OPS,
-            "ceiling": round(valu_tf, 1), "mfma_plus_valu_ceiling": round(both_tf, 1),
-            "unit": "TFLOP/s", "frac_of_mfma_plus_valu": round(attn["tflops"] / both_tf, 4),
-            "note": "ceiling: the SiLU vector work alone at the vector-ALU rate; "
-                    "mfma_plus_valu: MFMA at peak and SiLU at that rate, not overlapped"}
+    out = {"scores": int(scores), "ops_per_score": ops,
+           "ceiling": round(valu_tf, 1), "mfma_plus_valu_ceiling": round(both_tf, 1),
+           "unit": "TFLOP/s", "frac_of_mfma_plus_valu": round(attn["tflops"] / both_tf, 4),
+           "note": "ceiling: the vector work alone at the vector-ALU rate; mfma_plus_valu: MFMA "
+                   "at peak and the vector work at that rate, not overlapped"}
+    if busy:
+        out["busy"] = busy
+    return out
 
 
-def leg_mfalcon(steps, warmup):
+def mfalcon_flops(x):
+    """Algorithmic FLOPs of one mfalcon_score call: per layer, the candidates' f1 and f2 and
+    their attention to n_h history keys plus themselves; the history's f1 (its keys and
+    values) and, below the last layer, the history's whole layer."""
+    C = int(x.cand_offsets[-1])
+    n_h = int(x.hist_offsets[-1])
+    H, dqk, dv, dm, L = x.num_heads, x.d_qk, x.d_v, x.d_model, len(x.layers)
+    f1 = 2 * dm * 2 * H * (dqk + dv)
+    f2 = 2 * H * dv * dm
+    cand = C * (L * (f1 + f2) + L * (n_h + 1) * H * 2 * (dqk + dv))
+    lens = np.diff(x.hist_offsets)
+    hist_pairs = int(np.sum(lens * (lens + 1) // 2))
+    hist = n_h * f1 * L + (L - 1) * (n_h * f2 + hist_pairs * H * 2 * (dqk + dv))
+    return cand + hist
+
+
+def leg_mfalcon(steps, warmup, num_layers=1):
     import torch
     from hstu_jagged_pointwise_amd import ops, synth
     from hstu_jagged_pointwise_amd.device import mfalcon_to_device
-    x = synth.workload_mfalcon()
+    x = synth.workload_mfalcon(num_layers=num_layers)
     d = mfalcon_to_device(x)
     stream = torch.cuda.Stream()
     ld = ops.layer_desc(d["layers"], 1, x.num_heads, x.d_qk, x.d_v, x.d_model, x.max_seq_len,
@@ -199,16 +285,19 @@ def leg_mfalcon(steps, warmup):
     mean = float(ms.mean())
     cmean = float(cms.mean())
     n_h = int(x.hist_offsets[-1])
-    hd = x.num_heads
-    attn_flops = C * (n_h + 1) * hd * 2 * (x.d_qk + x.d_v)
-    proj_flops = C * 2 * x.d_model * (2 * hd * (x.d_qk + x.d_v) + hd * x.d_v)
-    hist_flops = n_h * 2 * x.d_model * 2 * hd * (x.d_qk + x.d_v)
-    return dict(candidates=C, ms=mean, candidates_per_s=C / (mean * 1e-3),
-                tflops=(attn_flops + proj_flops + hist_flops) / (mean * 1e-3) / 1e12,
+    flops = mfalcon_flops(x)
+    tf = flops / (mean * 1e-3) / 1e12
+    return dict(candidates=C, ms=round(mean, 4), candidates_per_s=C / (mean * 1e-3),
+                tflops=round(tf, 2),
+                roofline={"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+                          "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                          "flops_per_call": int(flops),
+                          "note": "the whole call (history pass included); FLOPs of the "
+                                  "projections and of the attention over useful pairs only"},
                 candidates_only=dict(ms=round(cmean, 4), candidates_per_s=C / (cmean * 1e-3),
                                      note="mfalcon_score_cached against a history cache built "
                                           "once by mfalcon_history"),
-                microbatch=x.microbatch, history=n_h, layers=1)
+                microbatch=x.microbatch, in_flight=4, history=n_h, layers=num_layers)
 
 
 def leg_layers(steps, warmup):
@@ -233,6 +322,7 @@ def leg_layers(steps, warmup):
 
         with torch.cuda.stream(stream):
             ms, _ = time_calls(call, stream, steps, warmup)
+            cold = time_calls_cold(call, stream, max(10, steps // 4))
         L = len(x.layers)
         T = int(x.offsets[-1])
         pairs = int(np.sum(x.lengths * (x.lengths + 1) // 2))
@@ -240,8 +330,21 @@ def leg_layers(steps, warmup):
         f2 = T * 2 * x.num_heads * x.d_v * x.d_model
         at = pairs * x.num_heads * 2 * (x.d_qk + x.d_v)
         mean = float(ms.mean())
-        res[name] = dict(tokens=T, layers=L, ms_per_call=mean, us_per_layer=mean * 1e3 / L,
-                         tflops=L * (f1 + f2 + at) / (mean * 1e-3) / 1e12)
+        cmean = float(cold.mean())
+        tf = L * (f1 + f2 + at) / (mean * 1e-3) / 1e12
+        by = layer_bytes(x)
+        gbs = L * by["total"] / (mean * 1e-3) / 1e9
+        cgbs = L * by["total"] / (cmean * 1e-3) / 1e9
+        res[name] = dict(tokens=T, layers=L, ms_per_call=round(mean, 4),
+                         us_per_layer=round(mean * 1e3 / L, 2), tflops=round(tf, 2),
+                         mfma_frac=round(tf / PEAK_BF16_TFLOPS, 4),
+                         bytes_per_layer=by, hbm_gbs=round(gbs, 1),
+                         hbm_frac=round(gbs / PEAK_HBM_GBS, 4),
+                         cold=dict(ms_per_call=round(cmean, 4),
+                                   us_per_layer=round(cmean * 1e3 / L, 2),
+                                   hbm_gbs=round(cgbs, 1), hbm_frac=round(cgbs / PEAK_HBM_GBS, 4),
+                                   note="512 MB written between calls (last-level cache "
+                                        "flushed), outside the timed events"))
     return res
 
 
@@ -437,6 +540,11 @@ def main():
         log("M-FALCON leg")
         result["mfalcon"] = leg_mfalcon(args.steps, args.warmup)
         log(f"M-FALCON: {result['mfalcon']['candidates_per_s']:.3e} candidates/s")
+        log("M-FALCON leg, 4 layers")
+        result["mfalcon_4_layers"] = leg_mfalcon(max(10, args.steps // 4), args.warmup,
+                                                 num_layers=4)
+        log(f"M-FALCON 4 layers: {result['mfalcon_4_layers']['candidates_per_s']:.3e} "
+            "candidates/s")
     if "layers" in legs:
         log("layer legs")
         result["layers"] = leg_layers(args.steps, args.warmup)
