@@ -64,6 +64,18 @@ constexpr int MBM = kMfmaRows;  // 128 query rows per workgroup
 constexpr int MBN = 64;         // keys per LDS tile
 constexpr int kMaxP = 1024;     // position-table entries kept in LDS
 constexpr int kTimeTab = 64;    // time-table entries ever reachable (buckets <= 63)
+constexpr int kBufferWord3 = 0x00020000;  // buffer descriptor dword 3: 32-bit data format, raw
+
+// One 16-byte-per-lane buffer load into LDS: lane L's chunk at base + voff lands in
+// slot L of the 1 KiB span at lds. The descriptor's record count is limoff + 16, the
+// end of the last valid chunk: a lane past it reads zeros. (The flat-encoded global
+// form would make the compiler count every fetch against the LDS counter as well, so
+// that a wait for an LDS read would also wait for the fetches in flight.)
+__device__ __forceinline__ void fetch16(const char* base, uint32_t limoff, bf16* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)(limoff + 16u), kBufferWord3),
+      (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
+}
 
 __device__ __forceinline__ bf16x8 load_bf16x8(const bf16* p) {
   return *reinterpret_cast<const bf16x8*>(p);
@@ -286,13 +298,12 @@ attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[c][r] = 0.f;
 
-  // ---- key tiles go global -> LDS directly (global_load_lds_dwordx4): lane L of one
-  // instruction fills 16-byte slot L of a contiguous 1 KiB span, so the LDS layout
+  // ---- key tiles go global -> LDS directly (buffer_load_dwordx4 ... lds): lane L of
+  // one instruction fills 16-byte slot L of a contiguous 1 KiB span, so the LDS layout
   // comes from which source chunk each lane fetches. K rows are padded by one slot
   // (row-fragment reads, see tile_off); V rows are unpadded with their 16-byte chunks
-  // permuted by an XOR of the row (see vtile_off). Rows past the data fetch the last
-  // chunk of the last valid row instead: their scores are masked and multiply finite
-  // values.
+  // permuted by an XOR of the row (see vtile_off). Rows past the data read zeros (see
+  // fetch16): their scores are masked, and they multiply P = 0.
   constexpr int SPR = CPR + 1;        // 16-byte slots per K row
   constexpr int NSLOT = MBN * SPR;    // slots per K tile
   constexpr int NINSTR = NSLOT / 64;  // wave-instructions per K tile
@@ -301,10 +312,10 @@ attn_mfma_kernel(AttnArgs a) {
   static_assert(MBN * CPR == 4 * 64 * (NIW - 1), "each wavefront issues NIW - 1 V instructions");
   // Wavefront w issues instructions w, w+4, w+8, ... of each matrix tile. The byte
   // offset of each of its slots' source chunk from the tile's first row is computed
-  // once (K and V share the row stride). The address is a uniform base plus that
-  // 32-bit offset (the scalar-base form of the instruction). Offsets grow with the row
-  // (a row's chunks span less than the row stride), so one unsigned minimum against the
-  // offset of the last valid row's last chunk keeps every fetch inside the data.
+  // once (K and V share the row stride). The address is the tile's base (a buffer
+  // descriptor) plus that 32-bit offset. Offsets grow with the row (a row's chunks span
+  // less than the row stride), so a record count that ends at the last valid row's last
+  // chunk keeps every fetch inside the data.
   const uint32_t ldb = (uint32_t)(a.ld_k * 2);
   uint32_t offk[NIW], offv[NIW - 1];
 #pragma unroll
@@ -326,7 +337,8 @@ attn_mfma_kernel(AttnArgs a) {
     const char* vb;
     const char* klb;  // K lo parts (SPLIT), same row stride as K
     uint32_t lim;     // last key row of the data, counted from the tile's first row
-    uint32_t limoff;  // offset of that row's last chunk (rows past the tile: its last row's)
+    uint32_t limoff;  // offset of that row's last chunk (rows past the tile: its last row's);
+                      // the descriptor's record count is limoff + 16
   };
   auto lim_off = [&](uint32_t lim) {
     return (lim < (uint32_t)MBN - 1 ? lim : (uint32_t)MBN - 1) * ldb + 16u * (CPR - 1);
@@ -346,17 +358,9 @@ attn_mfma_kernel(AttnArgs a) {
     bf16* Kd = buf ? Ks1 : Ks0;
     bf16* Vd = buf ? Vs1 : Vs0;
     const int i = wu + 4 * j;
-    __builtin_amdgcn_global_load_lds(
-        (const __attribute__((address_space(1))) void*)(src.kb + min(offk[j], src.limoff)),
-        (__attribute__((address_space(3))) void*)(&Kd[512 * i]), 16, 0, 0);
-    if constexpr (SPLIT)
-      __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(src.klb + min(offk[j], src.limoff)),
-          (__attribute__((address_space(3))) void*)(&(buf ? Kl1 : Kl0)[512 * i]), 16, 0, 0);
-    if (j < NIW - 1)
-      __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(src.vb + min(offv[j], src.limoff)),
-          (__attribute__((address_space(3))) void*)(&Vd[512 * i]), 16, 0, 0);
+    fetch16(src.kb, src.limoff, &Kd[512 * i], offk[j]);
+    if constexpr (SPLIT) fetch16(src.klb, src.limoff, &(buf ? Kl1 : Kl0)[512 * i], offk[j]);
+    if (j < NIW - 1) fetch16(src.vb, src.limoff, &Vd[512 * i], offv[j]);
   };
   static_assert(NINSTR == 4 * (NIW - 1) + 1, "only wavefront 0 issues a last K instruction");
   auto dma_tile = [&](auto bufc, const DmaSrc& src) {
@@ -521,12 +525,17 @@ attn_mfma_kernel(AttnArgs a) {
     // buckets each (the fast path's schedule plus a per-element two-bucket select)
     const bool fast2 = !CAND && (cls.f & 0x1717u) == 0x0505u;
     constexpr int E = 16 / NKK;  // scores activated per interleaved step
-    // SiLU of accumulator slots st*E .. st*E+E-1 into bf16 A fragments
-    auto act_step = [&](const f32x16& x, bf16x8* pa, int st) {
+    // SiLU of accumulator slots st*E .. st*E+E-1 into bf16 A fragments, as c SiLU(x)
+    // with c = -log2(e) (the output scale divides c out again). Pre-scaled scores
+    // arrive as c x with their bias inside; otherwise a block on the fast paths starts
+    // its S^T chain from 0 and its constant bias, scaled, is cb, which joins the score
+    // in the same fma that scales it (cb = 0 when the accumulator holds the bias).
+    auto act_step = [&](const f32x16& x, float cb, bf16x8* pa, int st) {
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         const int r = st * E + e;
-        pa[r >> 3][r & 7] = (bf16)(PRE ? silu_prescaled(x[r]) : silu_fast(x[r]));
+        const float xp = PRE ? x[r] : fmaf(x[r], kPre, cb);
+        pa[r >> 3][r & 7] = (bf16)silu_prescaled(xp);
       }
     };
     // the start of a block's S^T accumulator: the block's constant bias, or, given keyA,
@@ -579,6 +588,13 @@ attn_mfma_kernel(AttnArgs a) {
     // exactly 0.
     bf16x8 pa0[2];
     f32x16 x1;
+    // the fast paths' constant biases (plain causal mode: the chains start from 0 and
+    // each block's constant joins its SiLU), else 0
+    const float cb0 = PRE ? 0.f : kPre * (pb + c0.tlo);
+    const float cb1 = PRE ? 0.f : kPre * (pb + c1.tlo);
+    float cba = 0.f, cbb = 0.f;  // the constants of block 0 and block 1 as activated
+    const float sb0 = PRE ? pb + c0.tlo : 0.f;  // the fast paths' accumulator starts
+    const float sb1 = PRE ? pb + c1.tlo : 0.f;
     // Common case: both blocks live, no mask, one position bucket and one time
     // bucket per block, so the bias is a constant that starts the accumulator. The
     // path is one basic block (no branch, so nothing moves across the fences);
@@ -611,19 +627,21 @@ attn_mfma_kernel(AttnArgs a) {
         kA[0] = __builtin_bit_cast(bf16x8, f0);
         kA[1] = __builtin_bit_cast(bf16x8, f1);
       }
-      const f32x16 s0 = s_chain(0, pb + c0.tlo, CAND && keyb ? &kA[0] : nullptr, true);
+      cba = cb0;
+      cbb = cb1;
+      const f32x16 s0 = s_chain(0, sb0, CAND && keyb ? &kA[0] : nullptr, true);
       bf16x8 k1[NKK], k1l[SPLIT ? NKK : 1];
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
         k1[kk] = kfrag(Kt, 1, kk);
         if constexpr (SPLIT) k1l[kk] = kfrag(Klt, 1, kk);
       }
-      f32x16 s1 = bias_step(pb + c1.tlo, CAND && keyb ? &kA[1] : nullptr);
+      f32x16 s1 = bias_step(sb1, CAND && keyb ? &kA[1] : nullptr);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
         s1 = s_step(s1, k1[kk], k1l[SPLIT ? kk : 0], kk);
-        act_step(s0, pa0, kk);
+        act_step(s0, cba, pa0, kk);
         __builtin_amdgcn_sched_barrier(0);
       }
       x1 = s1;
@@ -650,7 +668,9 @@ attn_mfma_kernel(AttnArgs a) {
     // Fast path with two-bucket blocks (causal mode): the fast path's order, each
     // block's scores corrected right after its S^T chain.
     auto fast2_path = [&]() {
-      f32x16 s0 = s_chain(0, pb + c0.tlo, nullptr, true);
+      cba = cb0;
+      cbb = cb1;
+      f32x16 s0 = s_chain(0, sb0, nullptr, true);
       if (c0.tmode() == 1) two_bucket(s0, 0, c0);
       bf16x8 k1[NKK], k1l[SPLIT ? NKK : 1];
 #pragma unroll
@@ -658,12 +678,12 @@ attn_mfma_kernel(AttnArgs a) {
         k1[kk] = kfrag(Kt, 1, kk);
         if constexpr (SPLIT) k1l[kk] = kfrag(Klt, 1, kk);
       }
-      f32x16 s1 = bias_step(pb + c1.tlo, nullptr);
+      f32x16 s1 = bias_step(sb1, nullptr);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
         s1 = s_step(s1, k1[kk], k1l[SPLIT ? kk : 0], kk);
-        act_step(s0, pa0, kk);
+        act_step(s0, cba, pa0, kk);
         __builtin_amdgcn_sched_barrier(0);
       }
       if (c1.tmode() == 1) two_bucket(s1, 1, c1);
@@ -751,7 +771,7 @@ attn_mfma_kernel(AttnArgs a) {
       for (int j = 0; j < NIW - 1; ++j) dma(j);
       const f32x16 x0 = general_block(0, c0);
 #pragma unroll
-      for (int st = 0; st < NKK; ++st) act_step(x0, pa0, st);
+      for (int st = 0; st < NKK; ++st) act_step(x0, 0.f, pa0, st);
       x1 = general_block(1, c1);
     };
 
@@ -781,7 +801,7 @@ attn_mfma_kernel(AttnArgs a) {
       for (int m = 0; m < NPV; ++m) {
         const bf16x8 vnext = vfrag(Vt, m + 1 < NPV ? 0 : 1, (m + 1) % NPV);
         o[m % NC] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa0[m / NC], vb, o[m % NC], 0, 0, 0);
-        act_step(x1, pa1, m);
+        act_step(x1, cbb, pa1, m);
         vb = vnext;
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -803,7 +823,7 @@ attn_mfma_kernel(AttnArgs a) {
   __syncthreads();
   if (!wave_live) return;
 
-  const float oscale = PRE ? a.inv_n / kPre : a.inv_n;
+  const float oscale = a.inv_n / kPre;  // P carries c = -log2(e)
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int rw = 8 * (r >> 2) + 4 * hl + (r & 3);  // row within the wavefront
