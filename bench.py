@@ -175,13 +175,14 @@ def leg_attention(steps, warmup, warm_s=0.0):
 # the attention kernel (profiles/attn_long_counters.json: SQ_INSTS_VALU, SQ_INSTS_MFMA and
 # SQ_INSTS_VALU_TRANS_F32 per dispatch, wave instructions of 64 lanes) when it was taken on
 # the current kernel source; otherwise from the kernel's fast path as written (2
-# transcendentals and 3.5 ordinary ops per score, plus one accumulator-start move). Rates
+# transcendentals and 3.5 ordinary ops per score: the fma that scales the score and adds its
+# block's constant bias, SiLU's add and multiply, half a pack). Rates
 # from the chip's unit counts: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz ordinary lane-ops/s
 # (packed fp32 disabled); transcendentals at half that (measured on the device: a wave64
 # exp2 or reciprocal takes twice the cycles of an fp32 FMA).
 VALU_PLAIN_PER_S = 256 * 4 * 16 * 2.4e9
 VALU_TRANS_PER_S = VALU_PLAIN_PER_S / 2
-FAST_PATH_OPS = {"transcendental": 2.0, "plain": 4.5}
+FAST_PATH_OPS = {"transcendental": 2.0, "plain": 3.5}
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "attn_long_counters.json")
 
 
