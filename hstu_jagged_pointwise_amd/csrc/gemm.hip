@@ -29,9 +29,32 @@ constexpr int NST = 4;  // LDS ring stages: NST-1 stages load while one is multi
 // K per pipeline stage of a BM-row tile
 constexpr int stage_k(int bm) { return bm >= 128 ? 32 : 64; }
 
+// s_waitcnt vmcnt(N) through the builtin (gfx9 encoding: vmcnt in bits 3:0 and 15:14,
+// expcnt and lgkmcnt at their maxima), so that the compiler sees it.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// One 16-byte-per-lane load into LDS (buffer_load_dwordx4 ... lds): lane L's 16 bytes at
+// base + voff land in slot L of the 1 KiB span at lds. The descriptor has no range limit:
+// the callers keep every address inside the data. Written as assembly, so that the
+// compiler does not track these loads: the next stage's loads are issued between the
+// current stage's MFMAs, and with the loads visible the compiler would make the LDS
+// reads after each such branch wait for every load in flight. The ring's own waits
+// (wait_vmcnt before each barrier) order the loads with the reads. The instruction has
+// no register result; its operands (offset, descriptor, M0) are read when it issues.
+__device__ __forceinline__ void stage_fetch(const char* base, bf16* lds, uint32_t voff) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, -1, 0x00020000);
+  const uint32_t m0v = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds;
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %0, %1, 0 offen lds"
+      :
+      : "v"(voff), "s"(r), "s"(m0v)
+      : "memory", "m0");
 }
 // Workgroup barrier that leaves in-flight global->LDS loads alone (__syncthreads
 // also waits for every outstanding vector memory operation, which would drain the
@@ -134,18 +157,16 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const bf16* __restric
   // that lie past K fetch that one instead (they are zeroed in LDS before use), so no
   // load leaves the row
   const uint32_t klast = (uint32_t)(K - 8) * 2u;
-  auto issue = [&](auto bufc, int ks) {
+  // this wavefront's instruction j of stage ks
+  auto issue_one = [&](auto bufc, int ks, int j) {
     constexpr int buf = decltype(bufc)::value;
     bf16* D = buf == 0 ? S0 : buf == 1 ? S1 : buf == 2 ? S2 : S3;
     const uint32_t kb = (uint32_t)ks * GBK * 2;
+    stage_fetch(isA[j] ? abase : wbase, &D[512 * (wu + 4 * j)], soff[j] + min(kb + coff[j], klast));
+  };
+  auto issue = [&](auto bufc, int ks) {
 #pragma unroll
-    for (int j = 0; j < PERW; ++j) {
-      const int i = wu + 4 * j;
-      const char* src = (isA[j] ? abase : wbase) + soff[j] + min(kb + coff[j], klast);
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                       (__attribute__((address_space(3))) void*)(&D[512 * i]), 16,
-                                       0, 0);
-    }
+    for (int j = 0; j < PERW; ++j) issue_one(bufc, ks, j);
   };
   f32x16 acc[FM][FN];
 #pragma unroll
@@ -154,7 +175,10 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const bf16* __restric
     for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-  auto compute = [&](auto bufc, int ks) {
+  // the MFMAs of stage ks, with this wavefront's loads of stage ks+NST-1 (into buffer
+  // nbufc) issued one after each MFMA when `more`: a load can wait for room in the memory
+  // pipeline, and the MFMAs issued before it run meanwhile
+  auto compute = [&](auto bufc, int ks, auto nbufc, bool more) {
     constexpr int buf = decltype(bufc)::value;
     bf16* D = buf == 0 ? S0 : buf == 1 ? S1 : buf == 2 ? S2 : S3;
     if ((ks + 1) * GBK > K) {  // K tail: zero the chunks past K (uniform branch, last stage only)
@@ -181,9 +205,16 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const bf16* __restric
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
+        for (int j = 0; j < FN; ++j) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          const int n = (kk * FM + i) * FN + j;  // this stage's MFMA count so far
+          if (n < PERW && more) issue_one(nbufc, ks + NST - 1, n);
+        }
     }
+    constexpr int NMF = (GBK / 16) * FM * FN;
+#pragma unroll
+    for (int n = NMF; n < PERW; ++n)
+      if (more) issue_one(nbufc, ks + NST - 1, n);
   };
   // prologue: NST-1 stages in flight
   using B0 = std::integral_constant<int, 0>;
@@ -201,9 +232,9 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const bf16* __restric
     else if (ks + 1 < nks) wait_vmcnt<PERW>();
     else wait_vmcnt<0>();
     lds_barrier();
-    // the buffer of stage ks-1 is free (every wavefront passed this barrier after using it)
-    if (ks + NST - 1 < nks) issue(BI{}, ks + NST - 1);
-    compute(bufc, ks);
+    // the buffer of stage ks-1 is free (every wavefront passed this barrier after using it);
+    // stage ks+NST-1 goes into it during this stage's MFMAs
+    compute(bufc, ks, BI{}, ks + NST - 1 < nks);
   };
   for (int ks = 0; ks < nks; ks += NST) {
     step(B0{}, ks);
