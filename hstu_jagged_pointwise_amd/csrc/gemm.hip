@@ -193,20 +193,26 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const bf16* __restric
       }
       lds_barrier();
     }
+    // every k-step's fragments are read first, so that the reads of later k-steps
+    // complete under the MFMAs of earlier ones
+    constexpr int NKS = GBK / 16;
+    bf16x8 af[NKS][FM], bfr[NKS][FN];
 #pragma unroll
-    for (int kk = 0; kk < GBK / 16; ++kk) {
-      bf16x8 af[FM], bfr[FN];
+    for (int kk = 0; kk < NKS; ++kk) {
 #pragma unroll
       for (int i = 0; i < FM; ++i)
-        af[i] = *reinterpret_cast<const bf16x8*>(&D[(wm * G::WM + 32 * i + l32) * GLD + 16 * kk + 8 * hl]);
+        af[kk][i] = *reinterpret_cast<const bf16x8*>(&D[(wm * G::WM + 32 * i + l32) * GLD + 16 * kk + 8 * hl]);
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8*>(&D[(BM + wn * G::WN + 32 * j + l32) * GLD + 16 * kk + 8 * hl]);
+        bfr[kk][j] = *reinterpret_cast<const bf16x8*>(&D[(BM + wn * G::WN + 32 * j + l32) * GLD + 16 * kk + 8 * hl]);
+    }
+#pragma unroll
+    for (int kk = 0; kk < NKS; ++kk) {
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[kk][i], bfr[kk][j], acc[i][j], 0, 0, 0);
           const int n = (kk * FM + i) * FN + j;  // this stage's MFMA count so far
           if (n < PERW && more) issue_one(nbufc, ks + NST - 1, n);
         }
