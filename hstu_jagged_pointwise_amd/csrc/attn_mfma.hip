@@ -63,6 +63,11 @@ namespace {
 constexpr int MBM = kMfmaRows;  // 128 query rows per workgroup
 constexpr int MBN = 64;         // keys per LDS tile
 constexpr int kMaxP = 1024;     // position-table entries kept in LDS
+// The position table in LDS is padded on both sides with its clamped values: entry
+// kPadLo + d holds rab_pos[min(max(d, 0), P - 1)] for d = -kPadLo .. P - 1 + kPadHi. A
+// 32 x 32 block whose bucket varies has every i - j in that range (see general_block), so
+// its elements read the table at one base plus constant offsets, with no clamping.
+constexpr int kPadLo = 64, kPadHi = 64;
 constexpr int kTimeTab = 64;    // time-table entries ever reachable (buckets <= 63)
 constexpr int kBufferWord3 = 0x00020000;  // buffer descriptor dword 3: 32-bit data format, raw
 
@@ -133,7 +138,6 @@ __device__ __forceinline__ int bucket_of(int64_t dt, int T) {
 //   bit 2 pos_c    one position bucket over the block (or no position bias)
 //   bits 3-4 tmode time bias: 0 one bucket (or none), 1 two adjacent buckets, 2 general
 //   bit 5 tfast    every elapsed time fits the 32-bit forms
-//   bit 6 tsorted  no elapsed time in the block is negative
 // and bits 16 + 8*kb .. 21 + 8*kb hold the block's highest time bucket bhi
 // (tmode 1: an element is in it when the 32-bit t_i + 1 - t_j >= 2^bhi).
 struct TileClass {
@@ -148,7 +152,6 @@ struct BlockClass {  // one block's view of a TileClass
   __device__ bool pos_c() const { return bits & 4u; }
   __device__ uint32_t tmode() const { return (bits >> 3) & 3u; }
   __device__ bool tfast() const { return bits & 32u; }
-  __device__ bool tsorted() const { return bits & 64u; }
   __device__ int thr() const { return (int)(1u << bhi); }
 };
 __device__ __forceinline__ BlockClass block_class(const TileClass& c, int kb) {
@@ -199,7 +202,7 @@ attn_mfma_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 Vs1[MBN * D];
   __shared__ __attribute__((aligned(16))) uint32_t tk_lo[2][MBN];
   __shared__ int64_t tk64[2][MBN];
-  __shared__ float rp[kMaxP];
+  __shared__ float rpx[kPadLo + kMaxP + kPadHi];
   __shared__ float rt[kTimeTab];
   __shared__ float rtc[32];
 
@@ -216,87 +219,12 @@ attn_mfma_kernel(AttnArgs a) {
                         a.key_ranges != nullptr;
   const int P = a.P, T = a.T;
 
-  if (has_pos)
-    for (int i = tid; i < P; i += 256) rp[i] = tscale * a.rab_pos[(int64_t)h * P + i];
-  if (has_time) {
-    if (tid < kTimeTab)
-      rt[tid] = tscale * a.rab_time[(int64_t)h * T + (tid < T - 1 ? tid : T - 1)];
-    if (tid < 32) {
-      const int bt = 31 - tid;
-      rtc[tid] = tscale * a.rab_time[(int64_t)h * T + (bt < T - 1 ? bt : T - 1)];
-    }
-  }
-  const float pb = has_pos ? tscale * sload(a.rab_pos + (int64_t)h * P + P - 1) : 0.f;  // P-1
-
-  // this lane's query row (the S^T column it holds) and its Q fragment
+  // this lane's query row (the S^T column it holds)
   const int wrow = 32 * w + l32;
   const bool row_ok = wrow < t.rows;
   const bool wave_live = 32 * wu < t.rows;
-  bf16x8 qf[NKK];
-  bf16x8 qlf[SPLIT ? NKK : 1];  // lo parts of the queries (SPLIT)
-#pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) {
-    const int64_t qo = (t.q_local + wrow) * a.ld_q + (int64_t)h * D + 16 * kk + 8 * hl;
-    if (row_ok) {
-      qf[kk] = load_bf16x8(q + qo);
-      if constexpr (SPLIT) qlf[kk] = load_bf16x8((const bf16*)a.q_lo + qo);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) qf[kk][i] = (bf16)0.f;
-      if constexpr (SPLIT)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) qlf[kk][i] = (bf16)0.f;
-    }
-  }
-  // candidate mode, first key range: the candidate's own key (relative position 0,
-  // elapsed time 0) is loaded with Q and its weight SiLU(score) / N stored per row and
-  // head, for the layer norm that follows to add weight * v_c (it reads the row anyway)
-  if (CAND && blockIdx.z == 0) {
-    const bf16* kc = (const bf16*)a.kc;
-    float part = 0.f;
-    if (row_ok) {
-      bf16x8 kf[NKK];
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk)
-        kf[kk] = load_bf16x8(kc + (t.q_local + wrow) * a.ld_kc + (int64_t)h * D + 16 * kk + 8 * hl);
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) part = fmaf((float)qf[kk][i], (float)kf[kk][i], part);
-    }
-    part += __shfl_xor(part, 32, 64);
-    float xs = part;  // pre-scaled like the queries
-    if (has_pos) xs += kPre * sload(a.rab_pos + (int64_t)h * P);
-    if (has_time) xs += kPre * sload(a.rab_time + (int64_t)h * T);
-    if (hl == 0 && row_ok)
-      a.self_w[(t.q_local + wrow) * a.H + h] = silu_prescaled(xs) * (a.inv_n / kPre);
-  }
-  const int64_t tq = (has_time && row_ok) ? a.ts_q[t.q_base + wrow] : 0;
-  const uint32_t tq1 = (uint32_t)tq + 1u;
-  const int64_t qmin = uniform64(wave_min64(row_ok ? tq : INT64_MAX));
-  const int64_t qmax = uniform64(wave_max64(row_ok ? tq : INT64_MIN));
   // positions inside one sequence fit in 32 bits (lengths are bounded by an int N)
   const int nk = (int)t.nk, kend = (int)t.kend, kbeg = (int)t.kbeg, qpos0 = (int)t.qpos0;
-  const int qpos = CAND ? qpos0 : qpos0 + wrow;
-  const int wrow0 = qpos0 + 32 * wu;                        // the wavefront's first row
-  const int wlast = qpos0 + min(32 * wu + 31, t.rows - 1);  // its last live row
-  // candidate mode: the wavefront's candidates share one timestamp (or there is no time
-  // bias), so a pair's bias depends on the key alone
-  const bool keyb_ok = CAND && (!has_time || qmin == qmax);
-
-  // constant fragment of the bias k-step (candidate mode), [0] = [1] = 1 in the first
-  // half-wavefront, rebuilt at each use rather than held in registers
-  const uint32_t ones_w = hl == 0 ? 0x3f803f80u : 0u;  // two bf16 ones in one word
-  auto ones = [&]() {
-    u32x4 f = {ones_w, 0u, 0u, 0u};
-    return __builtin_bit_cast(bf16x8, f);
-  };
-
-  f32x16 o[NC];
-#pragma unroll
-  for (int c = 0; c < NC; ++c)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) o[c][r] = 0.f;
 
   // ---- key tiles go global -> LDS directly (buffer_load_dwordx4 ... lds): lane L of
   // one instruction fills 16-byte slot L of a contiguous 1 KiB span, so the LDS layout
@@ -391,7 +319,7 @@ attn_mfma_kernel(AttnArgs a) {
   // from their lanes. The ranges of the next group are fetched a group ahead.
   const KeyRange* krs = has_time ? a.key_ranges + key_range_slot(t.k_base, t.seq) : nullptr;
   struct LaneClass {
-    uint32_t bits;  // a TileClass byte in bits 0-6, the highest time bucket in bits 8-13
+    uint32_t bits;  // a TileClass byte in bits 0-5, the highest time bucket in bits 8-13
     float tlo, thi;
   };
   auto lane_range = [&](int g) {
@@ -400,19 +328,122 @@ attn_mfma_kernel(AttnArgs a) {
     if (has_time && wave_live && kb0 < kend) r = krs[kb0 >> 5];
     return r;
   };
+
+  const int nkt = (kend - kbeg + MBN - 1) / MBN;
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  // The first tile's keys, values, key timestamps and timestamp ranges are requested
+  // before the bias tables, the queries and the query timestamps, so that both sets of
+  // loads are in flight together: one memory round trip before the first tile, not two.
+  KeyRange lrn{0, 0};  // this lane's timestamp range in the next group
+  if (nkt > 0) {
+    dma_tile(B0{}, nsrc);
+    ts_fetch(kbeg);
+    lrn = lane_range(0);
+  }
+
+  // bias-table entries: loaded into registers here (indices clamped into the tables, no
+  // divergent branches) and written to LDS once the queries' loads are issued too
+  float vp = 0.f, vt = 0.f, vtc = 0.f;
+  if (has_pos) vp = a.rab_pos[(int64_t)h * P + min(max(tid - kPadLo, 0), P - 1)];
+  if (has_time) {
+    vt = a.rab_time[(int64_t)h * T + min(tid, T - 1)];     // rt[tid], tid < kTimeTab
+    vtc = a.rab_time[(int64_t)h * T + min(max(31 - tid, 0), T - 1)];  // rtc[tid], tid < 32
+  }
+  const float pb = has_pos ? tscale * sload(a.rab_pos + (int64_t)h * P + P - 1) : 0.f;  // P-1
+
+  // this lane's Q fragment; lanes past the tile's rows load its last row (no divergent
+  // branch between the loads) and zero it once the loads have landed
+  bf16x8 qf[NKK];
+  bf16x8 qlf[SPLIT ? NKK : 1];  // lo parts of the queries (SPLIT)
+  const int qrow = row_ok ? wrow : t.rows - 1;
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+    const int64_t qo = (t.q_local + qrow) * a.ld_q + (int64_t)h * D + 16 * kk + 8 * hl;
+    qf[kk] = load_bf16x8(q + qo);
+    if constexpr (SPLIT) qlf[kk] = load_bf16x8((const bf16*)a.q_lo + qo);
+  }
+  // candidate mode, first key range: the candidate's own key (relative position 0,
+  // elapsed time 0) is loaded with Q and its weight SiLU(score) / N stored per row and
+  // head, for the layer norm that follows to add weight * v_c (it reads the row anyway)
+  if (CAND && blockIdx.z == 0) {
+    const bf16* kc = (const bf16*)a.kc;
+    float part = 0.f;
+    if (row_ok) {
+      bf16x8 kf[NKK];
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk)
+        kf[kk] = load_bf16x8(kc + (t.q_local + wrow) * a.ld_kc + (int64_t)h * D + 16 * kk + 8 * hl);
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) part = fmaf((float)qf[kk][i], (float)kf[kk][i], part);
+    }
+    part += __shfl_xor(part, 32, 64);
+    float xs = part;  // pre-scaled like the queries
+    if (has_pos) xs += kPre * sload(a.rab_pos + (int64_t)h * P);
+    if (has_time) xs += kPre * sload(a.rab_time + (int64_t)h * T);
+    if (hl == 0 && row_ok)
+      a.self_w[(t.q_local + wrow) * a.H + h] = silu_prescaled(xs) * (a.inv_n / kPre);
+  }
+  const int64_t tq = (has_time && row_ok) ? a.ts_q[t.q_base + wrow] : 0;
+  const uint32_t tq1 = (uint32_t)tq + 1u;
+  const int64_t qmin = uniform64(wave_min64(row_ok ? tq : INT64_MAX));
+  const int64_t qmax = uniform64(wave_max64(row_ok ? tq : INT64_MIN));
+  // (the pin keeps the scaling here: folded into the loads' branches it would wait there)
+  asm volatile("" : "+v"(vp), "+v"(vt), "+v"(vtc));
+  if (has_pos) {
+    const int np = kPadLo + P + kPadHi;
+    if (tid < np) rpx[tid] = tscale * vp;
+    for (int i = tid + 256; i < np; i += 256)
+      rpx[i] = tscale * a.rab_pos[(int64_t)h * P + min(max(i - kPadLo, 0), P - 1)];
+  }
+  if (has_time) {
+    if (tid < kTimeTab) rt[tid] = tscale * vt;
+    if (tid < 32) rtc[tid] = tscale * vtc;
+  }
+  if (!row_ok) {
+    const bf16x8 z = {};
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      qf[kk] = z;
+      if constexpr (SPLIT) qlf[kk] = z;
+    }
+  }
+  const int qpos = CAND ? qpos0 : qpos0 + wrow;
+  const int wrow0 = qpos0 + 32 * wu;                        // the wavefront's first row
+  const int wlast = qpos0 + min(32 * wu + 31, t.rows - 1);  // its last live row
+  // candidate mode: the wavefront's candidates share one timestamp (or there is no time
+  // bias), so a pair's bias depends on the key alone
+  const bool keyb_ok = CAND && (!has_time || qmin == qmax);
+
+  // constant fragment of the bias k-step (candidate mode), [0] = [1] = 1 in the first
+  // half-wavefront, rebuilt at each use rather than held in registers
+  const uint32_t ones_w = hl == 0 ? 0x3f803f80u : 0u;  // two bf16 ones in one word
+  auto ones = [&]() {
+    u32x4 f = {ones_w, 0u, 0u, 0u};
+    return __builtin_bit_cast(bf16x8, f);
+  };
+
+  f32x16 o[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[c][r] = 0.f;
+
   auto lane_classify = [&](int g, const KeyRange& r) {
     const int kb0 = kbeg + 32 * (64 * g + lane);
     const bool act = wave_live && kb0 < kend && (CAND || kb0 <= wlast);
     const bool mask = CAND ? (kb0 + 32 > kend) : (kb0 + 31 > wrow0);
     const int min_dpos = (CAND ? qpos0 : wrow0) - (kb0 + 31);
     const bool pos_c = !has_pos || min_dpos >= P - 1;
-    LaneClass c{(act ? 1u : 0u) | (mask ? 2u : 0u) | (pos_c ? 4u : 0u) | 32u | 64u, 0.f, 0.f};
+    LaneClass c{(act ? 1u : 0u) | (mask ? 2u : 0u) | (pos_c ? 4u : 0u) | 32u, 0.f, 0.f};
     if (has_time && act) {
       const int64_t lo = qmin - r.hi, hi = qmax - r.lo;  // elapsed-time range
       const int blo = bucket_of(lo, T), bhi = bucket_of(hi, T);
       const bool tfast = time_fast_ok(qmin, qmax, r.lo, r.hi);
       const uint32_t tmode = blo == bhi ? 0u : ((bhi == blo + 1 && tfast) ? 1u : 2u);
-      c.bits = (c.bits & 7u) | (tmode << 3) | (tfast ? 32u : 0u) | (lo >= 0 ? 64u : 0u) |
+      c.bits = (c.bits & 7u) | (tmode << 3) | (tfast ? 32u : 0u) |
                ((uint32_t)bhi << 8);
       c.tlo = rt[blo];
       c.thi = rt[bhi];
@@ -435,20 +466,11 @@ attn_mfma_kernel(AttnArgs a) {
     return c;
   };
 
-  const int nkt = (kend - kbeg + MBN - 1) / MBN;
-  using B0 = std::integral_constant<int, 0>;
-  using B1 = std::integral_constant<int, 1>;
   // Pipeline: tile t computes while tile t+1's keys and values stream into the
   // idle buffer. Every 32 tiles the lanes classify the next 64 key blocks from
   // timestamp ranges fetched 32 tiles earlier.
   LaneClass lcl{0u, 0.f, 0.f};
-  KeyRange lrn{0, 0};  // this lane's timestamp range in the next group
-  if (nkt > 0) {
-    dma_tile(B0{}, nsrc);
-    ts_fetch(kbeg);
-    lrn = lane_range(0);
-    finish_tile(B0{}, true);
-  }
+  if (nkt > 0) finish_tile(B0{}, true);
   __syncthreads();  // also publishes the bias tables in LDS
   if (nkt > 0) {
     lcl = lane_classify(0, lrn);
@@ -615,7 +637,7 @@ attn_mfma_kernel(AttnArgs a) {
         // high one), split into bf16 high and low parts packed in one word; the k-step
         // fragments carry the word in the low half-wavefront only
         const int j = k0 + lane;
-        float b = has_pos ? rp[min(qpos0 - j, P - 1)] : 0.f;
+        float b = has_pos ? rpx[kPadLo + min(qpos0 - j, P - 1)] : 0.f;
         if (has_time) b += rt[bucket_of(qmin - tk64[buf][lane], T)];
         const bf16 bh = (bf16)b;
         const bf16 bl = (bf16)(b - (float)bh);
@@ -703,7 +725,7 @@ attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int j = kb0 + 8 * (r >> 2) + 4 * hl + (r & 3);
-          float b = has_pos ? rp[max(0, min(qpos0 - j, P - 1))] : 0.f;
+          float b = has_pos ? rpx[kPadLo + max(0, min(qpos0 - j, P - 1))] : 0.f;
           if (has_time) b += rt[bucket_of(tq - tk64[buf][j - k0], T)];
           const bf16 bh = (bf16)b;
           x[r] = (float)bh + (float)(bf16)(b - (float)bh);
@@ -727,12 +749,14 @@ attn_mfma_kernel(AttnArgs a) {
       // i - j = dbase - (8*(r/4) + r%4) for accumulator slot r
       const int dbase = qpos - kb0 - 4 * hl;
       if (!bc.pos_c()) {
+        // Over the wavefront's rows (dead rows included) and the block's keys, i - j lies
+        // in [wrow0 - kb0 - 31, wrow0 - kb0 + 31]. The block is active (kb0 <= wlast <=
+        // wrow0 + 31) and its bucket varies (wrow0 - kb0 - 31 < P - 1), so that range is
+        // inside [-62, P + 60], which the padded table covers. Slot r reads i - j =
+        // dbase - off(r), off(r) = 8 (r / 4) + r % 4 <= 27: one base, constant offsets.
+        const float* rq = rpx + (kPadLo - 27) + dbase;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          int d = dbase - (8 * (r >> 2) + (r & 3));
-          d = d < 0 ? 0 : (d < P - 1 ? d : P - 1);
-          x[r] += rp[d];
-        }
+        for (int r = 0; r < 16; ++r) x[r] += rq[27 - (8 * (r >> 2) + (r & 3))];
       }
       const uint32_t* tkl = tk_lo[buf] + 32 * kb + 4 * hl;
       if (bc.tmode() == 1) {
@@ -744,8 +768,7 @@ attn_mfma_kernel(AttnArgs a) {
             const u32x4 tk4 = *reinterpret_cast<const u32x4*>(tkl + 8 * g4);
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              x[4 * g4 + e] += rtc[bc.tsorted() ? __builtin_clz((tq1 - tk4[e]) | 1u)
-                                              : time_clz_fast(tq1, tk4[e])];
+              x[4 * g4 + e] += rtc[time_clz_fast(tq1, tk4[e])];
           }
         } else {
           const int64_t* tk = tk64[buf] + 32 * kb + 4 * hl;
