@@ -20,7 +20,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libhstu.so")
-SOURCES = ["api.cpp", "plan.hip", "attn_simple.hip", "attn_mfma.hip", "lngate.hip", "gemm.hip",
+SOURCES = ["api.cpp", "plan.hip", "attn_simple.hip", "attn_mfma.hip", "lngate.hip", "lngate_f2.hip", "gemm.hip",
            "misc.hip", "sl.hip",
            "attn_bwd.hip", "attn_bwd_mfma.hip", "layer_bwd.hip",
            "attn_softmax.hip"]

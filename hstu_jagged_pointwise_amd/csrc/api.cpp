@@ -349,6 +349,13 @@ hstu_status layer_once(const hstu_layer_desc* d, const int64_t* off_dev, const i
   aa.items = b.items;
   aa.n_items = (int)j.items;
   HSTU_TRY(run_attention(&a, aa, false, s), "attention");
+  if (ln_gate_f2_supported(hv, d->d_model, bf)) {  // narrow layers: the gated rows stay in LDS
+    HSTU_TRY(launch_ln_gate_f2(b.o, hv, 1, 0, vw.u, vw.ld, w.ln_gamma, w.ln_beta, a.ln_eps, w.w2,
+                               hv, w.b2, d->residual ? x : nullptr, d->d_model, y, d->d_model,
+                               rows, hv, d->d_model, s),
+             "layer norm gate and f2 projection");
+    return HSTU_OK;
+  }
   HSTU_TRY(launch_ln_gate(b.o, hv, 1, 0, vw.u, vw.ld, w.ln_gamma, w.ln_beta, a.ln_eps, b.g, hv, rows,
                           hv, bf, s),
            "layer norm gate");
@@ -615,13 +622,21 @@ hstu_status run_candidates(const mfalcon_desc* d, const MfPlan& p, const int64_t
         aa.n_users = std::min(ue - u0, 65535);
         HSTU_TRY(run_attention(&a, aa, true, s), "candidate attention");
       }
-      HSTU_TRY(launch_ln_gate(b.c_o, hv, aa.kv_splits, aa.part_stride, cv.u, cv.ld, w.ln_gamma,
-                              w.ln_beta, a.ln_eps, b.c_g, hv, rows, hv, bf, s, aa.self_w, cv.v,
-                              cv.ld, a.d_v),
-               "candidate layer norm gate");
-      HSTU_TRY(launch_gemm(b.c_g, hv, w.w2, hv, w.b2, ld.residual ? in : nullptr, dm, out, dm,
-                           rows, dm, hv, 0, bf, s),
-               "candidate f2 projection");
+      if (ln_gate_f2_supported(hv, dm, bf)) {
+        HSTU_TRY(launch_ln_gate_f2(b.c_o, hv, aa.kv_splits, aa.part_stride, cv.u, cv.ld,
+                                   w.ln_gamma, w.ln_beta, a.ln_eps, w.w2, hv, w.b2,
+                                   ld.residual ? in : nullptr, dm, out, dm, rows, hv, dm, s,
+                                   aa.self_w, cv.v, cv.ld, a.d_v),
+                 "candidate layer norm gate and f2 projection");
+      } else {
+        HSTU_TRY(launch_ln_gate(b.c_o, hv, aa.kv_splits, aa.part_stride, cv.u, cv.ld, w.ln_gamma,
+                                w.ln_beta, a.ln_eps, b.c_g, hv, rows, hv, bf, s, aa.self_w, cv.v,
+                                cv.ld, a.d_v),
+                 "candidate layer norm gate");
+        HSTU_TRY(launch_gemm(b.c_g, hv, w.w2, hv, w.b2, ld.residual ? in : nullptr, dm, out, dm,
+                             rows, dm, hv, 0, bf, s),
+                 "candidate f2 projection");
+      }
       in = out;
     }
   }

@@ -134,6 +134,17 @@ hipError_t launch_ln_gate(const float* o, int64_t ld_o, int nsplit, int64_t spli
                           hipStream_t s, const float* self_w = nullptr,
                           const void* vself = nullptr, int64_t ld_vself = 0, int dv = 0);
 
+// The LN gate and f2 in one launch (bf16): y[r, :] = g[r, :] W2^T + b2 (+ R[r, :]) with g the
+// bf16 rounding of launch_ln_gate's output, never stored. K = H*d_v is the gated width and N
+// the model width (W2 is [N, K], row stride ldw). Shapes: ln_gate_f2_supported.
+bool ln_gate_f2_supported(int K, int N, int use_bf16);
+hipError_t launch_ln_gate_f2(const float* o, int64_t ld_o, int nsplit, int64_t split_stride,
+                             const void* u, int64_t ld_u, const float* gamma, const float* beta,
+                             float eps, const void* w2, int64_t ldw, const float* b2, const void* R,
+                             int64_t ldr, void* y, int64_t ldy, int64_t rows, int K, int N,
+                             hipStream_t s, const float* self_w = nullptr,
+                             const void* vself = nullptr, int64_t ld_vself = 0, int dv = 0);
+
 // C[M,N] = epi(A[M,K] W[N,K]^T + bias[N]); epi = SiLU when silu, + R[M,N] when R.
 // lo (bf16 output only): for columns n >= lo_c0 (a multiple of 8) also writes
 // lo[m, n] = bf16(y - bf16(y)), the part of the fp32 result y that the bf16 C drops, with

@@ -91,6 +91,20 @@ def test_small_layer_stack(dt, residual, num_layers):
     check_layer(x, f"layer {dt} L={num_layers} res={residual}")
 
 
+@pytest.mark.parametrize("H,d,d_model", [(2, 32, 64), (2, 32, 256), (1, 64, 128), (2, 64, 64),
+                                         (2, 64, 128), (2, 64, 256)])
+def test_narrow_layer_ln_gate_f2_in_one_kernel(H, d, d_model):
+    """bf16 layers with gated width H*d_v of 64 or 128 and model width 64, 128 or 256, where
+    the layer norm gate and f2 run as one kernel whose 64-row blocks of gated values stay
+    in LDS: two layers with the residual, random biases and LN affine, ragged lengths
+    (empty, 1, and sequences spanning several 64-row blocks with a ragged last one)."""
+    x = synth.make_layer(40 + H + d + d_model, lambda r: np.array([0, 1, 130, 64, 257, 9]), H, d,
+                         d, d_model, 32, 16, "bf16", num_layers=2, w_std=0.1, random_bias=True,
+                         with_ln_affine=True, residual=1)
+    announce(f"layer bf16 H={H} d={d} d_model={d_model} (one-kernel LN gate and f2)")
+    check_layer(x, f"narrow layer H={H} d={d} d_model={d_model}")
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_layer_other_widths(dt):
     x = synth.make_layer(31, lambda r: np.array([50, 200, 3]), 3, 32, 128, 40, 64, 32, dt,
