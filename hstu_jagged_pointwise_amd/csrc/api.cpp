@@ -429,17 +429,22 @@ void carve_hist_ws(Carver& c, const mfalcon_desc* d, const MfPlan& p, MfHistBufs
   b->qk_lo = ld.num_layers > 1 && layer_splits_qk(a) ? c.take((size_t)nh * f1 * es) : nullptr;
 }
 
-// The candidate pass keeps up to kInFlight microbatches in flight: their work is
-// issued together, one launch per step for all of them (the rows of one group of up to
-// kInFlight microbatches, in global candidate order), on the caller's stream. Each
-// microbatch's candidates are computed exactly as they would be alone (every output
-// row has its own fixed reduction order), so the grouping only sets how much work one
-// launch holds: a group fills the device where one microbatch of ~1k candidates would
-// leave most of it idle. The working set is that of kInFlight microbatches.
-constexpr int kInFlight = 4;
+// The candidate pass keeps up to kInFlight microbatches in flight (fewer when they would
+// exceed kGroupRowCap rows, never less than one): their work is issued together, one
+// launch per step for all of them (the rows of one group, in global candidate order), on
+// the caller's stream. Each microbatch's candidates are computed exactly as they would be
+// alone (every output row has its own fixed reduction order), so the grouping only sets
+// how much work one launch holds: one microbatch of ~1k candidates leaves most of the
+// device idle in every step, and a group of 16 lets each launch run several rounds of
+// workgroups, so that the tail of one round is a small part of it (4 -> 16 in flight:
+// 0.389 -> 0.309 ms on 16,384 candidates against a 4,096-key history). The workspace
+// holds the working set of one group (~10 KB per candidate row at d_model 512, 8 heads).
+constexpr int kInFlight = 16;
+constexpr int64_t kGroupRowCap = 65536;
 int64_t group_rows(const mfalcon_desc* d, const MfPlan& p) {
-  const int64_t g = (int64_t)d->microbatch * kInFlight;
-  return std::max<int64_t>(1, std::min<int64_t>(g, p.cand_total));
+  const int64_t mb = d->microbatch;
+  const int64_t n = std::max<int64_t>(1, std::min<int64_t>(kInFlight, kGroupRowCap / mb));
+  return std::max<int64_t>(1, std::min<int64_t>(mb * n, p.cand_total));
 }
 
 void carve_cand_ws(Carver& c, const mfalcon_desc* d, const MfPlan& p, MfCandBufs* b) {

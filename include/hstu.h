@@ -198,9 +198,10 @@ hstu_status hstu_layer_fwd(const hstu_layer_desc* desc, const int64_t* seq_offse
  * therefore equals the last row of hstu_layer_fwd run on
  * (history, candidate). The history pass runs once per call. The candidates
  * are then processed desc->microbatch at a time (in global candidate order)
- * through all layers, reusing the cached history keys and values. Up to four
- * microbatches are in flight at once: their work is issued together, one
- * launch per step for the group, which is what the workspace is sized for.
+ * through all layers, reusing the cached history keys and values. Up to 16
+ * microbatches (at most 65,536 rows, at least one microbatch) are in flight at
+ * once: their work is issued together, one launch per step for the group,
+ * which is what the workspace is sized for.
  * A candidate's result does not depend on the microbatch size or on the
  * other candidates, bit for bit.
  * hist_x [n_hist_tot, d_model], cand_x and cand_out [C_tot, d_model] (dtype).
