@@ -125,18 +125,29 @@ def time_calls_cold(fn, stream, steps):
     return np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
 
 
+def gate_f2_fused(x):
+    """True when the library runs the LN gate and f2 as one kernel for this layer shape
+    (bf16, gated width H*d_v of 64 or 128, model width 64, 128 or 256)."""
+    return (x.dtype == "bf16" and x.num_heads * x.d_v in (64, 128)
+            and x.d_model in (64, 128, 256))
+
+
 def layer_bytes(x, split_qk=True):
-    """Algorithmic HBM bytes of one layer as its four steps run here, each step reading its
+    """Algorithmic HBM bytes of one layer as its steps run here, each step reading its
     inputs once and writing its outputs once (bf16 activations and weights, fp32 attention
     rows for the gate, int64 timestamps): f1 reads X and W1 and writes U|V|Q|K (plus the
     bf16 remainder of Q and K that the split-precision scores read); the attention reads
     Q, K, V (and the remainders) and the timestamps and writes fp32 O; the gate reads O
-    and U and writes G; f2 reads G and W2 and writes Y."""
+    and U and writes G; f2 reads G and W2 and writes Y. Where the gate and f2 are one
+    kernel ("ln_gate_f2"), it reads O, U and W2 and writes Y: G never reaches HBM."""
     T, dm, H, dqk, dv = int(x.offsets[-1]), x.d_model, x.num_heads, x.d_qk, x.d_v
     f1c = 2 * H * (dqk + dv)
     lo = 2 * H * dqk if split_qk else 0
     f1 = T * dm * 2 + f1c * dm * 2 + T * (f1c + lo) * 2
     attn = T * (2 * H * dqk + lo + H * dv) * 2 + T * 8 + T * H * dv * 4
+    if gate_f2_fused(x):
+        g2 = T * H * dv * 4 + T * H * dv * 2 + dm * H * dv * 2 + T * dm * 2
+        return {"f1": f1, "attention": attn, "ln_gate_f2": g2, "total": f1 + attn + g2}
     gate = T * H * dv * 4 + T * H * dv * 2 * 2
     f2 = T * H * dv * 2 + dm * H * dv * 2 + T * dm * 2
     return {"f1": f1, "attention": attn, "ln_gate": gate, "f2": f2,
@@ -298,7 +309,7 @@ def leg_mfalcon(steps, warmup, num_layers=1):
                 candidates_only=dict(ms=round(cmean, 4), candidates_per_s=C / (cmean * 1e-3),
                                      note="mfalcon_score_cached against a history cache built "
                                           "once by mfalcon_history"),
-                microbatch=x.microbatch, in_flight=4, history=n_h, layers=num_layers)
+                microbatch=x.microbatch, in_flight=16, history=n_h, layers=num_layers)
 
 
 def leg_layers(steps, warmup):
