@@ -387,7 +387,29 @@ def leg_softmax(steps, warmup):
     pairs = int(np.sum(x.lengths * (x.lengths + 1) // 2))
     flops = pairs * x.num_heads * 2 * (x.d_qk + x.d_v)
     mean = float(ms.mean())
-    return dict(ms=round(mean, 4), tflops=round(flops / (mean * 1e-3) / 1e12, 2))
+    tf = flops / (mean * 1e-3) / 1e12
+    return dict(ms=round(mean, 4), tflops=round(tf, 2), roofline=mfma_roofline(tf))
+
+
+def mfma_roofline(tflops, note=None):
+    """A leg's rate against the bf16 MFMA peak."""
+    r = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+         "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4)}
+    if note:
+        r["note"] = note
+    return r
+
+
+def layer_train_flops(x):
+    """Algorithmic FLOPs of one layer's forward and backward (recomputation not counted):
+    forward f1, attention over useful pairs and f2; backward two GEMMs per projection
+    (activation and weight gradients) and four contractions per useful pair and head."""
+    T, dm, H, dqk, dv = int(x.offsets[-1]), x.d_model, x.num_heads, x.d_qk, x.d_v
+    f1c = 2 * H * (dqk + dv)
+    n = np.diff(np.asarray(x.offsets, np.int64))
+    attn = int(np.sum(n * (n + 1) // 2)) * H * 2 * (dqk + dv)
+    gemm = 2 * T * dm * f1c + 2 * T * H * dv * dm
+    return 3 * gemm + attn + 2 * attn
 
 
 def leg_backward(steps, warmup):
@@ -417,8 +439,9 @@ def leg_backward(steps, warmup):
     # dV = A^T G, dP = G V^T, dQ = dZ K, dK = dZ^T Q: four contractions per pair and head
     flops = pairs * x.num_heads * 2 * (2 * x.d_v + 2 * x.d_qk)
     mean = float(ms.mean())
-    res["attention_length_8192"] = dict(ms=round(mean, 4),
-                                        tflops=round(flops / (mean * 1e-3) / 1e12, 2))
+    tf = flops / (mean * 1e-3) / 1e12
+    res["attention_length_8192"] = dict(ms=round(mean, 4), tflops=round(tf, 2),
+                                        roofline=mfma_roofline(tf))
     for name, xl in (("short_history_layer", synth.workload_short_history_layer()),
                      ("heavy_tail_4_layer_stack", synth.workload_heavy_tail_stack())):
         dl = layer_to_device(xl)
@@ -437,8 +460,12 @@ def leg_backward(steps, warmup):
 
         with torch.cuda.stream(stream):
             ms, _ = time_calls(lcall, stream, max(5, steps // 5), max(2, warmup // 5))
-        res[name] = dict(ms_per_call=round(float(ms.mean()), 4), layers=len(xl.layers),
-                         note="forward recomputed inside the call")
+        lm = float(ms.mean())
+        ltf = layer_train_flops(xl) * len(xl.layers) / (lm * 1e-3) / 1e12
+        res[name] = dict(ms_per_call=round(lm, 4), layers=len(xl.layers),
+                         note="forward recomputed inside the call",
+                         roofline=mfma_roofline(ltf, "algorithmic FLOPs of forward and backward "
+                                                     "(the recomputed forward not counted)"))
     return res
 
 
@@ -460,8 +487,16 @@ def leg_sl(steps, warmup):
 
     with torch.cuda.stream(stream):
         ms, _ = time_calls(call, stream, steps, warmup)
-    return dict(ms=round(float(ms.mean()), 4), rows_in=int(x.offsets[-1]), rows_out=int(new[-1]),
-                target_length=int(L), note="includes host validation and output allocation")
+    mean = float(ms.mean())
+    # select: one 4-byte key per action; gather: each kept row and timestamp read and written
+    rows_in, rows_out = int(x.offsets[-1]), int(new[-1])
+    by = rows_in * 4 + rows_out * 2 * (x.x.shape[1] * 2 + 8)
+    gbs = by / (mean * 1e-3) / 1e9
+    return dict(ms=round(mean, 4), rows_in=rows_in, rows_out=rows_out, target_length=int(L),
+                note="includes host validation and output allocation",
+                roofline={"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                          "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                          "bytes_per_call": by})
 
 
 def leg_copy():
