@@ -94,7 +94,7 @@ bool attn_bwd_mfma_supported(int dtype_bf16, int d_qk, int d_v, int P) {
 
 // ------------------------------------------------------------------ query side
 template <int D>
-__global__ __launch_bounds__(256, D <= 64 ? 2 : 1) void attn_bwd_q_mfma(AttnBwdArgs a) {
+__global__ __launch_bounds__(256, 2) void attn_bwd_q_mfma(AttnBwdArgs a) {
   constexpr int NKK = D / 16, NC = D / 32;
   __shared__ __attribute__((aligned(16))) bf16 Ks[2][TR * (D + 8)];
   __shared__ __attribute__((aligned(16))) bf16 Vs[2][TR * (D + 8)];
