@@ -164,11 +164,12 @@ def test_mfalcon_workload_every_candidate():
 
 @pytest.mark.parametrize("L,shared", [(1, False), (2, False), (1, True), (2, True)])
 def test_split_history_multi_user(L, shared):
-    """Histories longer than one key range (1024 keys) are split across workgroups and the
-    partials summed in a fixed order: parity against the oracle, and outputs bit-for-bit
-    independent of the microbatch size and of the candidate order. With a shared request
-    time per user the per-key bias path runs (ragged tails take the masked path)."""
-    x = _small("bf16", L, seed=11, hist=(1300, 0, 700, 2000), cands=(37, 5, 20, 64), mb=50,
+    """Histories longer than one key range (2048 keys) are split across workgroups (4200
+    keys: three ranges) and the partials summed in a fixed order: parity against the
+    oracle, and outputs bit-for-bit independent of the microbatch size and of the candidate
+    order. With a shared request time per user the per-key bias path runs (ragged tails
+    take the masked path)."""
+    x = _small("bf16", L, seed=11, hist=(2600, 0, 700, 4200), cands=(37, 5, 20, 64), mb=50,
                shared=shared)
     announce(f"mfalcon split history L={L} shared_ts={shared}")
     out, lg = mf_on_gpu(x)
@@ -186,6 +187,28 @@ def test_split_history_multi_user(L, shared):
                            np.random.default_rng(1).permutation(np.arange(62, 126))])
     o, _ = mf_on_gpu(x, cand_x=x.cand_x[perm], cand_ts=x.cand_ts[perm])
     assert np.array_equal(o.float().cpu().numpy(), base[perm])
+
+
+@pytest.mark.parametrize("H,d,d_model", [(2, 32, 64), (2, 32, 256), (2, 64, 256)])
+def test_split_history_narrow_layer(H, d, d_model):
+    """Layer widths whose LN gate and f2 run as one kernel (gated width 64 or 128, model
+    width 64 or 256), with a history split over three key ranges and the candidates' own
+    key: the one-kernel gate sums the three partial rows and the self term. Parity against
+    the oracle, and outputs bit-for-bit independent of the microbatch size."""
+    x = synth.make_mfalcon(13, [2600, 0, 4200], [30, 7, 41], H, d, d, d_model, 32, 16, "bf16",
+                           num_layers=2, microbatch=16, shared_request_time=False, w_std=0.1,
+                           random_bias=True, with_ln_affine=True)
+    announce(f"mfalcon narrow layer H={H} d={d} d_model={d_model} split history")
+    out, lg = mf_on_gpu(x)
+    want, _ = mf_oracle(x)
+    want_s = mf_oracle(x, "bf16")[0]
+    check_rows(to_np(out), x, want, want_s, f"mfalcon narrow H={H} d={d} dm={d_model}")
+    _check_logits(lg, want_s, x, TOL["bf16"])
+    check_each_layer(x, to_np(out), f"mfalcon narrow H={H} d={d} dm={d_model}")
+    base = out.float().cpu().numpy()
+    for mb in (1, 45):
+        o, _ = mf_on_gpu(x, microbatch=mb)
+        assert np.array_equal(o.float().cpu().numpy(), base), f"microbatch {mb}"
 
 
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
