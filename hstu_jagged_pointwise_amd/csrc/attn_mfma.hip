@@ -638,7 +638,14 @@ attn_mfma_kernel(AttnArgs a) {
         // fragments carry the word in the low half-wavefront only
         const int j = k0 + lane;
         float b = has_pos ? rpx[kPadLo + min(qpos0 - j, P - 1)] : 0.f;
-        if (has_time) b += rt[bucket_of(qmin - tk64[buf][lane], T)];
+        if (has_time) {
+          // both blocks' elapsed times fit the 32-bit form: the same bucket from the low
+          // words (the count-of-leading-zeros table holds the same values as rt)
+          if ((cls.f & 0x2020u) == 0x2020u)
+            b += rtc[time_clz_fast((uint32_t)qmin + 1u, tk_lo[buf][lane])];
+          else
+            b += rt[bucket_of(qmin - tk64[buf][lane], T)];
+        }
         const bf16 bh = (bf16)b;
         const bf16 bl = (bf16)(b - (float)bh);
         const uint32_t word = (uint32_t)__builtin_bit_cast(uint16_t, bh) |
