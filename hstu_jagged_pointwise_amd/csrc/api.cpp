@@ -321,6 +321,12 @@ hstu_status layer_once(const hstu_layer_desc* d, const int64_t* off_dev, const i
   const int hv = a.num_heads * a.d_v;
   const int hq = a.num_heads * a.d_qk;
   void* lo = f1_only ? nullptr : b.qk_lo;
+  // f1 alone (the last history layer of M-FALCON): the candidates read only its keys and
+  // values, so only the V and K columns are computed where they are whole GEMM tiles
+  if (f1_only && bf &&
+      launch_gemm_2cols(x, d->d_model, w.w1, d->d_model, w.b1, b.uvqk, f1, rows, d->d_model, 1,
+                        hv, hv, 2 * hv + hq, hq, s) == hipSuccess)
+    return HSTU_OK;
   // with split scores the attention takes its queries pre-scaled (kQueryPrescale)
   const int q_c1 = lo ? 2 * hv + hq : 0;
   HSTU_TRY(launch_gemm(x, d->d_model, w.w1, d->d_model, w.b1, nullptr, 0, b.uvqk, f1, rows, (int)f1,

@@ -96,7 +96,8 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const bf16* __restric
                                                          int tiles_total, int64_t ksplit,
                                                          int64_t c_split, bf16* __restrict__ act,
                                                          bf16* __restrict__ rem, int rem_c0,
-                                                         int sc_c0, int sc_c1, float sc) {
+                                                         int sc_c0, int sc_c1, float sc,
+                                                         int cw_len0, int cw_off0, int cw_off1) {
   using G = GemmShape<BM, BN>;
   constexpr int GBK = G::GBK;
   constexpr int FM = G::FM, FN = G::FN, PERW = G::PERW, STAGE = G::STAGE;
@@ -119,6 +120,9 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const bf16* __restric
   }
   const int64_t m0 = (int64_t)(tile / tiles_n) * BM;
   const int n0 = (tile % tiles_n) * BN;
+  // computed column n is column n + cw_off0 of W and C below cw_len0, else n - cw_len0 +
+  // cw_off1 (two windows of whole tiles; the identity when cw_len0 = N and both offsets 0)
+  const int n0a = n0 < cw_len0 ? n0 + cw_off0 : n0 - cw_len0 + cw_off1;
   {  // split-K: blockIdx.y takes K range [y * ksplit, (y + 1) * ksplit) into its own C slice
     const int64_t kofs = (int64_t)blockIdx.y * ksplit;
     A += kofs;
@@ -151,7 +155,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const bf16* __restric
     }
   }
   const char* abase = (const char*)(A + m0 * lda);
-  const char* wbase = (const char*)(W + (int64_t)n0 * ldw);
+  const char* wbase = (const char*)(W + (int64_t)n0a * ldw);
   const int nks = (K + GBK - 1) / GBK;
   // byte offset of the last 16-byte chunk of a row inside K: chunks of the last stage
   // that lie past K fetch that one instead (they are zeroed in LDS before use), so no
@@ -259,7 +263,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const bf16* __restric
   for (int j = 0; j < FN; ++j) {
     const int nl = 32 * j + l32;
     const int n = n0 + wn * G::WN + nl;
-    const float bn = (bias && n < N) ? bias[n] : 0.f;
+    const float bn = (bias && n < N) ? bias[n0a + wn * G::WN + nl] : 0.f;
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -276,8 +280,8 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(const bf16* __restric
   for (int s = lane; s < SEGS; s += 64) {
     const int ml = s / (G::WN / 8), cs = s % (G::WN / 8);
     const int64_t m = m0 + wm * G::WM + ml;
-    const int n = n0 + wn * G::WN + 8 * cs;
-    if (m >= M || n >= N) continue;
+    if (m >= M || n0 + wn * G::WN + 8 * cs >= N) continue;
+    const int n = n0a + wn * G::WN + 8 * cs;  // the column of C (and R, act, rem) written
     const f32x4 lo = *reinterpret_cast<const f32x4*>(&E[ml * EP + 8 * cs]);
     const f32x4 hi = *reinterpret_cast<const f32x4*>(&E[ml * EP + 8 * cs + 4]);
     float y[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -581,7 +585,7 @@ hipError_t launch_gemm_ex(const void* A, int64_t lda, const void* W, int64_t ldw
       hipLaunchKernelGGL((gemm_bf16_kernel<T, T, O>), dim3(tn * tm, splits), dim3(256), 0, s,
                          (const bf16*)A, lda, (const bf16*)W, ldw, bias, (const bf16*)R, ldr, (O*)C,
                          ldc, M, N, K, silu, tn, tn * tm, ksplit, c_split, (bf16*)act,
-                         (bf16*)lo, lo_c0, sc_c0, sc_c1, sc);
+                         (bf16*)lo, lo_c0, sc_c0, sc_c1, sc, N, 0, 0);
     };
     using I128 = std::integral_constant<int, 128>;
     using I64 = std::integral_constant<int, 64>;
@@ -626,6 +630,31 @@ hipError_t launch_gemm_tn(const void* A, int64_t lda, const void* B, int64_t ldb
   else
     go(std::integral_constant<int, 64>{});
   return hipGetLastError();
+}
+
+hipError_t launch_gemm_2cols(const void* A, int64_t lda, const void* W, int64_t ldw,
+                             const float* bias, void* C, int64_t ldc, int64_t M, int K, int silu,
+                             int c0, int len0, int c1, int len1, hipStream_t s) {
+  if (M <= 0 || len0 + len1 <= 0) return hipSuccess;
+  const int N = len0 + len1;
+  if (len0 < 0 || len1 < 0 || c0 < 0 || c1 < 0 || N % 8 != 0 || K % 8 != 0 || lda % 8 != 0 ||
+      ldw % 8 != 0 || ldc % 8 != 0)
+    return hipErrorInvalidValue;
+  const int64_t big = ((N + 127) / 128) * ((M + 127) / 128);
+  auto go = [&](auto bm) {
+    constexpr int T = decltype(bm)::value;
+    // each window is whole tiles, so that no tile straddles the two
+    if (len0 % T != 0 || c0 % 8 != 0 || c1 % 8 != 0) return hipErrorInvalidValue;
+    const int tn = (N + T - 1) / T, tm = (int)((M + T - 1) / T);
+    hipLaunchKernelGGL((gemm_bf16_kernel<T, T, bf16>), dim3(tn * tm, 1), dim3(256), 0, s,
+                       (const bf16*)A, lda, (const bf16*)W, ldw, bias, (const bf16*)nullptr,
+                       (int64_t)0, (bf16*)C, ldc, M, N, K, silu, tn, tn * tm, (int64_t)K,
+                       (int64_t)0, (bf16*)nullptr, (bf16*)nullptr, 0, 0, 0, 1.f, len0, c0,
+                       c1);
+    return hipGetLastError();
+  };
+  return big >= 256 ? go(std::integral_constant<int, 128>{})
+                    : go(std::integral_constant<int, 64>{});
 }
 
 hipError_t launch_gemm(const void* A, int64_t lda, const void* W, int64_t ldw, const float* bias,

@@ -157,6 +157,14 @@ hipError_t launch_gemm(const void* A, int64_t lda, const void* W, int64_t ldw,
                        void* lo = nullptr, int lo_c0 = 0, int sc_c0 = 0, int sc_c1 = 0,
                        float sc = 1.f);
 
+// launch_gemm (bf16, no residual) computing only two column windows of C: columns
+// [c0, c0 + len0) and [c1, c1 + len1), from the same rows of W and bias. Returns
+// hipErrorInvalidValue, launching nothing, when len0 is not a multiple of the tile width
+// the size selects (the caller then computes every column).
+hipError_t launch_gemm_2cols(const void* A, int64_t lda, const void* W, int64_t ldw,
+                             const float* bias, void* C, int64_t ldc, int64_t M, int K, int silu,
+                             int c0, int len0, int c1, int len1, hipStream_t s);
+
 // launch_gemm with an fp32 output (bf16 inputs; fp32 inputs always write fp32) and
 // split-K: grid dimension y = splits, split y covers K range [y*ksplit, (y+1)*ksplit)
 // (ksplit a multiple of 64) and writes C + y*c_split; splits > 1 takes no bias,
