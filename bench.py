@@ -60,7 +60,12 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def time_calls(fn, stream, steps, warmup, warm_s=0.0):
+# Untimed near-continuous load before each later leg's timed calls (seconds; set from
+# --warm-seconds): a leg's set-up idles the device, whose clock then ramps down again.
+LEG_WARM_S = 0.0
+
+
+def time_calls(fn, stream, steps, warmup, warm_s=None):
     """Per-call durations (ms) from HIP events recorded on the library's stream.
 
     After the `warmup` calls, further untimed calls run until `warm_s` seconds have
@@ -76,6 +81,8 @@ def time_calls(fn, stream, steps, warmup, warm_s=0.0):
     counted as GPU time of that call."""
     import gc
     import torch
+    if warm_s is None:
+        warm_s = LEG_WARM_S
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     gc.collect()
@@ -579,6 +586,8 @@ def main():
         return
     result = {}
     attn = None
+    global LEG_WARM_S
+    LEG_WARM_S = args.warm_seconds / 4  # the legs after the first
     if "attn" in legs:
         log("attention leg (length-8192 workload)")
         attn = leg_attention(args.steps, args.warmup, args.warm_seconds)
