@@ -355,7 +355,8 @@ hstu_status layer_once(const hstu_layer_desc* d, const int64_t* off_dev, const i
   aa.items = b.items;
   aa.n_items = (int)j.items;
   HSTU_TRY(run_attention(&a, aa, false, s), "attention");
-  if (ln_gate_f2_supported(hv, d->d_model, bf)) {  // narrow layers: the gated rows stay in LDS
+  if (ln_gate_f2_supported(hv, d->d_model, bf, w.w2, w.ln_gamma, w.ln_beta)) {
+    // narrow layers: the gated rows stay in LDS
     HSTU_TRY(launch_ln_gate_f2(b.o, hv, 1, 0, vw.u, vw.ld, w.ln_gamma, w.ln_beta, a.ln_eps, w.w2,
                                hv, w.b2, d->residual ? x : nullptr, d->d_model, y, d->d_model,
                                rows, hv, d->d_model, s),
@@ -633,7 +634,7 @@ hstu_status run_candidates(const mfalcon_desc* d, const MfPlan& p, const int64_t
         aa.n_users = std::min(ue - u0, 65535);
         HSTU_TRY(run_attention(&a, aa, true, s), "candidate attention");
       }
-      if (ln_gate_f2_supported(hv, dm, bf)) {
+      if (ln_gate_f2_supported(hv, dm, bf, w.w2, w.ln_gamma, w.ln_beta)) {
         HSTU_TRY(launch_ln_gate_f2(b.c_o, hv, aa.kv_splits, aa.part_stride, cv.u, cv.ld,
                                    w.ln_gamma, w.ln_beta, a.ln_eps, w.w2, hv, w.b2,
                                    ld.residual ? in : nullptr, dm, out, dm, rows, hv, dm, s,

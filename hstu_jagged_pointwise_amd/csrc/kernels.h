@@ -136,8 +136,11 @@ hipError_t launch_ln_gate(const float* o, int64_t ld_o, int nsplit, int64_t spli
 
 // The LN gate and f2 in one launch (bf16): y[r, :] = g[r, :] W2^T + b2 (+ R[r, :]) with g the
 // bf16 rounding of launch_ln_gate's output, never stored. K = H*d_v is the gated width and N
-// the model width (W2 is [N, K], row stride ldw). Shapes: ln_gate_f2_supported.
-bool ln_gate_f2_supported(int K, int N, int use_bf16);
+// the model width (W2 is [N, K], row stride ldw). ln_gate_f2_supported: the shapes with a
+// one-kernel form, and W2, gamma and beta (NULL allowed for the last two) 16-byte aligned;
+// the caller runs launch_ln_gate and launch_gemm otherwise.
+bool ln_gate_f2_supported(int K, int N, int use_bf16, const void* w2, const float* gamma,
+                          const float* beta);
 hipError_t launch_ln_gate_f2(const float* o, int64_t ld_o, int nsplit, int64_t split_stride,
                              const void* u, int64_t ld_u, const float* gamma, const float* beta,
                              float eps, const void* w2, int64_t ldw, const float* b2, const void* R,

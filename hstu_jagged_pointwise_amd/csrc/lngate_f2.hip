@@ -40,7 +40,7 @@ struct LnF2Shape {
   static constexpr int OPER = (kRows + N) * LD;           // bf16 elements of A and W2
   static constexpr int EPI = 4 * 32 * EP * 2;             // the 4 epilogue tiles, in bf16 units
   static constexpr int LDS = OPER > EPI ? OPER : EPI;
-  static_assert(K % 64 == 0 && K <= 256 && LPR <= 64, "K: 64 or 128 (4 columns per lane)");
+  static_assert(K == 64 || K == 128, "K: 64 or 128 (4 columns per lane, at most 64 lanes)");
   static_assert(N % 64 == 0 && (N * K / 8) % 256 == 0, "N: a multiple of 64");
 };
 
@@ -187,8 +187,11 @@ __global__ __launch_bounds__(256) void ln_gate_f2_kernel(
 }
 }  // namespace
 
-bool ln_gate_f2_supported(int K, int N, int bf16flag) {
-  return bf16flag && (K == 64 || K == 128) && (N == 64 || N == 128 || N == 256);
+bool ln_gate_f2_supported(int K, int N, int bf16flag, const void* w2, const float* gamma,
+                          const float* beta) {
+  auto al16 = [](const void* q) { return q == nullptr || ((uintptr_t)q % 16) == 0; };
+  return bf16flag && (K == 64 || K == 128) && (N == 64 || N == 128 || N == 256) && al16(w2) &&
+         al16(gamma) && al16(beta);
 }
 
 hipError_t launch_ln_gate_f2(const float* o, int64_t ld_o, int nsplit, int64_t split_stride,
@@ -198,7 +201,7 @@ hipError_t launch_ln_gate_f2(const float* o, int64_t ld_o, int nsplit, int64_t s
                              hipStream_t s, const float* self_w, const void* vself,
                              int64_t ld_vself, int dv) {
   if (rows <= 0) return hipSuccess;
-  if (!ln_gate_f2_supported(K, N, 1)) return hipErrorInvalidValue;
+  if (!ln_gate_f2_supported(K, N, 1, w2, gamma, beta) || !w2) return hipErrorInvalidValue;
   // 16-byte rows of O, W2, R and Y; 8-byte rows of U and the candidates' values
   if (ld_o % 4 != 0 || (nsplit > 1 && split_stride % 4 != 0) || ld_u % 4 != 0 || ldw % 8 != 0 ||
       ldy % 8 != 0 || (R && ldr % 8 != 0))

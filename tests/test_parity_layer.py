@@ -105,6 +105,33 @@ def test_narrow_layer_ln_gate_f2_in_one_kernel(H, d, d_model):
     check_layer(x, f"narrow layer H={H} d={d} d_model={d_model}")
 
 
+def test_narrow_layer_unaligned_ln_affine():
+    """A narrow layer whose LN gamma and beta are passed as views 4 bytes past a 16-byte
+    boundary: the library takes the two-kernel LN gate and f2 (the one-kernel form reads them
+    in 16-byte pieces), and the output matches the oracle at the flat bf16 tolerance."""
+    import torch
+    from hstu_jagged_pointwise_amd import ops
+    x = synth.make_layer(47, lambda r: np.array([0, 1, 130, 64, 257, 9]), 2, 64, 64, 128, 32, 16,
+                         "bf16", w_std=0.1, random_bias=True, with_ln_affine=True)
+    announce("layer bf16 H=2 d=64 d_model=128, gamma and beta 4 bytes off alignment")
+    ws = layer_weights_on_gpu(x.layers, x.dtype)
+
+    def off4(v):  # the same values, at an address 4 bytes past a 16-byte boundary
+        t = torch.empty(v.numel() + 1, dtype=v.dtype, device=v.device)
+        t[1:] = v
+        view = t[1:]
+        assert view.data_ptr() % 16 == 4
+        return view
+
+    ws = [dataclasses.replace(w, ln_gamma=off4(w.ln_gamma), ln_beta=off4(w.ln_beta)) for w in ws]
+    y = ops.hstu_layer_fwd(dev(x.offsets), dev(x.ts), dev(x.x, act_dtype(x.dtype)), ws,
+                           num_heads=x.num_heads, d_qk=x.d_qk, d_v=x.d_v,
+                           max_seq_len=x.max_seq_len, ln_eps=x.eps, residual=x.residual,
+                           seq_offsets_host=x.offsets)
+    torch.cuda.synchronize()
+    assert_rows_close(to_np(y), layer_oracle(x), TOL["bf16"], "unaligned LN affine")
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_layer_other_widths(dt):
     x = synth.make_layer(31, lambda r: np.array([50, 200, 3]), 3, 32, 128, 40, 64, 32, dt,
