@@ -211,6 +211,22 @@ def test_split_history_narrow_layer(H, d, d_model):
         assert np.array_equal(o.float().cpu().numpy(), base), f"microbatch {mb}"
 
 
+@pytest.mark.parametrize("H,hist", [(2, 16500), (3, 11000)])
+def test_long_history_last_layer_keys_values(H, hist):
+    """One layer over a long history: the history pass computes only the V and K columns
+    of f1 when they are whole 128-wide GEMM tiles (H*d_v = 128), and every column when they
+    are not (H*d_v = 192). Both against the oracle at the flat bf16 tolerance, candidates
+    with their own timestamps (the per-element bias path)."""
+    x = synth.make_mfalcon(17 + H, [hist, 300], [24, 9], H, 64, 64, 64, 32, 16, "bf16",
+                           num_layers=1, microbatch=16, shared_request_time=False, w_std=0.1,
+                           random_bias=True, with_ln_affine=True)
+    announce(f"mfalcon long history {hist} H={H}")
+    out, lg = mf_on_gpu(x)
+    want, _ = mf_oracle(x)
+    assert_rows_close(to_np(out), want, TOL["bf16"], f"mfalcon history {hist} H={H}")
+    _check_logits(lg, want, x, TOL["bf16"])
+
+
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 def test_cached_history_equals_one_shot(dt):
     """mfalcon_history + mfalcon_score_cached equals mfalcon_score bit for bit, and one
